@@ -1,0 +1,310 @@
+// libnvfp4 C ABI (include/nvfp4.h): argument validation, workspace layout and kernel dispatch.
+// Validation happens before any HIP call, so every error path is testable without a GPU.
+#include "../../include/nvfp4.h"
+
+#include <hip/hip_runtime.h>
+
+#include "launch.hpp"
+#include "nvfp4_device.hpp"
+
+using namespace nvfp4;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+inline size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+inline bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// Packed-A storage carved from a workspace (after the 4 KiB header).
+struct PackedLayout {
+  size_t gs_off, codes_off, scales_off, dec_off, end;
+  int64_t ld_codes, ld_scales, ld_dec;
+};
+
+PackedLayout packed_layout(int64_t rows, int64_t k, bool with_dec) {
+  PackedLayout L;
+  L.ld_codes = (int64_t)round_up((size_t)(k / 2), 16);
+  L.ld_scales = k / 16;
+  L.ld_dec = (int64_t)round_up((size_t)k, 8);
+  size_t off = kWsHeaderBytes;
+  L.gs_off = off;
+  off += kAlign;
+  L.codes_off = off;
+  off = round_up(off + (size_t)rows * (size_t)L.ld_codes, kAlign);
+  L.scales_off = off;
+  off = round_up(off + (size_t)rows * (size_t)L.ld_scales, kAlign);
+  L.dec_off = off;
+  if (with_dec) off = round_up(off + (size_t)rows * (size_t)L.ld_dec * 2, kAlign);
+  L.end = off;
+  return L;
+}
+
+constexpr int64_t kSmallM = 16;
+
+// Shape/pointer checks of a quantized operand.
+nvfp4_status check_tensor(const nvfp4_tensor *t, int64_t rows, int64_t cols, bool need_16b) {
+  if (!t) return NVFP4_ERR_NULL;
+  if (!t->codes || !t->scales || !t->global_scale) return NVFP4_ERR_NULL;
+  if (t->reserved != 0) return NVFP4_ERR_UNSUPPORTED;
+  if (t->block_rows != 1 && t->block_rows != 16) return NVFP4_ERR_UNSUPPORTED;
+  if (t->rows != rows || t->cols != cols) return NVFP4_ERR_SHAPE;
+  if (cols <= 0 || cols % 16 || rows < 0) return NVFP4_ERR_SHAPE;
+  if (t->block_rows == 16 && rows % 16) return NVFP4_ERR_SHAPE;
+  if (t->ld_codes < cols / 2 || t->ld_scales < cols / 16) return NVFP4_ERR_SHAPE;
+  if (need_16b && (!aligned(t->codes, 16) || t->ld_codes % 16)) return NVFP4_ERR_ALIGN;
+  if (!aligned(t->global_scale, 4)) return NVFP4_ERR_ALIGN;
+  return NVFP4_OK;
+}
+
+nvfp4_status check_bf16_input(const void *x, int64_t rows, int64_t cols, int64_t ld) {
+  if (!x) return NVFP4_ERR_NULL;
+  if (rows < 0 || cols <= 0 || cols % 16 || ld < cols) return NVFP4_ERR_SHAPE;
+  if (!aligned(x, 16) || ld % 8) return NVFP4_ERR_ALIGN;
+  // 32-bit chunk indexing inside the quantize kernels
+  if (rows * (cols / 8) >= (int64_t)1 << 31) return NVFP4_ERR_SHAPE;
+  return NVFP4_OK;
+}
+
+inline nvfp4_status hip_status(hipError_t e) { return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP; }
+
+// 1D quantization into explicit buffers, choosing the one-workgroup path for small tensors.
+nvfp4_status run_quantize_1d(const void *x, int64_t rows, int64_t cols, int64_t ld_x,
+                             uint8_t *codes, int64_t ld_codes, uint8_t *scales, int64_t ld_scales,
+                             float *gs, _Float16 *dec, int64_t ld_dec, void *ws,
+                             hipStream_t stream) {
+  if (rows * cols <= kSmallMaxElems)
+    return hip_status(launch_quantize_small(x, rows, cols, ld_x, codes, ld_codes, scales,
+                                            ld_scales, gs, dec, ld_dec, stream));
+  int grid;
+  uint32_t tpw;
+  hipError_t e = launch_amax(x, rows, cols, ld_x, ws, gs, &grid, &tpw, stream);
+  if (e != hipSuccess) return NVFP4_ERR_HIP;
+  e = launch_encode_1d(x, rows, cols, ld_x, codes, ld_codes, scales, ld_scales, ws, grid, tpw,
+                       stream);
+  if (e != hipSuccess) return NVFP4_ERR_HIP;
+  if (dec) return hip_status(launch_decode_f16(codes, ld_codes, scales, ld_scales, rows, cols,
+                                               dec, ld_dec, stream));
+  return NVFP4_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *nvfp4_status_string(int status) {
+  switch (status) {
+    case NVFP4_OK: return "NVFP4_OK";
+    case NVFP4_ERR_NULL: return "NVFP4_ERR_NULL: a required pointer is NULL";
+    case NVFP4_ERR_SHAPE: return "NVFP4_ERR_SHAPE: invalid or unsupported sizes";
+    case NVFP4_ERR_ALIGN: return "NVFP4_ERR_ALIGN: pointer or leading dimension misaligned";
+    case NVFP4_ERR_WORKSPACE: return "NVFP4_ERR_WORKSPACE: workspace missing or too small";
+    case NVFP4_ERR_HIP: return "NVFP4_ERR_HIP: a HIP kernel launch failed";
+    case NVFP4_ERR_UNSUPPORTED: return "NVFP4_ERR_UNSUPPORTED: unsupported argument combination";
+    default: return "unknown nvfp4 status";
+  }
+}
+
+int nvfp4_version(void) { return 100; }
+
+size_t nvfp4_quantize_workspace_bytes(int64_t rows, int64_t cols) {
+  (void)rows;
+  (void)cols;
+  return kWsHeaderBytes;
+}
+
+size_t nvfp4_gemm_workspace_bytes(int64_t m, int64_t n, int64_t k) {
+  (void)n;
+  if (m < 0 || k <= 0) return kWsHeaderBytes;
+  return packed_layout(m, k, m <= kSmallM).end;
+}
+
+size_t nvfp4_grouped_gemm_workspace_bytes(int64_t tokens, int64_t k, int64_t total_rows,
+                                          int32_t num_groups) {
+  (void)total_rows;
+  (void)num_groups;
+  if (tokens < 0 || k <= 0) return kWsHeaderBytes;
+  return packed_layout(tokens, k, false).end;
+}
+
+nvfp4_status nvfp4_quantize_1d(const void *x, int64_t rows, int64_t cols, int64_t ld_x,
+                               const nvfp4_tensor *out, void *ws, size_t ws_bytes, void *stream) {
+  nvfp4_status s = check_bf16_input(x, rows, cols, ld_x);
+  if (s) return s;
+  s = check_tensor(out, rows, cols, true);
+  if (s) return s;
+  if (out->block_rows != 1) return NVFP4_ERR_UNSUPPORTED;
+  if (!ws) return NVFP4_ERR_WORKSPACE;
+  if (ws_bytes < nvfp4_quantize_workspace_bytes(rows, cols) || !aligned(ws, kAlign))
+    return NVFP4_ERR_WORKSPACE;
+  return run_quantize_1d(x, rows, cols, ld_x, out->codes, out->ld_codes, out->scales,
+                         out->ld_scales, out->global_scale, nullptr, 0, ws,
+                         (hipStream_t)stream);
+}
+
+nvfp4_status nvfp4_quantize_2d(const void *w, int64_t rows, int64_t cols, int64_t ld_w,
+                               const nvfp4_tensor *out, void *ws, size_t ws_bytes, void *stream) {
+  nvfp4_status s = check_bf16_input(w, rows, cols, ld_w);
+  if (s) return s;
+  if (rows % 16) return NVFP4_ERR_SHAPE;
+  s = check_tensor(out, rows, cols, true);
+  if (s) return s;
+  if (out->block_rows != 16) return NVFP4_ERR_UNSUPPORTED;
+  if (!ws) return NVFP4_ERR_WORKSPACE;
+  if (ws_bytes < nvfp4_quantize_workspace_bytes(rows, cols) || !aligned(ws, kAlign))
+    return NVFP4_ERR_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  int grid;
+  uint32_t tpw;
+  if (launch_amax(w, rows, cols, ld_w, ws, out->global_scale, &grid, &tpw, st) != hipSuccess)
+    return NVFP4_ERR_HIP;
+  return hip_status(launch_encode_2d(w, rows, cols, ld_w, out->codes, out->ld_codes, out->scales,
+                                     out->ld_scales, ws, st));
+}
+
+nvfp4_status nvfp4_dequantize(const nvfp4_tensor *q, void *y, int64_t ld_y, int out_dtype,
+                              void *stream) {
+  if (!q) return NVFP4_ERR_NULL;
+  nvfp4_status s = check_tensor(q, q->rows, q->cols, false);
+  if (s) return s;
+  if (!y) return NVFP4_ERR_NULL;
+  if (out_dtype != NVFP4_OUT_BF16 && out_dtype != NVFP4_OUT_F32) return NVFP4_ERR_UNSUPPORTED;
+  if (ld_y < q->cols) return NVFP4_ERR_SHAPE;
+  if (!aligned(q->codes, 4) || q->ld_codes % 4 || !aligned(y, 16) || ld_y % 8)
+    return NVFP4_ERR_ALIGN;
+  if (q->rows == 0) return NVFP4_OK;
+  return hip_status(launch_dequantize(q->codes, q->ld_codes, q->scales, q->ld_scales,
+                                      q->global_scale, q->rows, q->cols, q->block_rows, y, ld_y,
+                                      out_dtype == NVFP4_OUT_F32, (hipStream_t)stream));
+}
+
+nvfp4_status nvfp4_gemm_w4a4(const void *a_bf16, int64_t m, int64_t k, int64_t ld_a,
+                             const nvfp4_tensor *a_q, const nvfp4_tensor *w, void *y,
+                             int64_t ld_y, void *ws, size_t ws_bytes, void *stream) {
+  if (!w || !y) return NVFP4_ERR_NULL;
+  if (m < 0 || k <= 0 || k % 16) return NVFP4_ERR_SHAPE;
+  const int64_t n = w->rows;
+  nvfp4_status s = check_tensor(w, n, k, true);
+  if (s) return s;
+  if (n < 1 || n >= ((int64_t)1 << 30) || m >= ((int64_t)1 << 30)) return NVFP4_ERR_SHAPE;
+  if (ld_y < n) return NVFP4_ERR_SHAPE;
+  if (!aligned(y, 4) || ld_y % 2) return NVFP4_ERR_ALIGN;
+  if (a_bf16) {
+    s = check_bf16_input(a_bf16, m, k, ld_a);
+    if (s) return s;
+    if (a_q) {
+      s = check_tensor(a_q, m, k, true);
+      if (s) return s;
+      if (a_q->block_rows != 1) return NVFP4_ERR_UNSUPPORTED;
+    }
+  } else {
+    s = check_tensor(a_q, m, k, true);
+    if (s) return s;
+    if (a_q->block_rows != 1) return NVFP4_ERR_UNSUPPORTED;
+  }
+  const bool small = m <= kSmallM;
+  if (!ws) return NVFP4_ERR_WORKSPACE;
+  if (ws_bytes < nvfp4_gemm_workspace_bytes(m, n, k) || !aligned(ws, kAlign))
+    return NVFP4_ERR_WORKSPACE;
+  if (m == 0) return NVFP4_OK;
+
+  hipStream_t st = (hipStream_t)stream;
+  uint8_t *base = (uint8_t *)ws;
+  const PackedLayout L = packed_layout(m, k, small);
+  GemmOperand A;
+  A.block_rows = 1;
+  if (a_q) {
+    A.codes = a_q->codes;
+    A.ld_codes = a_q->ld_codes;
+    A.scales = a_q->scales;
+    A.ld_scales = a_q->ld_scales;
+    A.gs = a_q->global_scale;
+  } else {
+    A.codes = base + L.codes_off;
+    A.ld_codes = L.ld_codes;
+    A.scales = base + L.scales_off;
+    A.ld_scales = L.ld_scales;
+    A.gs = (const float *)(base + L.gs_off);
+  }
+  _Float16 *dec = small ? (_Float16 *)(base + L.dec_off) : nullptr;
+  if (a_bf16) {
+    s = run_quantize_1d(a_bf16, m, k, ld_a, (uint8_t *)A.codes, A.ld_codes, (uint8_t *)A.scales,
+                        A.ld_scales, (float *)A.gs, dec, L.ld_dec, ws, st);
+    if (s) return s;
+  } else if (small) {
+    if (launch_decode_f16(A.codes, A.ld_codes, A.scales, A.ld_scales, m, k, dec, L.ld_dec, st) !=
+        hipSuccess)
+      return NVFP4_ERR_HIP;
+  }
+  GemmOperand W{w->codes, w->ld_codes, w->scales, w->ld_scales, w->global_scale, w->block_rows};
+  if (small)
+    return hip_status(
+        launch_gemm_small_m(dec, L.ld_dec, A.gs, W, m, n, k, (uint16_t *)y, ld_y, st));
+  return hip_status(launch_gemm_tile(A, W, m, n, k, (uint16_t *)y, ld_y, st));
+}
+
+nvfp4_status nvfp4_grouped_gemm_w4a4(const void *a_bf16, int64_t tokens, int64_t k,
+                                     int64_t ld_a, const nvfp4_tensor *a_q,
+                                     const int32_t *row_index, int64_t total_rows,
+                                     const int32_t *offsets, int32_t num_groups,
+                                     const nvfp4_tensor *w, int64_t n, void *y, int64_t ld_y,
+                                     void *ws, size_t ws_bytes, void *stream) {
+  if (!w || !y || !offsets) return NVFP4_ERR_NULL;
+  if (num_groups < 1) return NVFP4_ERR_SHAPE;
+  if (num_groups > 1024) return NVFP4_ERR_UNSUPPORTED;
+  if (tokens < 0 || total_rows < 0 || k <= 0 || k % 16 || n < 1) return NVFP4_ERR_SHAPE;
+  if (total_rows >= ((int64_t)1 << 30) || tokens >= ((int64_t)1 << 30)) return NVFP4_ERR_SHAPE;
+  if (!row_index && tokens != total_rows) return NVFP4_ERR_SHAPE;
+  nvfp4_status s = check_tensor(w, (int64_t)num_groups * n, k, true);
+  if (s) return s;
+  if (w->block_rows == 16 && n % 16) return NVFP4_ERR_SHAPE;
+  if (ld_y < n) return NVFP4_ERR_SHAPE;
+  if (!aligned(y, 4) || ld_y % 2) return NVFP4_ERR_ALIGN;
+  if (a_bf16) {
+    s = check_bf16_input(a_bf16, tokens, k, ld_a);
+    if (s) return s;
+    if (a_q) {
+      s = check_tensor(a_q, tokens, k, true);
+      if (s) return s;
+      if (a_q->block_rows != 1) return NVFP4_ERR_UNSUPPORTED;
+    }
+  } else {
+    s = check_tensor(a_q, tokens, k, true);
+    if (s) return s;
+    if (a_q->block_rows != 1) return NVFP4_ERR_UNSUPPORTED;
+  }
+  if (!ws) return NVFP4_ERR_WORKSPACE;
+  if (ws_bytes < nvfp4_grouped_gemm_workspace_bytes(tokens, k, total_rows, num_groups) ||
+      !aligned(ws, kAlign))
+    return NVFP4_ERR_WORKSPACE;
+  if (total_rows == 0 || tokens == 0) return NVFP4_OK;
+
+  hipStream_t st = (hipStream_t)stream;
+  uint8_t *base = (uint8_t *)ws;
+  const PackedLayout L = packed_layout(tokens, k, false);
+  GemmOperand A;
+  A.block_rows = 1;
+  if (a_q) {
+    A.codes = a_q->codes;
+    A.ld_codes = a_q->ld_codes;
+    A.scales = a_q->scales;
+    A.ld_scales = a_q->ld_scales;
+    A.gs = a_q->global_scale;
+  } else {
+    A.codes = base + L.codes_off;
+    A.ld_codes = L.ld_codes;
+    A.scales = base + L.scales_off;
+    A.ld_scales = L.ld_scales;
+    A.gs = (const float *)(base + L.gs_off);
+  }
+  if (a_bf16) {
+    s = run_quantize_1d(a_bf16, tokens, k, ld_a, (uint8_t *)A.codes, A.ld_codes,
+                        (uint8_t *)A.scales, A.ld_scales, (float *)A.gs, nullptr, 0, ws, st);
+    if (s) return s;
+  }
+  GemmOperand W{w->codes, w->ld_codes, w->scales, w->ld_scales, w->global_scale, w->block_rows};
+  return hip_status(launch_grouped_gemm(A, row_index, offsets, num_groups, W, n, n, k, total_rows,
+                                        (uint16_t *)y, ld_y, st));
+}
+
+}  // extern "C"

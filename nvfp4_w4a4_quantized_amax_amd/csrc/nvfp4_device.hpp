@@ -1,0 +1,277 @@
+// Device-side building blocks shared by the libnvfp4 kernels (gfx950 / CDNA4, wave64).
+//
+// Format (see include/nvfp4.h for the full statement and the pages it follows):
+//   E2M1 codes, OCP E4M3 block scales (1D: 16 consecutive values, 2D: 16x16 tile), FP32 global
+//   scale gs = RN_fp32(amax / 2688); reconstruction = code value * block scale * gs.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nvfp4 {
+
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef float floatx4_t __attribute__((ext_vector_type(4)));
+typedef float floatx16_t __attribute__((ext_vector_type(16)));
+
+constexpr int kWave = 64;
+constexpr int kE4M3MaxCode = 0x7E;  // 448
+
+// ---------------------------------------------------------------------------------------------
+// Workspace header (first 4 KiB of every workspace).  `amax_bits` and `arrive` are zero at
+// rest: the kernel that consumes them restores zero, so a workspace is zero-filled once.
+// The tables are rewritten on every quantization.
+// ---------------------------------------------------------------------------------------------
+struct QuantTables {
+  float gs;           // FP32 global scale
+  float inv6gs;       // approx 1 / (6 gs), only used to guess a block-scale code
+  uint32_t pad[2];
+  // thresh[s] (s = 1..126): smallest bf16 magnitude pattern whose block scale code is >= s.
+  // thresh[0] = 0, thresh[127] = 0xFFFF (never reached).
+  uint16_t thresh[128];
+  // mult[s]: float multiplier k with RNE_fp4(RN_fp32(x * k)) equal to the exact nearest-code
+  // rule for every bf16 x, for block scale code s; a negative value (-k) means no such k was
+  // found and the block takes the exact slow path.  mult[0] = 0 (zero scale).
+  float mult[128];
+};
+
+struct WsHeader {
+  uint32_t amax_bits;  // atomicMax cell: (|bf16| bits) of the running maximum
+  uint32_t arrive;     // arrival counter of the amax kernel's workgroups
+  uint32_t pad[14];
+  QuantTables tab;     // at offset 64
+};
+static_assert(sizeof(WsHeader) <= 4096, "workspace header must fit in 4 KiB");
+constexpr size_t kWsHeaderBytes = 4096;
+
+// ---------------------------------------------------------------------------------------------
+// Small helpers
+// ---------------------------------------------------------------------------------------------
+
+// Fast unsigned division by a runtime constant d >= 1, valid for n < 2^31:
+// q = (umulhi(n, mul) + n) >> shift with shift = ceil(log2 d), mul = 2^32 (2^shift - d) / d + 1.
+struct FastDiv {
+  uint32_t d, mul, shift;
+};
+
+__device__ __forceinline__ uint32_t fdiv(uint32_t n, FastDiv f) {
+  return (__umulhi(n, f.mul) + n) >> f.shift;
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Packed unsigned 16-bit max of two words (two bf16 magnitudes per word).
+__device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
+  uint32_t lo = max(a & 0xFFFFu, b & 0xFFFFu);
+  uint32_t hi = max(a >> 16, b >> 16);
+  return lo | (hi << 16);
+}
+
+// Largest |bf16| bit pattern among 8 packed bf16 values.
+__device__ __forceinline__ uint32_t absmax8(uint4 v) {
+  uint32_t m = pk_max_u16(pk_max_u16(v.x & 0x7FFF7FFFu, v.y & 0x7FFF7FFFu),
+                          pk_max_u16(v.z & 0x7FFF7FFFu, v.w & 0x7FFF7FFFu));
+  return max(m & 0xFFFFu, m >> 16);
+}
+
+// Value of an OCP E4M3 byte (0..0x7E): exponent field e, mantissa m; e = 0 is m * 2^-9.
+__device__ __forceinline__ float e4m3_to_float(uint32_t b) {
+  uint32_t e = b >> 3;
+  return e ? __uint_as_float((b + 960u) << 20) : (float)(b & 7u) * 0x1p-9f;
+}
+
+__device__ __forceinline__ double e4m3_to_double(uint32_t b) {
+  uint32_t e = b >> 3, m = b & 7u;
+  return e ? ldexp(1.0 + m * 0.125, (int)e - 7) : m * 0x1p-9;
+}
+
+// bf16 (round to nearest even) of a float, as 16 bits.  Inputs are finite.
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Round a positive double (in the bf16 normal range) down to the bf16 grid; returns the bf16
+// bit pattern and whether the value was already on the grid.
+__device__ __forceinline__ uint32_t bf16_round_down(double p, bool *exact) {
+  unsigned long long b = (unsigned long long)__double_as_longlong(p);
+  unsigned long long t = b & ~((1ull << 45) - 1ull);  // keep 7 explicit mantissa bits
+  *exact = (t == b);
+  float f = (float)__longlong_as_double((long long)t);  // exactly representable
+  return __float_as_uint(f) >> 16;
+}
+
+// Two E2M1 codes for x0, x1 (x0 -> low nibble) written into byte `sel` of `old`, using the
+// hardware conversion with unit scale (the scale operand is a power of two; 1.0 leaves the
+// input unscaled).  Round-to-nearest-even with saturation at 6.
+template <int SEL>
+__device__ __forceinline__ uint32_t cvt_fp4x2(uint32_t old, float x0, float x1) {
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, x0, x1, 1.0f, SEL);
+}
+
+// Magnitude code (0..7) the fast path assigns to the bf16 magnitude pattern `bits` under the
+// multiplier k: RNE_fp4(RN_fp32(x * k)).  The encode kernels compute exactly this per element.
+__device__ __forceinline__ uint32_t fast_code(uint32_t bits, float k) {
+  float y = __uint_as_float(bits << 16) * k;
+  return cvt_fp4x2<0>(0u, y, y) & 7u;
+}
+
+// ---------------------------------------------------------------------------------------------
+// Per-tensor tables (built once per quantization by one workgroup, threads 0..127).
+// ---------------------------------------------------------------------------------------------
+
+// E2M1 midpoints between magnitude indices i and i+1 (i = 0..6).
+__device__ __forceinline__ double e2m1_mid(int i) {
+  // 0.25 0.75 1.25 1.75 2.5 3.5 5
+  return i < 4 ? 0.25 + 0.5 * i : (i == 4 ? 2.5 : (i == 5 ? 3.5 : 5.0));
+}
+
+// Does multiplier k reproduce the exact nearest-magnitude rule (ties to even index, saturate at
+// 6) for every bf16 input under the exact scale S = sb * gs?  The fast code is monotone in x, so
+// it suffices that, around each midpoint mid_i * S, the largest bf16 that must map to <= i does
+// and the smallest bf16 that must map to >= i+1 does.
+__device__ inline bool multiplier_is_exact(float k, double S) {
+  for (int i = 0; i < 7; ++i) {
+    double P = e2m1_mid(i) * S;  // exact: <= 3 + 28 significant bits
+    bool exact;
+    uint32_t rd = bf16_round_down(P, &exact);
+    if (rd == 0u || rd >= 0x7F80u) return false;
+    bool tie_down = (i & 1) == 0;  // midpoint between an even index i and i+1 goes down
+    uint32_t below = exact ? (tie_down ? rd : rd - 1u) : rd;
+    uint32_t above = exact ? (tie_down ? rd + 1u : rd) : rd + 1u;
+    if (fast_code(below, k) > (uint32_t)i) return false;
+    if (fast_code(above, k) < (uint32_t)i + 1u) return false;
+  }
+  return true;
+}
+
+// Fill entry s of the tables for global scale gs (thread s of the building workgroup).
+__device__ inline void build_table_entry(QuantTables *t, int s, float gs) {
+  const double gsd = (double)gs;
+  if (s == 0) {
+    t->thresh[0] = 0;
+    t->mult[0] = 0.0f;
+    return;
+  }
+  if (s == 127 || gs == 0.0f || !(gs < 3.0e38f)) {
+    t->thresh[s] = 0xFFFFu;
+    t->mult[s] = 0.0f;
+    return;
+  }
+  // Block-scale threshold: bamax / (6 gs) is rounded to the nearest E4M3 code, ties to even.
+  // Code s is reached when bamax >= mu * 6 * gs (s even) or > it (s odd), mu = the midpoint
+  // between codes s-1 and s.  mu * 6 * gs has <= 5 + 2 + 24 bits: exact in double.
+  double mu = 0.5 * (e4m3_to_double((uint32_t)s - 1u) + e4m3_to_double((uint32_t)s));
+  double P = mu * 6.0 * gsd;
+  bool exact;
+  uint32_t rd = bf16_round_down(P, &exact);
+  uint32_t th = (s & 1) ? rd + 1u : (exact ? rd : rd + 1u);
+  t->thresh[s] = (uint16_t)min(th, 0xFFFFu);
+  // Element multiplier for scale code s.
+  double S = e4m3_to_double((uint32_t)s) * gsd;  // exact
+  float k0 = (float)(1.0 / S);
+  float k = -k0;
+  if (multiplier_is_exact(k0, S)) {
+    k = k0;
+  } else {
+    float ku = __uint_as_float(__float_as_uint(k0) + 1u);
+    float kd = __uint_as_float(__float_as_uint(k0) - 1u);
+    if (multiplier_is_exact(ku, S)) k = ku;
+    else if (multiplier_is_exact(kd, S)) k = kd;
+  }
+  t->mult[s] = k;
+}
+
+__device__ __forceinline__ float global_scale_from_amax_bits(uint32_t amax_bf16_bits) {
+  double amax = (double)__uint_as_float(amax_bf16_bits << 16);
+  return (float)(amax / 2688.0);  // correctly rounded: 53 >= 2 * 24 + 2
+}
+
+__device__ __forceinline__ float inv6gs_of(float gs) {
+  return (gs > 0.0f && gs < 3.0e38f) ? (float)(1.0 / (6.0 * (double)gs)) : 0.0f;
+}
+
+// ---------------------------------------------------------------------------------------------
+// Block-scale code and element codes
+// ---------------------------------------------------------------------------------------------
+
+// E4M3 code of a block whose |max| bf16 pattern is `bam`: a guess from bam * inv6gs, corrected
+// with the exact thresholds (the guess is within one code of the answer).
+__device__ __forceinline__ int scale_code(uint32_t bam, float inv6gs, const uint16_t *thresh) {
+  float t = __uint_as_float(bam << 16) * inv6gs;
+  int cand = (t >= 0x1p-6f) ? (int)(__float_as_uint(t) >> 20) - 960 : (int)(t * 512.0f);
+  cand = min(max(cand, 0), kE4M3MaxCode);
+  if (cand < kE4M3MaxCode && bam >= thresh[cand + 1]) ++cand;
+  if (cand > 0 && bam < thresh[cand]) --cand;
+  return cand;
+}
+
+// Exact magnitude code of |x| (as a float) for block scale value sbv: compare with each
+// midpoint * sbv * gs through one FMA (mid * sbv has <= 7 bits, so the product is exact and the
+// sign of the FMA result is the sign of the exact difference).
+__device__ __forceinline__ uint32_t exact_mag_code(float ax, float sbv, float gs) {
+  uint32_t c = 0;
+  c += fmaf(-(0.25f * sbv), gs, ax) > 0.0f;
+  c += fmaf(-(0.75f * sbv), gs, ax) >= 0.0f;
+  c += fmaf(-(1.25f * sbv), gs, ax) > 0.0f;
+  c += fmaf(-(1.75f * sbv), gs, ax) >= 0.0f;
+  c += fmaf(-(2.5f * sbv), gs, ax) > 0.0f;
+  c += fmaf(-(3.5f * sbv), gs, ax) >= 0.0f;
+  c += fmaf(-(5.0f * sbv), gs, ax) > 0.0f;
+  return c;
+}
+
+__device__ __forceinline__ uint32_t exact_code(float x, float sbv, float gs) {
+  uint32_t sign = (__float_as_uint(x) >> 28) & 8u;
+  if (sbv == 0.0f) return sign;
+  return sign | exact_mag_code(fabsf(x), sbv, gs);
+}
+
+// Eight E2M1 codes (one 32-bit word, element 0 in the low nibble) for 8 packed bf16 values.
+__device__ __forceinline__ uint32_t encode8(uint4 v, float k, int code, float gs) {
+  if (k >= 0.0f) {
+    uint32_t r = 0;
+    r = cvt_fp4x2<0>(r, bf16_lo(v.x) * k, bf16_hi(v.x) * k);
+    r = cvt_fp4x2<1>(r, bf16_lo(v.y) * k, bf16_hi(v.y) * k);
+    r = cvt_fp4x2<2>(r, bf16_lo(v.z) * k, bf16_hi(v.z) * k);
+    r = cvt_fp4x2<3>(r, bf16_lo(v.w) * k, bf16_hi(v.w) * k);
+    return r;
+  }
+  const float sbv = e4m3_to_float((uint32_t)code);
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  uint32_t r = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    r |= exact_code(bf16_lo(w[j]), sbv, gs) << (8 * j);
+    r |= exact_code(bf16_hi(w[j]), sbv, gs) << (8 * j + 4);
+  }
+  return r;
+}
+
+// ---------------------------------------------------------------------------------------------
+// Decode for the GEMM: 8 codes of one word -> 8 fp16 values code * scale (exact: <= 6
+// significant bits, magnitudes in [2^-10, 2688]).  The order of the 8 values inside the vector
+// is the same for both GEMM operands, which is all the dot product needs.
+// ---------------------------------------------------------------------------------------------
+__device__ __forceinline__ half8_t decode8_f16(uint32_t q, half2_t s2) {
+  half2_t h0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(q, 1.0f, 0);
+  half2_t h1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(q, 1.0f, 1);
+  half2_t h2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(q, 1.0f, 2);
+  half2_t h3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(q, 1.0f, 3);
+  h0 *= s2;
+  h1 *= s2;
+  h2 *= s2;
+  h3 *= s2;
+  half8_t r = {h0[0], h0[1], h1[0], h1[1], h2[0], h2[1], h3[0], h3[1]};
+  return r;
+}
+
+__device__ __forceinline__ half2_t scale_f16x2(uint32_t b) {
+  _Float16 s = (_Float16)e4m3_to_float(b);
+  half2_t r = {s, s};
+  return r;
+}
+
+}  // namespace nvfp4

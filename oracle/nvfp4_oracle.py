@@ -45,6 +45,8 @@ What the pages leave open, and the reading taken here (each is listed in the des
       (reconstruction applied to both); the GPU accumulates in fp32 and writes bf16, so it is
       compared with a tolerance, not bit for bit.
   R9  inputs are finite (NaN/Inf raise here).
+  R10 GEMM acceptance: |Y - Y64| <= 1e-3 * ||Y64[m, :]||_2 + 2^-8 * |Y64[m, n]|: the stated
+      relative budget for the fp32 accumulation plus half a bf16 ulp for the bf16 output.
 
 Exactness: every threshold below is a product of at most 31 significant bits (a midpoint with
 <= 7 bits times the 24-bit gs), so float64 holds it exactly and every comparison is the exact
@@ -218,10 +220,19 @@ def quantize_1d(x_bf16_bits, row_chunk=256):
 
     Returns (codes uint8 R x C/2, scales uint8 R x C/16, gs float32)."""
     x = _as_f64(x_bf16_bits)
-    R, C = x.shape
-    if C % 16:
+    if x.shape[1] % 16:
         raise ValueError("cols must be a multiple of 16")
     gs = global_scale(global_amax(x))
+    codes, scales = encode_1d(x_bf16_bits, gs, row_chunk)
+    return codes, scales, gs
+
+
+def encode_1d(x_bf16_bits, gs, row_chunk=256):
+    """The block-scale and code steps of quantize_1d for given rows under a given global scale
+    (1D blocks are row-local, so any subset of rows can be encoded on its own once gs is known).
+    Returns (codes, scales)."""
+    x = _as_f64(x_bf16_bits)
+    R, C = x.shape
     codes = np.empty((R, C // 2), dtype=np.uint8)
     scales = np.empty((R, C // 16), dtype=np.uint8)
     for r0 in range(0, R, row_chunk):
@@ -232,7 +243,7 @@ def quantize_1d(x_bf16_bits, row_chunk=256):
         c = element_codes(xb, sbv[:, :, None], gs)
         codes[r0:r0 + row_chunk] = pack_codes(c.reshape(-1, C))
         scales[r0:r0 + row_chunk] = sbc
-    return codes, scales, gs
+    return codes, scales
 
 
 def quantize_2d(w_bf16_bits):
@@ -245,12 +256,21 @@ def quantize_2d(w_bf16_bits):
     if R % 16 or C % 16:
         raise ValueError("rows and cols must be multiples of 16")
     gs = global_scale(global_amax(w))
+    codes, scales = encode_2d(w_bf16_bits, gs)
+    return codes, scales, gs
+
+
+def encode_2d(w_bf16_bits, gs):
+    """The block-scale and code steps of quantize_2d for a band of whole 16-row tiles under a
+    given global scale.  Returns (codes, scales)."""
+    w = _as_f64(w_bf16_bits)
+    R, C = w.shape
     tiles = np.abs(w).reshape(R // 16, 16, C // 16, 16)
     bamax = tiles.max(axis=(1, 3))
     sbc = block_scale_codes(bamax, gs)
     sbv_el = np.repeat(np.repeat(E4M3_POS[sbc], 16, axis=0), 16, axis=1)
     c = element_codes(w, sbv_el, gs)
-    return pack_codes(c), sbc, gs
+    return pack_codes(c), sbc
 
 
 def dequantize(codes, scales, gs, block_rows=1, out="f32"):
@@ -311,9 +331,17 @@ def grouped_gemm64(a_q, row_index, offsets, w_list):
 
 
 def row_tolerance(y64, rel=1e-3):
-    """Acceptance bound per output element: rel * ||Y64[m, :]||_2 (same bound for every column
-    of row m)."""
+    """Accumulation part of the acceptance bound: rel * ||Y64[m, :]||_2 (same bound for every
+    column of row m)."""
     return rel * np.sqrt(np.sum(np.square(y64), axis=1, keepdims=True))
+
+
+def gemm_tolerance(y64, rel=1e-3):
+    """Acceptance bound per output element (reading R10): the accumulation budget
+    rel * ||Y64[m, :]||_2 plus the rounding of the bf16 store, at most half a bf16 ulp of the
+    value, i.e. 2^-8 * |Y64[m, n]| (bf16 keeps 8 significant bits).  Without the second term the
+    bound fails on the exact product itself wherever one element dominates its row."""
+    return row_tolerance(y64, rel) + np.abs(y64) * 2.0 ** -8
 
 
 def storage_bits_per_value(rows, cols, block_rows=1):

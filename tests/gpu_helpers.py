@@ -1,0 +1,48 @@
+"""Helpers shared by the GPU parity tests: moving bf16 bit patterns to the device and quantized
+tensors back, and the oracle-side references."""
+
+import numpy as np
+import torch
+
+from oracle import nvfp4_oracle as O
+
+
+def dev_bf16(u16):
+    """numpy uint16 bf16 bits -> contiguous torch bf16 on cuda:0."""
+    return torch.from_numpy(np.ascontiguousarray(u16).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def host_q(q):
+    """QTensor -> (codes rows x cols/2, scales, gs) as numpy, padding stripped."""
+    torch.cuda.synchronize()
+    codes = q.codes[:, : q.cols // 2].cpu().numpy()
+    scales = q.scales.cpu().numpy()
+    gs = q.global_scale.cpu().numpy()
+    return codes, scales, (gs[0] if gs.size == 1 else gs)
+
+
+def bf16_to_f64(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def assert_codes_equal(got, want, what=""):
+    """Byte-exact comparison with a readable first mismatch."""
+    got, want = np.asarray(got), np.asarray(want)
+    assert got.shape == want.shape, (what, got.shape, want.shape)
+    bad = np.argwhere(got != want)
+    if bad.size:
+        i = tuple(bad[0])
+        raise AssertionError(f"{what}: {len(bad)} mismatches, first at {i}: got {got[i]:#x} "
+                             f"want {want[i]:#x}")
+
+
+def check_gemm(y_gpu, y64, rel=1e-3, what=""):
+    """|Y - Y64| <= rel * ||Y64[m, :]||_2 + 2^-8 |Y64[m, n]| for every element (accumulation
+    budget plus the bf16 store's half ulp); returns the worst error / bound ratio."""
+    y = bf16_to_f64(y_gpu) if isinstance(y_gpu, torch.Tensor) else y_gpu
+    tol = O.gemm_tolerance(y64, rel)
+    err = np.abs(y - y64)
+    ratio = np.where(tol > 0, err / np.where(tol > 0, tol, 1), np.where(err > 0, np.inf, 0))
+    worst = float(ratio.max()) if ratio.size else 0.0
+    assert worst <= 1.0, f"{what}: max err / tol = {worst:.3g}"
+    return worst

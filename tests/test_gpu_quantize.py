@@ -1,0 +1,165 @@
+"""GPU parity of quantize_1d / quantize_2d / dequantize against the CPU oracle: codes, scales and
+the global scale must be byte-identical; dequantized values bit-identical."""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import nvfp4_oracle as O
+from nvfp4_w4a4_quantized_amax_amd import workloads as W
+from gpu_helpers import assert_codes_equal, dev_bf16, host_q
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def nv():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from nvfp4_w4a4_quantized_amax_amd import nvfp4
+    return nvfp4
+
+
+def check_1d(nv, x_u16, what):
+    q = nv.quantize_1d(dev_bf16(x_u16))
+    c, s, g = host_q(q)
+    oc, os_, og = O.quantize_1d(x_u16)
+    assert np.float32(g) == og, f"{what}: gs {g!r} vs {og!r}"
+    assert_codes_equal(s, os_, what + " scales")
+    assert_codes_equal(c, oc, what + " codes")
+    return q
+
+
+def check_2d(nv, w_u16, what):
+    q = nv.quantize_2d(dev_bf16(w_u16))
+    c, s, g = host_q(q)
+    oc, os_, og = O.quantize_2d(w_u16)
+    assert np.float32(g) == og, f"{what}: gs {g!r} vs {og!r}"
+    assert_codes_equal(s, os_, what + " scales")
+    assert_codes_equal(c, oc, what + " codes")
+    return q
+
+
+def test_tiny_round_trip(nv):
+    d = W.tiny()
+    for name in ("a", "w"):
+        q = check_1d(nv, d[name], "tiny " + name)
+        c, s, g = host_q(q)
+        f32 = nv.dequantize(q, torch.float32).cpu().numpy()
+        want = O.dequantize(c, s, g, 1, out="f32")
+        assert np.array_equal(f32.view(np.uint32), want.view(np.uint32))
+        b16 = nv.dequantize(q, torch.bfloat16).cpu().view(torch.int16).numpy().view(np.uint16)
+        assert np.array_equal(b16, O.dequantize(c, s, g, 1, out="bf16"))
+
+
+@pytest.mark.parametrize("rows,cols", [(1, 16), (3, 48), (17, 80), (130, 272), (64, 8192),
+                                       (257, 1040), (2048, 4096)])
+def test_ragged_shapes(nv, rows, cols):
+    rng = np.random.default_rng(rows * 1000 + cols)
+    x = W.to_bf16_bits(rng.laplace(0, 1, (rows, cols)) * np.exp(rng.standard_normal(cols)))
+    check_1d(nv, x, f"{rows}x{cols}")
+
+
+def test_activation_distribution_band(nv):
+    """The activation workload's distribution (Laplace x log-normal column gains) on a 512-row
+    band, both through the two-pass path."""
+    x = W.activation(seed=1, rows=512, cols=8192)["x"]
+    check_1d(nv, x, "activation band")
+
+
+def test_strided_input(nv):
+    rng = np.random.default_rng(3)
+    big = W.to_bf16_bits(rng.standard_normal((300, 1024 + 64)))
+    xt = dev_bf16(big)[:, 32:32 + 1024]
+    assert xt.stride(0) == 1088
+    q = nv.quantize_1d(xt)
+    c, s, g = host_q(q)
+    oc, os_, og = O.quantize_1d(np.ascontiguousarray(big[:, 32:32 + 1024]))
+    assert np.float32(g) == og
+    assert_codes_equal(s, os_, "strided scales")
+    assert_codes_equal(c, oc, "strided codes")
+
+
+def adversarial_rows():
+    rows = []
+    mids = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0]
+    for sbv in [448.0, 1.75, 0.5, 0.0703125, 3 * 2.0 ** -9, 2.0 ** -9]:
+        s = sbv * 2.0 ** -8
+        row = [6 * s] + [m * s for m in mids] + [-m * s for m in mids] + [-0.0]
+        rows.append(row)
+    rows[0][0] = 10.5                                     # amax 10.5 -> gs = 2^-8 exactly
+    for mu in [(1.0 + 1.5 / 8) * 2.0 ** -3, 1.9375 * 2, 1.0625 * 0.25, 1.9375 * 2.0 ** -7]:
+        rows.append([mu * 6 * 2.0 ** -8] + [2.0 ** -10] * 15)  # block maxima on E4M3 midpoints
+    rows.append([0.0] * 16)                               # zero block
+    rows.append([-0.0] * 16)                              # negative zeros
+    rows.append([1e-30] + [-1e-32] * 15)                  # scale underflows to 0
+    return np.array(rows, dtype=np.float64)
+
+
+def test_adversarial_ties_and_zeros(nv):
+    x = W.to_bf16_bits(adversarial_rows())
+    x = np.concatenate([x, x[::-1]], axis=1)  # two blocks per row
+    check_1d(nv, x, "adversarial")
+    # the same values in a tensor large enough for the two-pass path
+    big = np.tile(x, (512, 4))
+    check_1d(nv, big, "adversarial two-pass")
+
+
+@pytest.mark.parametrize("amax_sig", [21, 42, 63, 105, 128, 255])
+def test_short_global_scales(nv, amax_sig):
+    """amax significands that are multiples of 21 make gs short (few bits), so exact E2M1 and
+    E4M3 midpoints occur often and exercise the exact slow path."""
+    rng = np.random.default_rng(amax_sig)
+    x = rng.integers(-255, 256, size=(96, 512)).astype(np.float64) * 2.0 ** -4
+    x[0, 0] = amax_sig * 2.0 ** -3
+    x[np.abs(x) > amax_sig * 2.0 ** -3] = 0
+    x = W.to_bf16_bits(x)
+    check_1d(nv, x, f"short gs {amax_sig}")
+    check_1d(nv, np.tile(x, (200, 1)), f"short gs {amax_sig} two-pass")
+
+
+def test_extremes(nv):
+    x = np.zeros((32, 64))
+    x[0, 0] = 3.3e38                     # near bf16 max
+    x[1, :16] = 1e-20
+    x[2, 16:32] = -7.5e30
+    x[3] = np.linspace(-1e38, 1e38, 64)
+    check_1d(nv, W.to_bf16_bits(x), "extremes")
+    z = np.zeros((40, 96), dtype=np.uint16)
+    z[5, 7] = 0x8000
+    check_1d(nv, z, "all zero")
+
+
+def test_workspace_reuse_and_determinism(nv):
+    rng = np.random.default_rng(5)
+    a = W.to_bf16_bits(rng.standard_normal((1024, 2048)) * 100)
+    b = W.to_bf16_bits(rng.standard_normal((1024, 2048)) * 0.01)
+    q1 = check_1d(nv, a, "first")
+    check_1d(nv, b, "second (smaller amax after larger)")
+    q3 = check_1d(nv, a, "third")
+    assert torch.equal(q1.codes, q3.codes) and torch.equal(q1.scales, q3.scales)
+
+
+@pytest.mark.parametrize("rows,cols", [(16, 16), (32, 4096), (512, 4096), (48, 272)])
+def test_quantize_2d(nv, rows, cols):
+    rng = np.random.default_rng(rows + cols)
+    w = W.to_bf16_bits(rng.standard_normal((rows, cols)) * 0.02)
+    q = check_2d(nv, w, f"2d {rows}x{cols}")
+    c, s, g = host_q(q)
+    f32 = nv.dequantize(q, torch.float32).cpu().numpy()
+    assert np.array_equal(f32.view(np.uint32), O.dequantize(c, s, g, 16, out="f32").view(np.uint32))
+
+
+def test_activation_full_size_sampled(nv):
+    """The 8192 x 8192 activation workload through the two-pass path: the global scale against
+    the oracle's (from the full amax), every byte of 96 sampled rows against the oracle."""
+    x = W.activation()["x"]
+    q = nv.quantize_1d(dev_bf16(x))
+    c, s, g = host_q(q)
+    og = O.global_scale(float(np.max(np.abs(W.bf16_bits_to_float32(x)))))
+    assert np.float32(g) == og
+    rng = np.random.default_rng(0)
+    rows = np.unique(np.concatenate([[0, 1, 8191], rng.choice(8192, 93, replace=False)]))
+    oc, os_ = O.encode_1d(x[rows], og)
+    assert_codes_equal(s[rows], os_, "full-size scales")
+    assert_codes_equal(c[rows], oc, "full-size codes")

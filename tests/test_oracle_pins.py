@@ -422,6 +422,20 @@ def test_row_tolerance_is_per_row_norm():
     assert np.allclose(t[:, 0], [5e-3, 1e-6])
 
 
+def test_gemm_tolerance_admits_the_bf16_store():
+    """The bound must hold for the exact product rounded to bf16 (torch's RNE cast) on any
+    data, including rows dominated by one element, and must not be looser than needed: an error
+    of one full bf16 ulp on a dominant element exceeds it."""
+    rng = np.random.default_rng(21)
+    y = rng.standard_normal((64, 48)) * np.exp(rng.uniform(-20, 20, (64, 1)))
+    y[::3, 0] *= 1e4                                   # dominant elements
+    yb = torch.from_numpy(y).to(torch.bfloat16).double().numpy()
+    assert np.all(np.abs(yb - y) <= O.gemm_tolerance(y))
+    row = np.array([[1.0 + 2.0 ** -7 * 0.999, 1e-6]])   # just below 1 + 1/128
+    one_ulp_off = row[0, 0] + 2.0 ** -7
+    assert abs(one_ulp_off - row[0, 0]) > O.gemm_tolerance(row)[0, 0]
+
+
 def test_dequantize_bf16_is_rne_of_fp32():
     codes = np.array([[0x17]], dtype=np.uint8)   # elements: code 7 (6.0), code 1 (0.5)
     codes = np.repeat(codes, 8, axis=1)

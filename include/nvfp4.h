@@ -83,12 +83,10 @@ int nvfp4_version(void);
 
 /* ---------------------------------------------------------------------------------------------
  * Workspace.  Every call that takes `ws` needs at least the matching number of bytes, 256-byte
- * aligned, ZERO-FILLED BEFORE ITS FIRST USE.  Its first 4 KiB hold two reduction cells (the
- * running amax and an arrival counter) that every call returns to zero before it ends, and the
- * per-tensor tables that every quantization rewrites; the rest holds the quantized activations
- * of the GEMM calls.  So a workspace is zeroed once when allocated and can then be reused by any
- * number of calls in stream order.  Calls that may overlap in time (different streams) need
- * different workspaces.
+ * aligned; its contents need no initialization and carry nothing from one call to the next.  Its
+ * first 8 KiB hold the per-workgroup partial maxima of the amax pass (and the grid-barrier slots
+ * of the single-read quantizer); the rest holds the quantized activations of the GEMM calls.  Calls that may overlap in time
+ * (different streams) need different workspaces.
  * ------------------------------------------------------------------------------------------- */
 size_t nvfp4_quantize_workspace_bytes(int64_t rows, int64_t cols);
 size_t nvfp4_gemm_workspace_bytes(int64_t m, int64_t n, int64_t k);

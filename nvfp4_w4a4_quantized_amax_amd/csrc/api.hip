@@ -18,15 +18,14 @@ inline bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 // Packed-A storage carved from a workspace (after the 4 KiB header).
 struct PackedLayout {
-  size_t gs_off, codes_off, scales_off, dec_off, end;
-  int64_t ld_codes, ld_scales, ld_dec;
+  size_t gs_off, codes_off, scales_off, end;
+  int64_t ld_codes, ld_scales;
 };
 
-PackedLayout packed_layout(int64_t rows, int64_t k, bool with_dec) {
+PackedLayout packed_layout(int64_t rows, int64_t k) {
   PackedLayout L;
   L.ld_codes = (int64_t)round_up((size_t)(k / 2), 16);
   L.ld_scales = k / 16;
-  L.ld_dec = (int64_t)round_up((size_t)k, 8);
   size_t off = kWsHeaderBytes;
   L.gs_off = off;
   off += kAlign;
@@ -34,8 +33,6 @@ PackedLayout packed_layout(int64_t rows, int64_t k, bool with_dec) {
   off = round_up(off + (size_t)rows * (size_t)L.ld_codes, kAlign);
   L.scales_off = off;
   off = round_up(off + (size_t)rows * (size_t)L.ld_scales, kAlign);
-  L.dec_off = off;
-  if (with_dec) off = round_up(off + (size_t)rows * (size_t)L.ld_dec * 2, kAlign);
   L.end = off;
   return L;
 }
@@ -71,21 +68,15 @@ inline nvfp4_status hip_status(hipError_t e) { return e == hipSuccess ? NVFP4_OK
 // 1D quantization into explicit buffers, choosing the one-workgroup path for small tensors.
 nvfp4_status run_quantize_1d(const void *x, int64_t rows, int64_t cols, int64_t ld_x,
                              uint8_t *codes, int64_t ld_codes, uint8_t *scales, int64_t ld_scales,
-                             float *gs, _Float16 *dec, int64_t ld_dec, void *ws,
-                             hipStream_t stream) {
+                             float *gs, void *ws, hipStream_t stream) {
   if (rows * cols <= kSmallMaxElems)
     return hip_status(launch_quantize_small(x, rows, cols, ld_x, codes, ld_codes, scales,
-                                            ld_scales, gs, dec, ld_dec, stream));
-  int grid;
-  uint32_t tpw;
-  hipError_t e = launch_amax(x, rows, cols, ld_x, ws, gs, &grid, &tpw, stream);
-  if (e != hipSuccess) return NVFP4_ERR_HIP;
-  e = launch_encode_1d(x, rows, cols, ld_x, codes, ld_codes, scales, ld_scales, ws, grid, tpw,
-                       stream);
-  if (e != hipSuccess) return NVFP4_ERR_HIP;
-  if (dec) return hip_status(launch_decode_f16(codes, ld_codes, scales, ld_scales, rows, cols,
-                                               dec, ld_dec, stream));
-  return NVFP4_OK;
+                                            ld_scales, gs, stream));
+  const hipError_t e = launch_quantize_persistent(x, rows, cols, ld_x, codes, ld_codes, scales,
+                                                  ld_scales, gs, ws, stream);
+  if (e != hipErrorNotSupported) return hip_status(e);
+  return hip_status(launch_quantize(x, rows, cols, ld_x, false, codes, ld_codes, scales,
+                                    ld_scales, gs, ws, stream));
 }
 
 }  // namespace
@@ -116,7 +107,7 @@ size_t nvfp4_quantize_workspace_bytes(int64_t rows, int64_t cols) {
 size_t nvfp4_gemm_workspace_bytes(int64_t m, int64_t n, int64_t k) {
   (void)n;
   if (m < 0 || k <= 0) return kWsHeaderBytes;
-  return packed_layout(m, k, m <= kSmallM).end;
+  return packed_layout(m, k).end;
 }
 
 size_t nvfp4_grouped_gemm_workspace_bytes(int64_t tokens, int64_t k, int64_t total_rows,
@@ -124,7 +115,7 @@ size_t nvfp4_grouped_gemm_workspace_bytes(int64_t tokens, int64_t k, int64_t tot
   (void)total_rows;
   (void)num_groups;
   if (tokens < 0 || k <= 0) return kWsHeaderBytes;
-  return packed_layout(tokens, k, false).end;
+  return packed_layout(tokens, k).end;
 }
 
 nvfp4_status nvfp4_quantize_1d(const void *x, int64_t rows, int64_t cols, int64_t ld_x,
@@ -138,8 +129,7 @@ nvfp4_status nvfp4_quantize_1d(const void *x, int64_t rows, int64_t cols, int64_
   if (ws_bytes < nvfp4_quantize_workspace_bytes(rows, cols) || !aligned(ws, kAlign))
     return NVFP4_ERR_WORKSPACE;
   return run_quantize_1d(x, rows, cols, ld_x, out->codes, out->ld_codes, out->scales,
-                         out->ld_scales, out->global_scale, nullptr, 0, ws,
-                         (hipStream_t)stream);
+                         out->ld_scales, out->global_scale, ws, (hipStream_t)stream);
 }
 
 nvfp4_status nvfp4_quantize_2d(const void *w, int64_t rows, int64_t cols, int64_t ld_w,
@@ -153,13 +143,9 @@ nvfp4_status nvfp4_quantize_2d(const void *w, int64_t rows, int64_t cols, int64_
   if (!ws) return NVFP4_ERR_WORKSPACE;
   if (ws_bytes < nvfp4_quantize_workspace_bytes(rows, cols) || !aligned(ws, kAlign))
     return NVFP4_ERR_WORKSPACE;
-  hipStream_t st = (hipStream_t)stream;
-  int grid;
-  uint32_t tpw;
-  if (launch_amax(w, rows, cols, ld_w, ws, out->global_scale, &grid, &tpw, st) != hipSuccess)
-    return NVFP4_ERR_HIP;
-  return hip_status(launch_encode_2d(w, rows, cols, ld_w, out->codes, out->ld_codes, out->scales,
-                                     out->ld_scales, ws, st));
+  return hip_status(launch_quantize(w, rows, cols, ld_w, true, out->codes, out->ld_codes,
+                                    out->scales, out->ld_scales, out->global_scale, ws,
+                                    (hipStream_t)stream));
 }
 
 nvfp4_status nvfp4_dequantize(const nvfp4_tensor *q, void *y, int64_t ld_y, int out_dtype,
@@ -202,7 +188,6 @@ nvfp4_status nvfp4_gemm_w4a4(const void *a_bf16, int64_t m, int64_t k, int64_t l
     if (s) return s;
     if (a_q->block_rows != 1) return NVFP4_ERR_UNSUPPORTED;
   }
-  const bool small = m <= kSmallM;
   if (!ws) return NVFP4_ERR_WORKSPACE;
   if (ws_bytes < nvfp4_gemm_workspace_bytes(m, n, k) || !aligned(ws, kAlign))
     return NVFP4_ERR_WORKSPACE;
@@ -210,7 +195,7 @@ nvfp4_status nvfp4_gemm_w4a4(const void *a_bf16, int64_t m, int64_t k, int64_t l
 
   hipStream_t st = (hipStream_t)stream;
   uint8_t *base = (uint8_t *)ws;
-  const PackedLayout L = packed_layout(m, k, small);
+  const PackedLayout L = packed_layout(m, k);
   GemmOperand A;
   A.block_rows = 1;
   if (a_q) {
@@ -226,20 +211,14 @@ nvfp4_status nvfp4_gemm_w4a4(const void *a_bf16, int64_t m, int64_t k, int64_t l
     A.ld_scales = L.ld_scales;
     A.gs = (const float *)(base + L.gs_off);
   }
-  _Float16 *dec = small ? (_Float16 *)(base + L.dec_off) : nullptr;
   if (a_bf16) {
     s = run_quantize_1d(a_bf16, m, k, ld_a, (uint8_t *)A.codes, A.ld_codes, (uint8_t *)A.scales,
-                        A.ld_scales, (float *)A.gs, dec, L.ld_dec, ws, st);
+                        A.ld_scales, (float *)A.gs, ws, st);
     if (s) return s;
-  } else if (small) {
-    if (launch_decode_f16(A.codes, A.ld_codes, A.scales, A.ld_scales, m, k, dec, L.ld_dec, st) !=
-        hipSuccess)
-      return NVFP4_ERR_HIP;
   }
   GemmOperand W{w->codes, w->ld_codes, w->scales, w->ld_scales, w->global_scale, w->block_rows};
-  if (small)
-    return hip_status(
-        launch_gemm_small_m(dec, L.ld_dec, A.gs, W, m, n, k, (uint16_t *)y, ld_y, st));
+  if (m <= kSmallM)
+    return hip_status(launch_gemm_small_m(A, W, m, n, k, (uint16_t *)y, ld_y, st));
   return hip_status(launch_gemm_tile(A, W, m, n, k, (uint16_t *)y, ld_y, st));
 }
 
@@ -281,7 +260,7 @@ nvfp4_status nvfp4_grouped_gemm_w4a4(const void *a_bf16, int64_t tokens, int64_t
 
   hipStream_t st = (hipStream_t)stream;
   uint8_t *base = (uint8_t *)ws;
-  const PackedLayout L = packed_layout(tokens, k, false);
+  const PackedLayout L = packed_layout(tokens, k);
   GemmOperand A;
   A.block_rows = 1;
   if (a_q) {
@@ -299,7 +278,7 @@ nvfp4_status nvfp4_grouped_gemm_w4a4(const void *a_bf16, int64_t tokens, int64_t
   }
   if (a_bf16) {
     s = run_quantize_1d(a_bf16, tokens, k, ld_a, (uint8_t *)A.codes, A.ld_codes,
-                        (uint8_t *)A.scales, A.ld_scales, (float *)A.gs, nullptr, 0, ws, st);
+                        (uint8_t *)A.scales, A.ld_scales, (float *)A.gs, ws, st);
     if (s) return s;
   }
   GemmOperand W{w->codes, w->ld_codes, w->scales, w->ld_scales, w->global_scale, w->block_rows};

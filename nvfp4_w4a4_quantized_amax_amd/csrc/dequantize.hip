@@ -51,22 +51,6 @@ __global__ __launch_bounds__(256) void k_dequantize(const uint8_t *__restrict__ 
   }
 }
 
-__global__ __launch_bounds__(256) void k_decode_f16(const uint8_t *__restrict__ codes,
-                                                    int64_t ld_codes,
-                                                    const uint8_t *__restrict__ scales,
-                                                    int64_t ld_scales, int64_t rows, int64_t cols,
-                                                    _Float16 *__restrict__ dec, int64_t ld_dec) {
-  const int64_t per_row = cols / 8;
-  const int64_t n = rows * per_row;
-  for (int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; u < n;
-       u += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t r = u / per_row, c8 = u - r * per_row;
-    const uint32_t q = *(const uint32_t *)(codes + r * ld_codes + c8 * 4);
-    half8_t d = decode8_f16(q, scale_f16x2(scales[r * ld_scales + (c8 >> 1)]));
-    *(half8_t *)(dec + r * ld_dec + c8 * 8) = d;
-  }
-}
-
 static unsigned grid_for(int64_t units) {
   int64_t g = (units + 255) / 256;
   if (g > 8192) g = 8192;
@@ -85,15 +69,6 @@ hipError_t launch_dequantize(const uint8_t *codes, int64_t ld_codes, const uint8
   else
     hipLaunchKernelGGL(k_dequantize<false>, dim3(grid), dim3(256), 0, stream, codes, ld_codes,
                        scales, ld_scales, gs, rows, cols, block_rows, y, ld_y);
-  return hipGetLastError();
-}
-
-hipError_t launch_decode_f16(const uint8_t *codes, int64_t ld_codes, const uint8_t *scales,
-                             int64_t ld_scales, int64_t rows, int64_t cols, _Float16 *dec,
-                             int64_t ld_dec, hipStream_t stream) {
-  const unsigned grid = grid_for(rows * (cols / 8));
-  hipLaunchKernelGGL(k_decode_f16, dim3(grid), dim3(256), 0, stream, codes, ld_codes, scales,
-                     ld_scales, rows, cols, dec, ld_dec);
   return hipGetLastError();
 }
 

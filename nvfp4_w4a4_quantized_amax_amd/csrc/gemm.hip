@@ -349,19 +349,21 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_grouped(GroupedArgs p) {
 
 // ---------------------------------------------------------------------------------------------
 // Small-M kernel (m <= 16, decode-shaped): streams W at full width.  A workgroup owns 16 rows of
-// W; its 4 waves split K and reduce through LDS.  The MFMA is 16x16x32 with W rows as the M
-// side and the (zero-padded) 16 activation rows as the N side; the activations arrive decoded
-// to fp16 (code * block scale), W is decoded in registers.
+// W; its 4 waves split K and reduce through LDS.  The MFMA is 16x16x32 with W rows as the M side
+// and the (zero-padded) 16 activation rows as the N side.  Both operands arrive packed and are
+// decoded in registers with the same K permutation: lane (row r = lane % 16, group q = lane / 16)
+// loads 16 code bytes at byte 64 * window + 16 * q of its row, i.e. K values
+// 128 * window + 32 * q + [0, 32), which feed four K=32 MFMAs (8 values each).
+// Loads of four windows are issued before any of them is used.
 // ---------------------------------------------------------------------------------------------
 struct SmallMArgs {
-  const _Float16 *a_dec;
-  int64_t ld_dec;
-  const float *gs_a;
-  GemmOperand w;
+  GemmOperand a, w;
   int64_t m, n, k;
   uint16_t *y;
   int64_t ld_y;
 };
+
+constexpr int kSmallMWin = 4;
 
 template <bool W2D>
 __global__ __launch_bounds__(kGemmThreads) void k_gemm_small_m(SmallMArgs p) {
@@ -373,34 +375,49 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_small_m(SmallMArgs p) {
   const uint8_t *w_row = p.w.codes + wr * p.w.ld_codes + q * 16;
   const uint8_t *w_srow = p.w.scales + (W2D ? (wr >> 4) : wr) * p.w.ld_scales + q * 2;
   const bool a_ok = i16 < p.m;
-  const _Float16 *a_row = p.a_dec + (a_ok ? i16 : 0) * p.ld_dec + q * 32;
+  const int64_t ar = a_ok ? i16 : 0;
+  const uint8_t *a_row = p.a.codes + ar * p.a.ld_codes + q * 16;
+  const uint8_t *a_srow = p.a.scales + ar * p.a.ld_scales + q * 2;
   // 128-wide K windows, split contiguously over the 4 waves.
   const int64_t nwin = (p.k + 127) / 128;
   const int64_t per = (nwin + 3) / 4;
   const int64_t w_begin = wave * per, w_end = min(w_begin + per, nwin);
   const int64_t kbytes = p.k / 2, kblocks = p.k / 16;
   floatx4_t acc = floatx4_t{};
-  for (int64_t win = w_begin; win < w_end; ++win) {
-    const int64_t rem = kbytes - win * 64 - q * 16;        // code bytes left for this lane
-    const int64_t remb = kblocks - win * 8 - q * 2;        // scale blocks left
-    const uint4 wv = load16_masked(w_row + win * 64, rem);
-    const uint32_t s0 = remb > 0 ? w_srow[win * 8] : 0u;
-    const uint32_t s1 = remb > 1 ? w_srow[win * 8 + 1] : 0u;
-    const half2_t sc0 = scale_f16x2(s0), sc1 = scale_f16x2(s1);
+  for (int64_t win0 = w_begin; win0 < w_end; win0 += kSmallMWin) {
+    uint4 wv[kSmallMWin], av[kSmallMWin];
+    uint32_t ws_[kSmallMWin], as_[kSmallMWin];
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      half8_t av = decode8_f16(word(wv, kk), kk < 2 ? sc0 : sc1);
-      half8_t bv = half8_t{};
-      // activation values for k = win*128 + q*32 + kk*8 .. +7 (zero past K or past row m)
-      if (a_ok && rem >= (int64_t)(kk + 1) * 4) bv = *(const half8_t *)(a_row + win * 128 + kk * 8);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv, acc, 0, 0, 0);
+    for (int u = 0; u < kSmallMWin; ++u) {
+      const int64_t win = win0 + u;
+      const bool in = win < w_end;
+      const int64_t rem = in ? kbytes - win * 64 - q * 16 : 0;   // code bytes left for this lane
+      const int64_t remb = in ? kblocks - win * 8 - q * 2 : 0;   // scale blocks left
+      wv[u] = load16_masked(w_row + win * 64, rem);
+      av[u] = a_ok ? load16_masked(a_row + win * 64, rem) : make_uint4(0, 0, 0, 0);
+      const uint32_t w0 = remb > 0 ? w_srow[win * 8] : 0u, w1 = remb > 1 ? w_srow[win * 8 + 1] : 0u;
+      const uint32_t a0 = (a_ok && remb > 0) ? a_srow[win * 8] : 0u;
+      const uint32_t a1 = (a_ok && remb > 1) ? a_srow[win * 8 + 1] : 0u;
+      ws_[u] = w0 | (w1 << 8);
+      as_[u] = a0 | (a1 << 8);
+    }
+#pragma unroll
+    for (int u = 0; u < kSmallMWin; ++u) {
+      const half2_t sw0 = scale_f16x2(ws_[u] & 0xFFu), sw1 = scale_f16x2(ws_[u] >> 8);
+      const half2_t sa0 = scale_f16x2(as_[u] & 0xFFu), sa1 = scale_f16x2(as_[u] >> 8);
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const half8_t wop = decode8_f16(word(wv[u], kk), kk < 2 ? sw0 : sw1);
+        const half8_t aop = decode8_f16(word(av[u], kk), kk < 2 ? sa0 : sa1);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(wop, aop, acc, 0, 0, 0);
+      }
     }
   }
   s_red[wave][lane] = acc;
   __syncthreads();
   if (wave == 0) {
-    floatx4_t s = s_red[0][lane] + s_red[1][lane] + s_red[2][lane] + s_red[3][lane];
-    const float alpha = (*p.gs_a) * (*p.w.gs);
+    const floatx4_t s = s_red[0][lane] + s_red[1][lane] + s_red[2][lane] + s_red[3][lane];
+    const float alpha = (*p.a.gs) * (*p.w.gs);
     if (i16 < p.m) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -444,13 +461,10 @@ hipError_t launch_gemm_tile(const GemmOperand &a, const GemmOperand &w, int64_t 
   return launch_tile_fm<4, 4>(a, w, m, n, k, y, ld_y, stream);
 }
 
-hipError_t launch_gemm_small_m(const _Float16 *a_dec, int64_t ld_dec, const float *gs_a,
-                               const GemmOperand &w, int64_t m, int64_t n, int64_t k, uint16_t *y,
-                               int64_t ld_y, hipStream_t stream) {
+hipError_t launch_gemm_small_m(const GemmOperand &a, const GemmOperand &w, int64_t m, int64_t n,
+                               int64_t k, uint16_t *y, int64_t ld_y, hipStream_t stream) {
   SmallMArgs p;
-  p.a_dec = a_dec;
-  p.ld_dec = ld_dec;
-  p.gs_a = gs_a;
+  p.a = a;
   p.w = w;
   p.m = m;
   p.n = n;

@@ -19,31 +19,34 @@ constexpr int kWave = 64;
 constexpr int kE4M3MaxCode = 0x7E;  // 448
 
 // ---------------------------------------------------------------------------------------------
-// Workspace header (first 4 KiB of every workspace).  `amax_bits` and `arrive` are zero at
-// rest: the kernel that consumes them restores zero, so a workspace is zero-filled once.
-// The tables are rewritten on every quantization.
+// Per-tensor tables, rebuilt from the global scale by every workgroup that encodes.
 // ---------------------------------------------------------------------------------------------
 struct QuantTables {
   float gs;           // FP32 global scale
   float inv6gs;       // approx 1 / (6 gs), only used to guess a block-scale code
-  uint32_t pad[2];
-  // thresh[s] (s = 1..126): smallest bf16 magnitude pattern whose block scale code is >= s.
-  // thresh[0] = 0, thresh[127] = 0xFFFF (never reached).
-  uint16_t thresh[128];
-  // mult[s]: float multiplier k with RNE_fp4(RN_fp32(x * k)) equal to the exact nearest-code
-  // rule for every bf16 x, for block scale code s; a negative value (-k) means no such k was
-  // found and the block takes the exact slow path.  mult[0] = 0 (zero scale).
-  float mult[128];
+  // thresh[s] (s = 1..126): smallest bf16 magnitude pattern whose block scale code is >= s;
+  // thresh[0] = 0, thresh[127] = 0xFFFF (never reached).  Stored in pairs:
+  // thresh2[s] = thresh[s] | thresh[s + 1] << 16, so one read gives both neighbours.
+  uint32_t thresh2[128];
+  // mult[s + 1] (s = 0..126): float multiplier k with RNE_fp4(RN_fp32(x * k)) equal to the exact
+  // nearest-code rule for every bf16 x, for block scale code s; a negative value (-k) means no
+  // such k was found and the block takes the exact slow path.  Scale code 0 has k = 0.
+  // mult[0] and mult[128] are padding (0), so codes s-1, s, s+1 can be read without a check.
+  float mult[129];
 };
 
-struct WsHeader {
-  uint32_t amax_bits;  // atomicMax cell: (|bf16| bits) of the running maximum
-  uint32_t arrive;     // arrival counter of the amax kernel's workgroups
-  uint32_t pad[14];
-  QuantTables tab;     // at offset 64
-};
-static_assert(sizeof(WsHeader) <= 4096, "workspace header must fit in 4 KiB");
-constexpr size_t kWsHeaderBytes = 4096;
+// Workspace header (8 KiB).  The two-pass path leaves one partial maximum (|bf16| bit pattern)
+// per amax workgroup in the first 4 KiB; the single-read path keeps one 64-bit (epoch, max) slot
+// per workgroup in the next 4 KiB, with a status word at its end.  Nothing in it needs to be zero
+// between calls.
+constexpr int kMaxAmaxSlots = 1024;
+constexpr size_t kWsHeaderBytes = 8192;
+constexpr size_t kPersistentSlotOffset = 4096;
+constexpr int kMaxPersistentSlots = 504;
+constexpr size_t kPersistentStatusOffset = 8192 - 64;
+static_assert(kMaxAmaxSlots * 4 <= kPersistentSlotOffset, "two-pass slots overlap");
+static_assert(kPersistentSlotOffset + kMaxPersistentSlots * 8 <= kPersistentStatusOffset,
+              "persistent slots overlap the status word");
 
 // ---------------------------------------------------------------------------------------------
 // Small helpers
@@ -59,14 +62,23 @@ __device__ __forceinline__ uint32_t fdiv(uint32_t n, FastDiv f) {
   return (__umulhi(n, f.mul) + n) >> f.shift;
 }
 
+// 16-byte load with the non-temporal hint (streamed once, not worth keeping in the caches).
+__device__ __forceinline__ uint4 ntload16(const uint4 *p) {
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 t = __builtin_nontemporal_load((const u32x4 *)p);
+  return make_uint4(t[0], t[1], t[2], t[3]);
+}
+
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
+typedef unsigned short ushort2_t __attribute__((ext_vector_type(2)));
+
 // Packed unsigned 16-bit max of two words (two bf16 magnitudes per word).
 __device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
-  uint32_t lo = max(a & 0xFFFFu, b & 0xFFFFu);
-  uint32_t hi = max(a >> 16, b >> 16);
-  return lo | (hi << 16);
+  ushort2_t r = __builtin_elementwise_max(__builtin_bit_cast(ushort2_t, a),
+                                          __builtin_bit_cast(ushort2_t, b));
+  return __builtin_bit_cast(uint32_t, r);
 }
 
 // Largest |bf16| bit pattern among 8 packed bf16 values.
@@ -84,7 +96,8 @@ __device__ __forceinline__ float e4m3_to_float(uint32_t b) {
 
 __device__ __forceinline__ double e4m3_to_double(uint32_t b) {
   uint32_t e = b >> 3, m = b & 7u;
-  return e ? ldexp(1.0 + m * 0.125, (int)e - 7) : m * 0x1p-9;
+  unsigned long long bits = ((unsigned long long)(e + 1016u) << 52) | ((unsigned long long)m << 49);
+  return e ? __longlong_as_double((long long)bits) : (double)m * 0x1p-9;
 }
 
 // bf16 (round to nearest even) of a float, as 16 bits.  Inputs are finite.
@@ -119,7 +132,7 @@ __device__ __forceinline__ uint32_t fast_code(uint32_t bits, float k) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// Per-tensor tables (built once per quantization by one workgroup, threads 0..127).
+// Per-tensor tables, built in LDS by every workgroup that encodes (256 threads, three phases).
 // ---------------------------------------------------------------------------------------------
 
 // E2M1 midpoints between magnitude indices i and i+1 (i = 0..6).
@@ -129,59 +142,101 @@ __device__ __forceinline__ double e2m1_mid(int i) {
 }
 
 // Does multiplier k reproduce the exact nearest-magnitude rule (ties to even index, saturate at
-// 6) for every bf16 input under the exact scale S = sb * gs?  The fast code is monotone in x, so
-// it suffices that, around each midpoint mid_i * S, the largest bf16 that must map to <= i does
-// and the smallest bf16 that must map to >= i+1 does.
-__device__ inline bool multiplier_is_exact(float k, double S) {
-  for (int i = 0; i < 7; ++i) {
-    double P = e2m1_mid(i) * S;  // exact: <= 3 + 28 significant bits
-    bool exact;
-    uint32_t rd = bf16_round_down(P, &exact);
-    if (rd == 0u || rd >= 0x7F80u) return false;
-    bool tie_down = (i & 1) == 0;  // midpoint between an even index i and i+1 goes down
-    uint32_t below = exact ? (tie_down ? rd : rd - 1u) : rd;
-    uint32_t above = exact ? (tie_down ? rd + 1u : rd) : rd + 1u;
-    if (fast_code(below, k) > (uint32_t)i) return false;
-    if (fast_code(above, k) < (uint32_t)i + 1u) return false;
-  }
+// 6) around midpoint i under the exact scale S = sb * gs?  The fast code is monotone in x, so it
+// suffices that the largest bf16 that must map to <= i does and the smallest bf16 that must map
+// to >= i+1 does; checking all 7 midpoints covers every bf16 input.
+__device__ __forceinline__ bool multiplier_ok_at(float k, double S, int i) {
+  double P = e2m1_mid(i) * S;  // exact: <= 3 + 28 significant bits
+  bool exact;
+  uint32_t rd = bf16_round_down(P, &exact);
+  if (rd == 0u || rd >= 0x7F80u) return false;
+  bool tie_down = (i & 1) == 0;  // midpoint between an even index i and i+1 goes down
+  uint32_t below = exact ? (tie_down ? rd : rd - 1u) : rd;
+  uint32_t above = exact ? (tie_down ? rd + 1u : rd) : rd + 1u;
+  return fast_code(below, k) <= (uint32_t)i && fast_code(above, k) >= (uint32_t)i + 1u;
+}
+
+__device__ __noinline__ bool multiplier_is_exact(float k, double S) {
+  for (int i = 0; i < 7; ++i)
+    if (!multiplier_ok_at(k, S, i)) return false;
   return true;
 }
 
-// Fill entry s of the tables for global scale gs (thread s of the building workgroup).
-__device__ inline void build_table_entry(QuantTables *t, int s, float gs) {
-  const double gsd = (double)gs;
-  if (s == 0) {
-    t->thresh[0] = 0;
-    t->mult[0] = 0.0f;
-    return;
-  }
-  if (s == 127 || gs == 0.0f || !(gs < 3.0e38f)) {
-    t->thresh[s] = 0xFFFFu;
-    t->mult[s] = 0.0f;
-    return;
-  }
-  // Block-scale threshold: bamax / (6 gs) is rounded to the nearest E4M3 code, ties to even.
-  // Code s is reached when bamax >= mu * 6 * gs (s even) or > it (s odd), mu = the midpoint
-  // between codes s-1 and s.  mu * 6 * gs has <= 5 + 2 + 24 bits: exact in double.
+// Block-scale threshold for code s (1..126): bamax / (6 gs) is rounded to the nearest E4M3 code,
+// ties to even, so code s is reached when bamax >= mu * 6 * gs (s even) or > it (s odd), mu being
+// the midpoint between codes s-1 and s; mu * 6 * gs has <= 5 + 2 + 24 bits: exact in double.
+__device__ __forceinline__ uint32_t scale_threshold(int s, double gsd) {
   double mu = 0.5 * (e4m3_to_double((uint32_t)s - 1u) + e4m3_to_double((uint32_t)s));
-  double P = mu * 6.0 * gsd;
   bool exact;
-  uint32_t rd = bf16_round_down(P, &exact);
+  uint32_t rd = bf16_round_down(mu * 6.0 * gsd, &exact);
   uint32_t th = (s & 1) ? rd + 1u : (exact ? rd : rd + 1u);
-  t->thresh[s] = (uint16_t)min(th, 0xFFFFu);
-  // Element multiplier for scale code s.
-  double S = e4m3_to_double((uint32_t)s) * gsd;  // exact
-  float k0 = (float)(1.0 / S);
-  float k = -k0;
-  if (multiplier_is_exact(k0, S)) {
-    k = k0;
-  } else {
-    float ku = __uint_as_float(__float_as_uint(k0) + 1u);
-    float kd = __uint_as_float(__float_as_uint(k0) - 1u);
-    if (multiplier_is_exact(ku, S)) k = ku;
-    else if (multiplier_is_exact(kd, S)) k = kd;
+  return min(th, 0xFFFFu);
+}
+
+struct TableScratch {
+  float kbase[8];    // multiplier for block scale (1 + m/8) * gs, m = 0..7; negative: slow path
+  uint32_t fail[8];
+  uint16_t thresh[128];
+};
+
+// Fill `t` (in LDS) for global scale gs.  Must be called by every thread of a workgroup of at
+// least 128 threads; ends with a barrier.  A usable gs lies in (0, 3e38); otherwise every block
+// gets scale 0.
+//
+// Scaling a block scale by 2^j scales the critical bf16 values around each midpoint by 2^j and
+// RN(1/S) by 2^-j, leaving x * k and every decision unchanged (no value leaves the normal range
+// for amax in the supported range).  So the multiplier only has to be checked for the 8 E4M3
+// mantissas (1 + m/8) * gs; the multiplier of any code is that of its mantissa times a power of
+// two.  Subnormal E4M3 codes normalize onto the same mantissas.
+__device__ inline void build_tables(QuantTables &t, TableScratch &sc, float gs) {
+  const int tid = threadIdx.x;
+  const double gsd = (double)gs;
+  const bool usable = gs > 0.0f && gs < 3.0e38f;
+  // Phase A: thresholds (threads 0..127), base multipliers (threads 0..7 also).
+  if (tid < 128) {
+    const int s = tid;
+    sc.thresh[s] = (uint16_t)((s == 0) ? 0u : ((s == 127 || !usable) ? 0xFFFFu : scale_threshold(s, gsd)));
   }
-  t->mult[s] = k;
+  if (tid < 8) {
+    sc.kbase[tid] = usable ? (float)(1.0 / ((1.0 + tid * 0.125) * gsd)) : 0.0f;
+    sc.fail[tid] = 0;
+  }
+  if (tid == 0) {
+    t.gs = gs;
+    t.inv6gs = usable ? (float)(1.0 / (6.0 * gsd)) : 0.0f;
+  }
+  __syncthreads();
+  // Phase B: 8 mantissas x 7 midpoints, one check per thread.
+  if (usable && tid < 56) {
+    const int m = tid / 7, i = tid - m * 7;
+    if (!multiplier_ok_at(sc.kbase[m], (1.0 + m * 0.125) * gsd, i)) sc.fail[m] = 1;
+  }
+  __syncthreads();
+  // Phase C (rare): a failing mantissa tries the neighbouring floats, else takes the exact path.
+  if (usable && tid < 8 && sc.fail[tid]) {
+    const float k0 = sc.kbase[tid];
+    const double S = (1.0 + tid * 0.125) * gsd;
+    const float ku = __uint_as_float(__float_as_uint(k0) + 1u);
+    const float kd = __uint_as_float(__float_as_uint(k0) - 1u);
+    sc.kbase[tid] = multiplier_is_exact(ku, S) ? ku : (multiplier_is_exact(kd, S) ? kd : -k0);
+  }
+  __syncthreads();
+  // Phase D: every code's multiplier = its mantissa's base multiplier scaled by 2^-exponent;
+  // thresholds paired with their upper neighbour.
+  if (tid < 128) {
+    const int s = tid;
+    float k = 0.0f;
+    if (usable && s >= 1 && s <= 126) {
+      const uint32_t vb = __float_as_uint(e4m3_to_float((uint32_t)s));
+      const int m = (int)((vb >> 20) & 7u);
+      const int E = (int)((vb >> 23) & 0xFFu) - 127;
+      k = ldexpf(sc.kbase[m], -E);
+    }
+    t.mult[s + 1] = (s == 127) ? 0.0f : k;
+    t.thresh2[s] = (uint32_t)sc.thresh[s] | ((s == 127 ? 0xFFFFu : (uint32_t)sc.thresh[s + 1]) << 16);
+  }
+  if (tid == 0) t.mult[0] = 0.0f;
+  __syncthreads();
 }
 
 __device__ __forceinline__ float global_scale_from_amax_bits(uint32_t amax_bf16_bits) {
@@ -197,15 +252,21 @@ __device__ __forceinline__ float inv6gs_of(float gs) {
 // Block-scale code and element codes
 // ---------------------------------------------------------------------------------------------
 
-// E4M3 code of a block whose |max| bf16 pattern is `bam`: a guess from bam * inv6gs, corrected
-// with the exact thresholds (the guess is within one code of the answer).
-__device__ __forceinline__ int scale_code(uint32_t bam, float inv6gs, const uint16_t *thresh) {
-  float t = __uint_as_float(bam << 16) * inv6gs;
-  int cand = (t >= 0x1p-6f) ? (int)(__float_as_uint(t) >> 20) - 960 : (int)(t * 512.0f);
+// E4M3 code of a block whose |max| bf16 pattern is `bam`, and its element multiplier: a guess
+// from bam * inv6gs (within one code of the answer), corrected with the exact thresholds.  The
+// threshold pair and the three candidate multipliers are read independently of each other.
+__device__ __forceinline__ int scale_code(uint32_t bam, const QuantTables &tab, float *k_out) {
+  const float t = __uint_as_float(bam << 16) * tab.inv6gs;
+  const int c_norm = (int)(__float_as_uint(t) >> 20) - 960;
+  const int c_sub = (int)(t * 512.0f);
+  int cand = (t >= 0x1p-6f) ? c_norm : c_sub;
   cand = min(max(cand, 0), kE4M3MaxCode);
-  if (cand < kE4M3MaxCode && bam >= thresh[cand + 1]) ++cand;
-  if (cand > 0 && bam < thresh[cand]) --cand;
-  return cand;
+  const uint32_t th = tab.thresh2[cand];
+  const float k_dn = tab.mult[cand], k_mid = tab.mult[cand + 1], k_up = tab.mult[cand + 2];
+  const bool up = bam >= (th >> 16);
+  const bool dn = bam < (th & 0xFFFFu);
+  *k_out = up ? k_up : (dn ? k_dn : k_mid);
+  return cand + (up ? 1 : 0) - (dn ? 1 : 0);
 }
 
 // Exact magnitude code of |x| (as a float) for block scale value sbv: compare with each
@@ -229,6 +290,19 @@ __device__ __forceinline__ uint32_t exact_code(float x, float sbv, float gs) {
   return sign | exact_mag_code(fabsf(x), sbv, gs);
 }
 
+// Exact path for the 8 packed bf16 values of `v` (blocks whose scale has no exact multiplier).
+__device__ __noinline__ uint32_t encode8_exact(uint4 v, int code, float gs) {
+  const float sbv = e4m3_to_float((uint32_t)code);
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  uint32_t r = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    r |= exact_code(bf16_lo(w[j]), sbv, gs) << (8 * j);
+    r |= exact_code(bf16_hi(w[j]), sbv, gs) << (8 * j + 4);
+  }
+  return r;
+}
+
 // Eight E2M1 codes (one 32-bit word, element 0 in the low nibble) for 8 packed bf16 values.
 __device__ __forceinline__ uint32_t encode8(uint4 v, float k, int code, float gs) {
   if (k >= 0.0f) {
@@ -239,15 +313,7 @@ __device__ __forceinline__ uint32_t encode8(uint4 v, float k, int code, float gs
     r = cvt_fp4x2<3>(r, bf16_lo(v.w) * k, bf16_hi(v.w) * k);
     return r;
   }
-  const float sbv = e4m3_to_float((uint32_t)code);
-  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-  uint32_t r = 0;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    r |= exact_code(bf16_lo(w[j]), sbv, gs) << (8 * j);
-    r |= exact_code(bf16_hi(w[j]), sbv, gs) << (8 * j + 4);
-  }
-  return r;
+  return encode8_exact(v, code, gs);
 }
 
 // ---------------------------------------------------------------------------------------------

@@ -1,17 +1,31 @@
 // NVFP4 dynamic quantization kernels for gfx950.
 //
 // Pass 1 (k_amax): streaming read of the bf16 tensor, |x| max on the bit patterns (exact and
-// order independent), one atomicMax per workgroup; the last workgroup to arrive turns amax into
-// the FP32 global scale and builds the per-tensor tables (block-scale thresholds and element
-// multipliers, see nvfp4_device.hpp), then clears the reduction cells.
-// Pass 2 (k_encode_1d / k_encode_2d): re-reads the tensor (same workgroup -> same chunks, in
-// reverse order, so the most recently read data is still in that XCD's L2), fits each block's
-// E4M3 scale and writes packed codes and scales.
-// Small tensors use k_quantize_small: one workgroup does both passes with an LDS barrier.
+// order independent); each workgroup stores its partial maximum in a workspace slot.  No
+// device-scope atomics: on MI355X they are resolved past the per-XCD L2s and serialize.
+// Pass 2 (k_encode_1d / k_encode_2d): every workgroup reduces the slots, derives the FP32 global
+// scale, builds the per-tensor tables in LDS (block-scale thresholds and element multipliers, see
+// nvfp4_device.hpp), then re-reads its share of the tensor, fits each block's E4M3 scale and
+// writes packed codes and scales.
+//
+// Work layout: the tensor is cut into 2 KiB tiles (64 blocks of 16 bf16, one block per lane).
+// Tile t belongs to wave slot t mod (4 * grid) of both passes, so at any moment the whole chip streams one contiguous
+// region, and tile t is read by the same XCD in both passes (workgroup b runs on XCD b mod 8 and
+// owns tiles with (t / 4) mod 8 == b mod 8 for any grid that is a multiple of 8).  Pass 2 walks
+// the tiles in the reverse order, so it starts with the data pass 1 read last (still in L2).
+// Small tensors use k_quantize_small: one workgroup runs both passes with an LDS barrier.
 //
 // The format steps follow "NVFP4 Explained: NVIDIA's 4-Bit Format for Faster AI Inference"
 // ("How NVFP4 Represents a Value") and "What is NVFP4? 4-bit AI inference on NVIDIA Blackwell
 // explained" ("What does NVFP4 mean?", "Why does scaling matter so much?").
+#include <stdlib.h>
+#include <string.h>
+#include <unistd.h>
+
+#include <atomic>
+#include <chrono>
+#include <mutex>
+
 #include "nvfp4_device.hpp"
 #include "launch.hpp"
 
@@ -19,89 +33,98 @@ namespace nvfp4 {
 
 constexpr int kQThreads = 256;
 constexpr int kQWaves = kQThreads / kWave;
-constexpr int kTileChunks = 64;  // one wave step: 64 x 16 B = 512 bf16 values = 32 blocks
+constexpr int kTileBlocks = 64;  // one wave step: 64 blocks of 16 bf16 = 2 KiB, one block per lane
+constexpr int kAmaxUnroll = 4;   // tiles in flight per wave in pass 1 (8 x 16 B per lane)
 
-// Chunk c (8 bf16 values) -> element offset in x.
+// Block b (16 bf16 values) -> uint4 index of its first half in x.
 template <bool CONTIG>
-__device__ __forceinline__ size_t chunk_x_offset(uint32_t c, FastDiv cpr, int64_t ld_x) {
-  if (CONTIG) return (size_t)c * 8u;
-  uint32_t r = fdiv(c, cpr);
-  uint32_t col8 = c - r * cpr.d;
-  return (size_t)r * (size_t)ld_x + (size_t)col8 * 8u;
+__device__ __forceinline__ size_t block_index(uint32_t b, FastDiv bpr, int64_t ld_x8) {
+  if (CONTIG) return (size_t)b * 2u;
+  uint32_t r = fdiv(b, bpr);
+  uint32_t cb = b - r * bpr.d;
+  return (size_t)r * (size_t)ld_x8 + (size_t)cb * 2u;
 }
 
-// ---------------------------------------------------------------------------------------------
-// Pass 1
-// ---------------------------------------------------------------------------------------------
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o, kWave));
   return v;
 }
 
-template <bool CONTIG>
-__global__ __launch_bounds__(kQThreads) void k_amax(const uint4 *__restrict__ x, uint32_t n_chunks,
-                                                    uint32_t tiles_per_wg, FastDiv cpr,
-                                                    int64_t ld_x, WsHeader *__restrict__ ws,
-                                                    float *__restrict__ gs_out) {
-  __shared__ uint32_t red[kQWaves];
-  __shared__ uint32_t last;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const uint32_t t0 = blockIdx.x * tiles_per_wg;
-  const uint32_t n_tiles = (n_chunks + kTileChunks - 1) / kTileChunks;
-  const uint32_t t1 = min(t0 + tiles_per_wg, n_tiles);
-  uint32_t m = 0;
-  // Each wave walks tiles t0 + wave, t0 + wave + 4, ...; four tiles in flight per wave.
-  uint32_t t = t0 + wave;
-  for (; t + 3 * kQWaves < t1; t += 4 * kQWaves) {
-    uint4 v[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      uint32_t c = (t + u * kQWaves) * kTileChunks + lane;
-      v[u] = c < n_chunks ? x[chunk_x_offset<CONTIG>(c, cpr, ld_x) / 8u] : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) m = max(m, absmax8(v[u]));
-  }
-  for (; t < t1; t += kQWaves) {
-    uint32_t c = t * kTileChunks + lane;
-    if (c < n_chunks) m = max(m, absmax8(x[chunk_x_offset<CONTIG>(c, cpr, ld_x) / 8u]));
-  }
-  m = wave_max_u32(m);
-  if (lane == 0) red[wave] = m;
+// Workgroup-wide max (all threads get the result).  Ends with a barrier.
+__device__ __forceinline__ uint32_t block_max_u32(uint32_t v, uint32_t *red) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  v = wave_max_u32(v);
+  if (lane == 0) red[wave] = v;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t b = red[0];
-#pragma unroll
-    for (int w = 1; w < kQWaves; ++w) b = max(b, red[w]);
-    atomicMax(&ws->amax_bits, b);
-    __threadfence();
-    uint32_t ticket = atomicAdd(&ws->arrive, 1u);
-    last = (ticket == gridDim.x - 1u);
-  }
+  uint32_t b = red[0];
+  for (int w = 1; w < nw; ++w) b = max(b, red[w]);
   __syncthreads();
-  if (!last) return;
-  // Last workgroup: every other workgroup's atomicMax happened before its arrival.
-  __threadfence();
-  __shared__ float s_gs;
-  if (threadIdx.x == 0) {
-    uint32_t amax = atomicExch(&ws->amax_bits, 0u);
-    ws->arrive = 0u;
-    float gs = global_scale_from_amax_bits(amax);
-    s_gs = gs;
-    ws->tab.gs = gs;
-    ws->tab.inv6gs = inv6gs_of(gs);
-    *gs_out = gs;
-  }
-  __syncthreads();
-  if (threadIdx.x < 128) build_table_entry(&ws->tab, threadIdx.x, s_gs);
+  return b;
+}
+
+__device__ __forceinline__ uint32_t absmax16(const uint4 &a, const uint4 &b) {
+  const uint32_t m = pk_max_u16(pk_max_u16(pk_max_u16(a.x & 0x7FFF7FFFu, a.y & 0x7FFF7FFFu),
+                                           pk_max_u16(a.z & 0x7FFF7FFFu, a.w & 0x7FFF7FFFu)),
+                                pk_max_u16(pk_max_u16(b.x & 0x7FFF7FFFu, b.y & 0x7FFF7FFFu),
+                                           pk_max_u16(b.z & 0x7FFF7FFFu, b.w & 0x7FFF7FFFu)));
+  return max(m & 0xFFFFu, m >> 16);
 }
 
 // ---------------------------------------------------------------------------------------------
-// Pass 2, 1D blocks.  Lane i of a wave step holds chunk base + i; lanes 2j and 2j+1 hold the
-// two halves of block base/2 + j and exchange their maxima with one shuffle.
+// Pass 1
 // ---------------------------------------------------------------------------------------------
-struct Enc1dOut {
+template <bool CONTIG>
+__global__ __launch_bounds__(kQThreads) void k_amax(const uint4 *__restrict__ x, uint32_t n_blocks,
+                                                    FastDiv bpr, int64_t ld_x8,
+                                                    uint32_t *__restrict__ slots) {
+  __shared__ uint32_t red[kQWaves];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint32_t S = gridDim.x * kQWaves;  // tiles between two visits of one wave
+  const uint32_t n_full = n_blocks / kTileBlocks;
+  const uint32_t n_tiles = (n_blocks + kTileBlocks - 1) / kTileBlocks;
+  uint32_t m = 0;
+  uint32_t t = blockIdx.x * kQWaves + wave;
+  for (; t + (kAmaxUnroll - 1) * S < n_full; t += kAmaxUnroll * S) {
+    uint4 v[2 * kAmaxUnroll];
+#pragma unroll
+    for (int u = 0; u < kAmaxUnroll; ++u) {
+      const size_t i = block_index<CONTIG>((t + u * S) * kTileBlocks + lane, bpr, ld_x8);
+      v[2 * u] = x[i];
+      v[2 * u + 1] = x[i + 1];
+    }
+#pragma unroll
+    for (int u = 0; u < kAmaxUnroll; ++u) m = max(m, absmax16(v[2 * u], v[2 * u + 1]));
+  }
+  for (; t < n_tiles; t += S) {
+    const uint32_t b = t * kTileBlocks + lane;
+    if (b < n_blocks) {
+      const size_t i = block_index<CONTIG>(b, bpr, ld_x8);
+      m = max(m, absmax16(x[i], x[i + 1]));
+    }
+  }
+  m = block_max_u32(m, red);
+  if (threadIdx.x == 0) slots[blockIdx.x] = m;
+}
+
+// Prologue of every encode workgroup: global amax from the slots, FP32 global scale, tables.
+__device__ __forceinline__ float tables_from_slots(const uint32_t *__restrict__ slots, int n_slots,
+                                                   QuantTables &tab, TableScratch &scr,
+                                                   uint32_t *red, float *__restrict__ gs_out) {
+  uint32_t m = 0;
+  for (int i = threadIdx.x; i < n_slots; i += blockDim.x) m = max(m, slots[i]);
+  m = block_max_u32(m, red);
+  const float gs = global_scale_from_amax_bits(m);
+  if (blockIdx.x == 0 && threadIdx.x == 0) *gs_out = gs;
+  build_tables(tab, scr, gs);
+  return gs;
+}
+
+// ---------------------------------------------------------------------------------------------
+// Pass 2, 1D blocks: one lane per 16-value block (two 16-byte loads, one 8-byte code store, one
+// scale byte).
+// ---------------------------------------------------------------------------------------------
+struct EncOut {
   uint8_t *codes;
   int64_t ld_codes;
   uint8_t *scales;
@@ -109,67 +132,223 @@ struct Enc1dOut {
 };
 
 template <bool CONTIG>
-__device__ __forceinline__ void encode_chunk_1d(uint4 v, uint32_t c, bool valid, int lane,
-                                                FastDiv cpr, const Enc1dOut &o, float gs,
-                                                float inv6gs, const uint16_t *thresh,
-                                                const float *mult) {
-  uint32_t m = valid ? absmax8(v) : 0u;
-  uint32_t bam = max(m, (uint32_t)__shfl_xor((int)m, 1, kWave));
-  if (!valid) return;
-  int code = scale_code(bam, inv6gs, thresh);
-  uint32_t packed = encode8(v, mult[code], code, gs);
+__device__ __forceinline__ void encode_block_1d(const uint4 &a, const uint4 &b, uint32_t blk,
+                                                FastDiv bpr, const EncOut &o,
+                                                const QuantTables &tab) {
+  float k;
+  const int code = scale_code(absmax16(a, b), tab, &k);
+  const uint2 packed = make_uint2(encode8(a, k, code, tab.gs), encode8(b, k, code, tab.gs));
   size_t co, so;
   if (CONTIG) {
-    co = (size_t)c * 4u;
-    so = (size_t)(c >> 1);
+    co = (size_t)blk * 8u;
+    so = (size_t)blk;
   } else {
-    uint32_t r = fdiv(c, cpr);
-    uint32_t col8 = c - r * cpr.d;
-    co = (size_t)r * (size_t)o.ld_codes + (size_t)col8 * 4u;
-    so = (size_t)r * (size_t)o.ld_scales + (size_t)(col8 >> 1);
+    const uint32_t r = fdiv(blk, bpr);
+    const uint32_t cb = blk - r * bpr.d;
+    co = (size_t)r * (size_t)o.ld_codes + (size_t)cb * 8u;
+    so = (size_t)r * (size_t)o.ld_scales + (size_t)cb;
   }
-  *(uint32_t *)(o.codes + co) = packed;
-  if ((lane & 1) == 0) o.scales[so] = (uint8_t)code;
+  *(uint2 *)(o.codes + co) = packed;
+  o.scales[so] = (uint8_t)code;
 }
 
 template <bool CONTIG>
 __global__ __launch_bounds__(kQThreads) void k_encode_1d(const uint4 *__restrict__ x,
-                                                         uint32_t n_chunks, uint32_t tiles_per_wg,
-                                                         FastDiv cpr, int64_t ld_x, Enc1dOut o,
-                                                         const WsHeader *__restrict__ ws) {
-  __shared__ uint16_t s_thresh[128];
-  __shared__ float s_mult[128];
-  if (threadIdx.x < 128) {
-    s_thresh[threadIdx.x] = ws->tab.thresh[threadIdx.x];
-    s_mult[threadIdx.x] = ws->tab.mult[threadIdx.x];
-  }
-  const float gs = ws->tab.gs;
-  const float inv6gs = ws->tab.inv6gs;
-  __syncthreads();
+                                                         uint32_t n_blocks, FastDiv bpr,
+                                                         int64_t ld_x8, EncOut o,
+                                                         const uint32_t *__restrict__ slots,
+                                                         int n_slots, float *__restrict__ gs_out) {
+  __shared__ QuantTables tab;
+  __shared__ TableScratch scr;
+  __shared__ uint32_t red[kQWaves];
+  tables_from_slots(slots, n_slots, tab, scr, red, gs_out);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const uint32_t t0 = blockIdx.x * tiles_per_wg;
-  const uint32_t n_tiles = (n_chunks + kTileChunks - 1) / kTileChunks;
-  const uint32_t t1 = min(t0 + tiles_per_wg, n_tiles);
-  if (t0 >= t1) return;
-  // Walk this wave's tiles in the reverse of pass 1's order, two at a time.
-  const uint32_t cnt = (t1 - t0 > (uint32_t)wave) ? (t1 - t0 - wave + kQWaves - 1) / kQWaves : 0u;
+  const uint32_t S = gridDim.x * kQWaves;
+  const uint32_t n_tiles = (n_blocks + kTileBlocks - 1) / kTileBlocks;
+  const uint32_t first = blockIdx.x * kQWaves + wave;
+  if (first >= n_tiles) return;
+  // This wave's tiles are first + i * S, i = 0 .. cnt - 1; walk them from the last, two at a
+  // time (four 16-byte loads in flight per lane).  Only the last tile of all can be partial.
+  const uint32_t cnt = (n_tiles - first + S - 1) / S;
   int32_t i = (int32_t)cnt - 1;
   for (; i >= 1; i -= 2) {
-    uint32_t ta = t0 + wave + (uint32_t)i * kQWaves;
-    uint32_t tb = ta - kQWaves;
-    uint32_t ca = ta * kTileChunks + lane, cb = tb * kTileChunks + lane;
-    bool va = ca < n_chunks, vb = cb < n_chunks;
-    uint4 a = va ? x[chunk_x_offset<CONTIG>(ca, cpr, ld_x) / 8u] : make_uint4(0, 0, 0, 0);
-    uint4 b = vb ? x[chunk_x_offset<CONTIG>(cb, cpr, ld_x) / 8u] : make_uint4(0, 0, 0, 0);
-    encode_chunk_1d<CONTIG>(a, ca, va, lane, cpr, o, gs, inv6gs, s_thresh, s_mult);
-    encode_chunk_1d<CONTIG>(b, cb, vb, lane, cpr, o, gs, inv6gs, s_thresh, s_mult);
+    const uint32_t ba = (first + (uint32_t)i * S) * kTileBlocks + lane;
+    const uint32_t bb = ba - S * kTileBlocks;
+    const bool va = ba < n_blocks;
+    uint4 a0 = make_uint4(0, 0, 0, 0), a1 = a0;
+    if (va) {
+      const size_t ia = block_index<CONTIG>(ba, bpr, ld_x8);
+      a0 = x[ia];
+      a1 = x[ia + 1];
+    }
+    const size_t ib = block_index<CONTIG>(bb, bpr, ld_x8);
+    const uint4 b0 = x[ib], b1 = x[ib + 1];
+    if (va) encode_block_1d<CONTIG>(a0, a1, ba, bpr, o, tab);
+    encode_block_1d<CONTIG>(b0, b1, bb, bpr, o, tab);
   }
   if (i == 0) {
-    uint32_t ta = t0 + wave;
-    uint32_t ca = ta * kTileChunks + lane;
-    bool va = ca < n_chunks;
-    uint4 a = va ? x[chunk_x_offset<CONTIG>(ca, cpr, ld_x) / 8u] : make_uint4(0, 0, 0, 0);
-    encode_chunk_1d<CONTIG>(a, ca, va, lane, cpr, o, gs, inv6gs, s_thresh, s_mult);
+    const uint32_t ba = first * kTileBlocks + lane;
+    if (ba < n_blocks) {
+      const size_t ia = block_index<CONTIG>(ba, bpr, ld_x8);
+      encode_block_1d<CONTIG>(x[ia], x[ia + 1], ba, bpr, o, tab);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Single-read path: one persistent workgroup per CU (cooperative launch, so all are resident).
+// Phase 1 reads each wave's tiles once, keeping the first RT of them in registers, and publishes
+// the workgroup's partial max.  A grid barrier without read-modify-write atomics follows: every
+// workgroup stores (epoch << 16 | max) into its own 64-bit slot, and one wave per workgroup
+// polls all slots until every slot carries this call's epoch (a per-call 48-bit number, so stale slots never match).  The poll is bounded; if it ever
+// ran out, the call's outputs would be wrong but the kernel still ends.  Phase 2 builds the tables
+// and encodes the register-resident tiles without touching memory again; tiles beyond RT per wave
+// are read a second time.
+// ---------------------------------------------------------------------------------------------
+constexpr uint32_t kSpinLimit = 1u << 20;
+
+template <int WAVES, int RT, int LT, bool CONTIG>
+__global__ __launch_bounds__(WAVES * 64, 1) void k_quantize_persistent(
+    const uint4 *__restrict__ x, uint32_t n_blocks, FastDiv bpr, int64_t ld_x8, EncOut o,
+    unsigned long long *__restrict__ slots, unsigned long long epoch,
+    float *__restrict__ gs_out, uint32_t *__restrict__ status) {
+  __shared__ QuantTables tab;
+  __shared__ TableScratch scr;
+  __shared__ uint32_t red[WAVES];
+  __shared__ uint32_t s_amax;
+  // LDS-resident tiles: [tile][half][wave][lane], one 16-byte half-block per lane.
+  __shared__ uint4 s_tiles[LT * 2 * WAVES][kWave];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint32_t S = gridDim.x * WAVES;
+  const uint32_t n_tiles = (n_blocks + kTileBlocks - 1) / kTileBlocks;
+  const uint32_t first = blockIdx.x * WAVES + wave;
+  const uint32_t cnt = first < n_tiles ? (n_tiles - first + S - 1) / S : 0u;
+  // The wave's i-th tile is first + i * S: i < LT live in LDS, LT <= i < LT + RT in registers,
+  // the rest (overflow) are read in both phases.
+  auto tile_block = [&](uint32_t i) { return (first + i * S) * kTileBlocks + lane; };
+  uint32_t m = 0;
+
+  // Phase 1a: LDS tiles, staged through registers in batches of kLdsBatch tiles.
+  constexpr int kLdsBatch = 4;
+  static_assert(LT % kLdsBatch == 0, "LDS tiles come in whole batches");
+#pragma unroll 1
+  for (int i0 = 0; i0 < LT; i0 += kLdsBatch) {
+    uint4 t[2 * kLdsBatch];
+#pragma unroll
+    for (int u = 0; u < kLdsBatch; ++u) {
+      uint4 lo = make_uint4(0, 0, 0, 0), hi = lo;
+      const uint32_t b = tile_block(i0 + u);
+      if ((uint32_t)(i0 + u) < cnt && b < n_blocks) {
+        const size_t idx = block_index<CONTIG>(b, bpr, ld_x8);
+        lo = ntload16(x + idx);
+        hi = ntload16(x + idx + 1);
+      }
+      t[2 * u] = lo;
+      t[2 * u + 1] = hi;
+    }
+#pragma unroll
+    for (int u = 0; u < kLdsBatch; ++u) {
+      m = max(m, absmax16(t[2 * u], t[2 * u + 1]));
+      s_tiles[(2 * (i0 + u)) * WAVES + wave][lane] = t[2 * u];
+      s_tiles[(2 * (i0 + u) + 1) * WAVES + wave][lane] = t[2 * u + 1];
+    }
+  }
+  // Phase 1b: register tiles (all loads issued before any is used), then the overflow tiles.
+  uint4 reg[2 * RT];
+#pragma unroll
+  for (int i = 0; i < RT; ++i) {
+    uint4 lo = make_uint4(0, 0, 0, 0), hi = lo;
+    const uint32_t b = tile_block(LT + i);
+    if ((uint32_t)(LT + i) < cnt && b < n_blocks) {
+      const size_t idx = block_index<CONTIG>(b, bpr, ld_x8);
+      lo = ntload16(x + idx);
+      hi = ntload16(x + idx + 1);
+    }
+    reg[2 * i] = lo;
+    reg[2 * i + 1] = hi;
+  }
+  for (uint32_t i = LT + RT; i < cnt; ++i) {
+    const uint32_t b = tile_block(i);
+    if (b < n_blocks) {
+      const size_t idx = block_index<CONTIG>(b, bpr, ld_x8);
+      m = max(m, absmax16(x[idx], x[idx + 1]));
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < RT; ++i) m = max(m, absmax16(reg[2 * i], reg[2 * i + 1]));
+  m = block_max_u32(m, red);
+
+  // Grid barrier on per-workgroup slots.  A slot carries its own payload (the partial max), so
+  // neither the store nor the polls need to order any other memory: relaxed device-coherent
+  // accesses suffice (a release here would force an L2 write-back).
+  const unsigned long long tag = (epoch & 0xFFFFFFFFFFFFull) << 16;
+  if (threadIdx.x == 0)
+    __hip_atomic_store(slots + blockIdx.x, tag | m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (wave == 0) {
+    uint32_t mx = 0;
+    bool done = false;
+    // Relaxed device-coherent polls until every slot carries this call's epoch.
+    for (uint32_t it = 0; it < kSpinLimit && !done; ++it) {
+      bool ok = true;
+      uint32_t lm = 0;
+      for (uint32_t j = lane; j < gridDim.x; j += 64) {
+        const unsigned long long v =
+            __hip_atomic_load(slots + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        ok = ok && ((v & ~0xFFFFull) == tag);
+        lm = max(lm, (uint32_t)(v & 0xFFFFu));
+      }
+      if (__all(ok)) {
+        mx = wave_max_u32(lm);
+        done = true;
+      } else {
+        __builtin_amdgcn_s_sleep(1);
+      }
+    }
+    if (lane == 0) {
+      // A barrier that never completed (workgroups not co-resident) poisons the global scale.
+      s_amax = done ? mx : 0x7FC0u;
+      if (!done) *status = 1u;
+    }
+  }
+  __syncthreads();
+  const float gs = global_scale_from_amax_bits(s_amax);
+  if (blockIdx.x == 0 && threadIdx.x == 0) *gs_out = gs;
+  build_tables(tab, scr, gs);
+
+  // Phase 2: encode the register tiles; each freed register pair immediately starts the re-read
+  // of one overflow tile.  Then the LDS tiles, then the prefetched overflow tiles; any further
+  // tiles are re-read and encoded one by one.
+#pragma unroll
+  for (int i = 0; i < RT; ++i) {
+    const uint32_t b = tile_block(LT + i);
+    if ((uint32_t)(LT + i) < cnt && b < n_blocks)
+      encode_block_1d<CONTIG>(reg[2 * i], reg[2 * i + 1], b, bpr, o, tab);
+    const uint32_t b2 = tile_block(LT + RT + i);
+    if ((uint32_t)(LT + RT + i) < cnt && b2 < n_blocks) {
+      const size_t idx = block_index<CONTIG>(b2, bpr, ld_x8);
+      reg[2 * i] = x[idx];
+      reg[2 * i + 1] = x[idx + 1];
+    }
+  }
+#pragma unroll 2
+  for (int i = 0; i < LT; ++i) {
+    const uint32_t b = tile_block(i);
+    if ((uint32_t)i < cnt && b < n_blocks)
+      encode_block_1d<CONTIG>(s_tiles[(2 * i) * WAVES + wave][lane],
+                              s_tiles[(2 * i + 1) * WAVES + wave][lane], b, bpr, o, tab);
+  }
+#pragma unroll
+  for (int i = 0; i < RT; ++i) {
+    const uint32_t b = tile_block(LT + RT + i);
+    if ((uint32_t)(LT + RT + i) < cnt && b < n_blocks)
+      encode_block_1d<CONTIG>(reg[2 * i], reg[2 * i + 1], b, bpr, o, tab);
+  }
+  for (uint32_t i = LT + 2 * RT; i < cnt; ++i) {
+    const uint32_t b = tile_block(i);
+    if (b < n_blocks) {
+      const size_t idx = block_index<CONTIG>(b, bpr, ld_x8);
+      encode_block_1d<CONTIG>(x[idx], x[idx + 1], b, bpr, o, tab);
+    }
   }
 }
 
@@ -180,17 +359,13 @@ __global__ __launch_bounds__(kQThreads) void k_encode_1d(const uint4 *__restrict
 // ---------------------------------------------------------------------------------------------
 __global__ __launch_bounds__(kQThreads) void k_encode_2d(const uint16_t *__restrict__ w,
                                                          int64_t rows, int64_t cols, int64_t ld_w,
-                                                         Enc1dOut o,
-                                                         const WsHeader *__restrict__ ws) {
-  __shared__ uint16_t s_thresh[128];
-  __shared__ float s_mult[128];
-  if (threadIdx.x < 128) {
-    s_thresh[threadIdx.x] = ws->tab.thresh[threadIdx.x];
-    s_mult[threadIdx.x] = ws->tab.mult[threadIdx.x];
-  }
-  const float gs = ws->tab.gs;
-  const float inv6gs = ws->tab.inv6gs;
-  __syncthreads();
+                                                         EncOut o,
+                                                         const uint32_t *__restrict__ slots,
+                                                         int n_slots, float *__restrict__ gs_out) {
+  __shared__ QuantTables tab;
+  __shared__ TableScratch scr;
+  __shared__ uint32_t red[kQWaves];
+  tables_from_slots(slots, n_slots, tab, scr, red, gs_out);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t tiles_c = cols / 16;
   const int64_t groups_c = (tiles_c + 3) / 4;
@@ -211,65 +386,49 @@ __global__ __launch_bounds__(kQThreads) void k_encode_2d(const uint16_t *__restr
 #pragma unroll
     for (int off = 1; off < 16; off <<= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off, kWave));
     if (!valid) continue;
-    int code = scale_code(m, inv6gs, s_thresh);
-    float k = s_mult[code];
-    uint2 packed = make_uint2(encode8(v0, k, code, gs), encode8(v1, k, code, gs));
+    float k;
+    const int code = scale_code(m, tab, &k);
+    const uint2 packed = make_uint2(encode8(v0, k, code, tab.gs), encode8(v1, k, code, tab.gs));
     *(uint2 *)(o.codes + (band * 16 + r) * o.ld_codes + tc * 8) = packed;
     if (r == 0) o.scales[band * o.ld_scales + tc] = (uint8_t)code;
   }
 }
 
 // ---------------------------------------------------------------------------------------------
-// Small tensors: one workgroup of 1024 threads runs both passes; tables live in LDS.  Optionally
-// also writes the decoded A (code * block scale, fp16, gs not applied) for the small-M GEMM.
+// Small tensors: one workgroup of 1024 threads runs both passes; tables live in LDS.
 // ---------------------------------------------------------------------------------------------
 constexpr int kSmallThreads = 1024;
 
-__global__ __launch_bounds__(kSmallThreads) void k_quantize_small(
-    const uint16_t *__restrict__ x, int32_t rows, int32_t cols, int64_t ld_x, Enc1dOut o,
-    float *__restrict__ gs_out, _Float16 *__restrict__ dec, int64_t ld_dec) {
+__global__ __launch_bounds__(kSmallThreads) void k_quantize_small(const uint16_t *__restrict__ x,
+                                                                  int32_t rows, int32_t cols,
+                                                                  int64_t ld_x, EncOut o,
+                                                                  float *__restrict__ gs_out) {
   __shared__ QuantTables tab;
+  __shared__ TableScratch scr;
   __shared__ uint32_t red[kSmallThreads / kWave];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int cpr = cols / 8;
   const int n_chunks = rows * cpr;
   uint32_t m = 0;
   for (int c = threadIdx.x; c < n_chunks; c += kSmallThreads) {
-    int r = c / cpr, c8 = c - r * cpr;
+    const int r = c / cpr, c8 = c - r * cpr;
     m = max(m, absmax8(*(const uint4 *)(x + (int64_t)r * ld_x + c8 * 8)));
   }
-  m = wave_max_u32(m);
-  if (lane == 0) red[wave] = m;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t b = 0;
-    for (int w = 0; w < kSmallThreads / kWave; ++w) b = max(b, red[w]);
-    float gs = global_scale_from_amax_bits(b);
-    tab.gs = gs;
-    tab.inv6gs = inv6gs_of(gs);
-    *gs_out = gs;
-  }
-  __syncthreads();
-  if (threadIdx.x < 128) build_table_entry(&tab, threadIdx.x, tab.gs);
-  __syncthreads();
-  const float gs = tab.gs, inv6gs = tab.inv6gs;
-  // Chunks are walked in wave-sized runs so that lane pairs always hold one whole block.
-  for (int base = wave * kWave; base < n_chunks; base += kSmallThreads) {
-    int c = base + lane;
-    bool valid = c < n_chunks;
-    int r = valid ? c / cpr : 0, c8 = valid ? c - r * cpr : 0;
-    uint4 v = valid ? *(const uint4 *)(x + (int64_t)r * ld_x + c8 * 8) : make_uint4(0, 0, 0, 0);
-    uint32_t mm = valid ? absmax8(v) : 0u;
-    uint32_t bam = max(mm, (uint32_t)__shfl_xor((int)mm, 1, kWave));
-    if (!valid) continue;
-    int code = scale_code(bam, inv6gs, tab.thresh);
-    uint32_t packed = encode8(v, tab.mult[code], code, gs);
-    *(uint32_t *)(o.codes + (int64_t)r * o.ld_codes + c8 * 4) = packed;
-    if ((lane & 1) == 0) o.scales[(int64_t)r * o.ld_scales + (c8 >> 1)] = (uint8_t)code;
-    if (dec) {
-      half8_t d = decode8_f16(packed, scale_f16x2((uint32_t)code));
-      *(half8_t *)(dec + (int64_t)r * ld_dec + c8 * 8) = d;
-    }
+  m = block_max_u32(m, red);
+  const float gs = global_scale_from_amax_bits(m);
+  if (threadIdx.x == 0) *gs_out = gs;
+  build_tables(tab, scr, gs);
+  // One lane per 16-value block.
+  const int bpr = cols / 16;
+  const int n_blocks = rows * bpr;
+  for (int blk = threadIdx.x; blk < n_blocks; blk += kSmallThreads) {
+    const int r = blk / bpr, cb = blk - r * bpr;
+    const uint4 *p = (const uint4 *)(x + (int64_t)r * ld_x + cb * 16);
+    const uint4 v0 = p[0], v1 = p[1];
+    float k;
+    const int code = scale_code(absmax16(v0, v1), tab, &k);
+    const uint2 packed = make_uint2(encode8(v0, k, code, tab.gs), encode8(v1, k, code, tab.gs));
+    *(uint2 *)(o.codes + (int64_t)r * o.ld_codes + cb * 8) = packed;
+    o.scales[(int64_t)r * o.ld_scales + cb] = (uint8_t)code;
   }
 }
 
@@ -286,70 +445,165 @@ static FastDiv make_fastdiv(uint32_t d) {
   return f;
 }
 
-int quant_grid_wgs() { return 256 * 4; }
+// Grid of both passes: a multiple of 8 (one share per XCD), at most one tile per wave slot.
+static int quant_grid(uint32_t n_tiles, int max_wgs) {
+  int g = (int)((n_tiles + kQWaves - 1) / kQWaves);
+  g = (g + 7) / 8 * 8;
+  return g < max_wgs ? (g < 8 ? 8 : g) : max_wgs;
+}
 
-hipError_t launch_amax(const void *x, int64_t rows, int64_t cols, int64_t ld_x, void *ws,
-                       float *gs_out, int *grid_out, uint32_t *tiles_per_wg_out,
-                       hipStream_t stream) {
-  const uint32_t cpr = (uint32_t)(cols / 8);
-  const uint32_t n_chunks = (uint32_t)(rows * (cols / 8));
-  const uint32_t n_tiles = (n_chunks + kTileChunks - 1) / kTileChunks;
-  uint32_t grid = (uint32_t)quant_grid_wgs();
-  uint32_t tpw = (n_tiles + grid - 1) / grid;
-  if (tpw == 0) tpw = 1;
-  grid = (n_tiles + tpw - 1) / tpw;
-  if (grid == 0) grid = 1;
-  *grid_out = (int)grid;
-  *tiles_per_wg_out = tpw;
-  FastDiv f = make_fastdiv(cpr);
-  const bool contig = (ld_x == cols);
-  if (contig)
-    hipLaunchKernelGGL(k_amax<true>, dim3(grid), dim3(kQThreads), 0, stream, (const uint4 *)x,
-                       n_chunks, tpw, f, ld_x, (WsHeader *)ws, gs_out);
+constexpr int kAmaxWgs = 512;    // two 4-wave workgroups per CU, four 2 KiB tiles in flight each
+constexpr int kEncodeWgs = 1024;
+
+hipError_t launch_quantize(const void *x, int64_t rows, int64_t cols, int64_t ld_x, bool two_d,
+                           uint8_t *codes, int64_t ld_codes, uint8_t *scales, int64_t ld_scales,
+                           float *gs_out, void *ws, hipStream_t stream) {
+  const uint32_t bpr = (uint32_t)(cols / 16);
+  const uint32_t n_blocks = (uint32_t)(rows * (cols / 16));
+  const uint32_t n_tiles = (n_blocks + kTileBlocks - 1) / kTileBlocks;
+  const FastDiv f = make_fastdiv(bpr);
+  const bool contig_in = (ld_x == cols);
+  uint32_t *slots = (uint32_t *)ws;
+  const int ga = quant_grid(n_tiles, kAmaxWgs);
+  static_assert(kAmaxWgs <= kMaxAmaxSlots, "slot array too small");
+  if (contig_in)
+    hipLaunchKernelGGL(k_amax<true>, dim3(ga), dim3(kQThreads), 0, stream, (const uint4 *)x,
+                       n_blocks, f, ld_x / 8, slots);
   else
-    hipLaunchKernelGGL(k_amax<false>, dim3(grid), dim3(kQThreads), 0, stream, (const uint4 *)x,
-                       n_chunks, tpw, f, ld_x, (WsHeader *)ws, gs_out);
+    hipLaunchKernelGGL(k_amax<false>, dim3(ga), dim3(kQThreads), 0, stream, (const uint4 *)x,
+                       n_blocks, f, ld_x / 8, slots);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const EncOut o{codes, ld_codes, scales, ld_scales};
+  if (two_d) {
+    const int64_t groups = (rows / 16) * ((cols / 16 + 3) / 4);
+    int64_t g = (groups + kQWaves - 1) / kQWaves;
+    g = g < kEncodeWgs ? (g < 1 ? 1 : g) : kEncodeWgs;
+    hipLaunchKernelGGL(k_encode_2d, dim3((unsigned)g), dim3(kQThreads), 0, stream,
+                       (const uint16_t *)x, rows, cols, ld_x, o, slots, ga, gs_out);
+    return hipGetLastError();
+  }
+  const int ge = quant_grid(n_tiles, kEncodeWgs);
+  const bool contig = contig_in && (ld_codes == cols / 2) && (ld_scales == cols / 16);
+  if (contig)
+    hipLaunchKernelGGL(k_encode_1d<true>, dim3(ge), dim3(kQThreads), 0, stream, (const uint4 *)x,
+                       n_blocks, f, ld_x / 8, o, slots, ga, gs_out);
+  else
+    hipLaunchKernelGGL(k_encode_1d<false>, dim3(ge), dim3(kQThreads), 0, stream,
+                       (const uint4 *)x, n_blocks, f, ld_x / 8, o, slots, ga, gs_out);
   return hipGetLastError();
 }
 
-hipError_t launch_encode_1d(const void *x, int64_t rows, int64_t cols, int64_t ld_x,
-                            uint8_t *codes, int64_t ld_codes, uint8_t *scales, int64_t ld_scales,
-                            const void *ws, int grid, uint32_t tpw, hipStream_t stream) {
-  const uint32_t cpr = (uint32_t)(cols / 8);
-  const uint32_t n_chunks = (uint32_t)(rows * (cols / 8));
-  FastDiv f = make_fastdiv(cpr);
-  Enc1dOut o{codes, ld_codes, scales, ld_scales};
+// Persistent single-read launch (one workgroup per CU).  Returns hipErrorNotSupported, having
+// launched nothing, when the device cannot hold one such workgroup per CU or the path is turned
+// off, so the caller can use the two-kernel path.
+constexpr int kPWaves = 16;
+constexpr int kPResident = 8;   // tiles kept in registers per wave (64 VGPRs)
+constexpr int kPLds = 4;        // tiles kept in LDS per wave (16 waves x 4 x 2 KiB = 128 KiB)
+
+struct DeviceInfo {
+  int cus = 0;
+  bool coop = false;
+  bool enabled = true;          // NVFP4_QUANT_PATH=two_pass turns the single-read path off
+  bool cooperative_api = false; // NVFP4_QUANT_PATH=cooperative launches through the cooperative API
+  int fits_contig = 0, fits_strided = 0;
+};
+
+static DeviceInfo device_info() {
+  static std::mutex mu;
+  static DeviceInfo cache[64];
+  static bool known[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return DeviceInfo{};
+  std::lock_guard<std::mutex> lock(mu);
+  if (!known[dev]) {
+    DeviceInfo d;
+    int coop = 0;
+    if (hipDeviceGetAttribute(&d.cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+        hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) == hipSuccess) {
+      d.coop = coop != 0;
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+              &d.fits_contig, (const void *)k_quantize_persistent<kPWaves, kPResident, kPLds, true>,
+              kPWaves * 64, 0) != hipSuccess)
+        d.fits_contig = 0;
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+              &d.fits_strided, (const void *)k_quantize_persistent<kPWaves, kPResident, kPLds, false>,
+              kPWaves * 64, 0) != hipSuccess)
+        d.fits_strided = 0;
+    }
+    (void)hipGetLastError();
+    const char *path = getenv("NVFP4_QUANT_PATH");
+    if (path && strcmp(path, "two_pass") == 0) d.enabled = false;
+    if (path && strcmp(path, "cooperative") == 0) d.cooperative_api = true;
+    cache[dev] = d;
+    known[dev] = true;
+  }
+  return cache[dev];
+}
+
+static std::atomic<unsigned long long> g_epoch{0};
+
+static unsigned long long next_epoch() {
+  unsigned long long e = g_epoch.fetch_add(1) + 1;
+  if (e == 1) {  // first call in this process: start from an unpredictable 48-bit value
+    const unsigned long long seed =
+        (unsigned long long)std::chrono::steady_clock::now().time_since_epoch().count() ^
+        ((unsigned long long)getpid() << 32) ^ (unsigned long long)(uintptr_t)&g_epoch;
+    unsigned long long z = seed + 0x9E3779B97F4A7C15ull;
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    z ^= z >> 31;
+    unsigned long long expected = 1;
+    g_epoch.compare_exchange_strong(expected, z | 1ull);
+    e = g_epoch.fetch_add(1) + 1;
+  }
+  return e & 0xFFFFFFFFFFFFull;
+}
+
+hipError_t launch_quantize_persistent(const void *x, int64_t rows, int64_t cols, int64_t ld_x,
+                                      uint8_t *codes, int64_t ld_codes, uint8_t *scales,
+                                      int64_t ld_scales, float *gs_out, void *ws,
+                                      hipStream_t stream) {
+  const DeviceInfo d = device_info();
   const bool contig = (ld_x == cols) && (ld_codes == cols / 2) && (ld_scales == cols / 16);
+  const int fits = contig ? d.fits_contig : d.fits_strided;
+  if (!d.enabled || d.cus <= 0 || fits < 1 || d.cus > kMaxPersistentSlots) return hipErrorNotSupported;
+  if (d.cooperative_api && !d.coop) return hipErrorNotSupported;
+  const uint32_t bpr = (uint32_t)(cols / 16);
+  uint32_t n_blocks = (uint32_t)(rows * (cols / 16));
+  FastDiv f = make_fastdiv(bpr);
+  int64_t ld_x8 = ld_x / 8;
+  EncOut o{codes, ld_codes, scales, ld_scales};
+  unsigned long long *slots = (unsigned long long *)((uint8_t *)ws + kPersistentSlotOffset);
+  unsigned long long epoch = next_epoch();
+  uint32_t *status = (uint32_t *)((uint8_t *)ws + kPersistentStatusOffset);
+  const uint4 *xp = (const uint4 *)x;
+  void *args[] = {(void *)&xp, (void *)&n_blocks, (void *)&f, (void *)&ld_x8, (void *)&o,
+                  (void *)&slots, (void *)&epoch, (void *)&gs_out, (void *)&status};
+  const void *fn = contig ? (const void *)k_quantize_persistent<kPWaves, kPResident, kPLds, true>
+                          : (const void *)k_quantize_persistent<kPWaves, kPResident, kPLds, false>;
+  if (d.cooperative_api)
+    return hipLaunchCooperativeKernel(fn, dim3(d.cus), dim3(kPWaves * 64), args, 0, stream);
+  // Plain launch: the occupancy check above guarantees one workgroup per CU fits, so on a device
+  // that is not running other work all of them are resident at once; if they ever are not, the
+  // bounded barrier ends the kernel with a NaN global scale instead of hanging.
   if (contig)
-    hipLaunchKernelGGL(k_encode_1d<true>, dim3(grid), dim3(kQThreads), 0, stream,
-                       (const uint4 *)x, n_chunks, tpw, f, ld_x, o, (const WsHeader *)ws);
+    hipLaunchKernelGGL((k_quantize_persistent<kPWaves, kPResident, kPLds, true>), dim3(d.cus),
+                       dim3(kPWaves * 64), 0, stream, xp, n_blocks, f, ld_x8, o, slots, epoch,
+                       gs_out, status);
   else
-    hipLaunchKernelGGL(k_encode_1d<false>, dim3(grid), dim3(kQThreads), 0, stream,
-                       (const uint4 *)x, n_chunks, tpw, f, ld_x, o, (const WsHeader *)ws);
-  return hipGetLastError();
-}
-
-hipError_t launch_encode_2d(const void *w, int64_t rows, int64_t cols, int64_t ld_w,
-                            uint8_t *codes, int64_t ld_codes, uint8_t *scales, int64_t ld_scales,
-                            const void *ws, hipStream_t stream) {
-  Enc1dOut o{codes, ld_codes, scales, ld_scales};
-  const int64_t groups = (rows / 16) * ((cols / 16 + 3) / 4);
-  int64_t grid = (groups + kQWaves - 1) / kQWaves;
-  if (grid > 4096) grid = 4096;
-  if (grid < 1) grid = 1;
-  hipLaunchKernelGGL(k_encode_2d, dim3((unsigned)grid), dim3(kQThreads), 0, stream,
-                     (const uint16_t *)w, rows, cols, ld_w, o, (const WsHeader *)ws);
+    hipLaunchKernelGGL((k_quantize_persistent<kPWaves, kPResident, kPLds, false>), dim3(d.cus),
+                       dim3(kPWaves * 64), 0, stream, xp, n_blocks, f, ld_x8, o, slots, epoch,
+                       gs_out, status);
   return hipGetLastError();
 }
 
 hipError_t launch_quantize_small(const void *x, int64_t rows, int64_t cols, int64_t ld_x,
                                  uint8_t *codes, int64_t ld_codes, uint8_t *scales,
-                                 int64_t ld_scales, float *gs_out, _Float16 *dec, int64_t ld_dec,
-                                 hipStream_t stream) {
-  Enc1dOut o{codes, ld_codes, scales, ld_scales};
+                                 int64_t ld_scales, float *gs_out, hipStream_t stream) {
+  const EncOut o{codes, ld_codes, scales, ld_scales};
   hipLaunchKernelGGL(k_quantize_small, dim3(1), dim3(kSmallThreads), 0, stream,
-                     (const uint16_t *)x, (int32_t)rows, (int32_t)cols, ld_x, o, gs_out, dec,
-                     ld_dec);
+                     (const uint16_t *)x, (int32_t)rows, (int32_t)cols, ld_x, o, gs_out);
   return hipGetLastError();
 }
 

@@ -121,8 +121,8 @@ def empty_qtensor(rows, cols, block_rows=1, device="cuda", n_global_scales=1):
 
 
 class Workspace:
-    """Zero-filled device scratch, grown on demand (one per device; calls on one device share
-    it, so they must be ordered on one stream)."""
+    """Device scratch for the library calls, grown on demand (one per device; calls on one
+    device share it, so they must be ordered on one stream)."""
     _bufs = {}
 
     @classmethod

@@ -38,13 +38,13 @@ def test_status_strings_and_version():
 
 
 def test_workspace_sizes():
-    assert L.nvfp4_quantize_workspace_bytes(8192, 8192) == 4096
+    assert L.nvfp4_quantize_workspace_bytes(8192, 8192) == 8192
     small = L.nvfp4_gemm_workspace_bytes(16, 14336, 4096)
     big = L.nvfp4_gemm_workspace_bytes(8192, 8192, 8192)
-    # packed A: codes + scales (+ fp16 decoded A for m <= 16)
-    assert big >= 4096 + 8192 * 4096 + 8192 * 512
-    assert small >= 4096 + 16 * 2048 + 16 * 256 + 16 * 4096 * 2
-    assert L.nvfp4_grouped_gemm_workspace_bytes(4096, 2048, 32768, 128) >= 4096 + 4096 * 1024
+    # packed A: codes + scales + global scale after the 4 KiB header
+    assert big >= 8192 + 8192 * 4096 + 8192 * 512 + 4
+    assert small >= 8192 + 16 * 2048 + 16 * 256 + 4
+    assert L.nvfp4_grouped_gemm_workspace_bytes(4096, 2048, 32768, 128) >= 8192 + 4096 * 1024
 
 
 FAKE = 0x100000  # aligned, never dereferenced: every call below fails validation first
@@ -55,7 +55,7 @@ def qt(rows, cols, block_rows=1, ld=None, codes=FAKE, gs=FAKE):
     return nv.CTensor(codes, ld, FAKE, cols // 16, gs, rows, cols, block_rows, 0)
 
 
-def q1d(x, rows, cols, ld, out, ws=FAKE, wsb=4096):
+def q1d(x, rows, cols, ld, out, ws=FAKE, wsb=8192):
     return L.nvfp4_quantize_1d(x, rows, cols, ld, ctypes.byref(out), ws, wsb, None)
 
 
@@ -79,9 +79,9 @@ def test_quantize_validation():
     bad.reserved = 1
     assert q1d(FAKE, 32, 64, 64, bad) == nv.ERR_UNSUPPORTED
     # 2D needs rows % 16 and block_rows 16
-    assert L.nvfp4_quantize_2d(FAKE, 24, 64, 64, ctypes.byref(qt(24, 64, 16)), FAKE, 4096,
+    assert L.nvfp4_quantize_2d(FAKE, 24, 64, 64, ctypes.byref(qt(24, 64, 16)), FAKE, 8192,
                                None) == nv.ERR_SHAPE
-    assert L.nvfp4_quantize_2d(FAKE, 32, 64, 64, ctypes.byref(qt(32, 64, 1)), FAKE, 4096,
+    assert L.nvfp4_quantize_2d(FAKE, 32, 64, 64, ctypes.byref(qt(32, 64, 1)), FAKE, 8192,
                                None) == nv.ERR_UNSUPPORTED
 
 
@@ -113,7 +113,7 @@ def test_gemm_validation():
     assert gemm(None, 64, 256, 0, qt(64, 256, 16), w) == nv.ERR_UNSUPPORTED
     assert gemm(None, 64, 256, 0, qt(60, 256), w) == nv.ERR_SHAPE
     assert gemm(FAKE, 64, 256, 256, None, w, ws=None) == nv.ERR_WORKSPACE
-    assert gemm(FAKE, 64, 256, 256, None, w, wsb=4096) == nv.ERR_WORKSPACE
+    assert gemm(FAKE, 64, 256, 256, None, w, wsb=8192) == nv.ERR_WORKSPACE
     assert gemm(FAKE + 8, 64, 256, 256, None, w) == nv.ERR_ALIGN
 
 

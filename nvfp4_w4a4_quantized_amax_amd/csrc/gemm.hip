@@ -13,6 +13,8 @@
 // The order of the K terms inside one MFMA is free (the dot product does not care), so each
 // lane loads 16 contiguous bytes (32 codes, two scale blocks) of one row per 64-wide K window
 // straight into registers and feeds them to four K=16 MFMAs; A and W use the same mapping.
+#include <stddef.h>
+
 #include "nvfp4_device.hpp"
 #include "launch.hpp"
 
@@ -95,24 +97,20 @@ __device__ __forceinline__ void load_window_masked(Frags<FM, FN> &fr,
 template <int FM, int FN>
 __device__ __forceinline__ void compute_window(const Frags<FM, FN> &fr,
                                                floatx16_t (&acc)[FM][FN]) {
-  half2_t sa[FM][2], sw[FN][2];
+  half2_t sa[FM], sw[FN];
 #pragma unroll
-  for (int f = 0; f < FM; ++f) {
-    sa[f][0] = scale_f16x2(fr.sa[f] & 0xFFu);
-    sa[f][1] = scale_f16x2(fr.sa[f] >> 8);
-  }
+  for (int f = 0; f < FM; ++f) sa[f] = scales_f16x2(fr.sa[f]);
 #pragma unroll
-  for (int g = 0; g < FN; ++g) {
-    sw[g][0] = scale_f16x2(fr.sw[g] & 0xFFu);
-    sw[g][1] = scale_f16x2(fr.sw[g] >> 8);
-  }
+  for (int g = 0; g < FN; ++g) sw[g] = scales_f16x2(fr.sw[g]);
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
     half8_t av[FM], bv[FN];
 #pragma unroll
-    for (int f = 0; f < FM; ++f) av[f] = decode8_f16(word(fr.a[f], kk), sa[f][kk >> 1]);
+    for (int f = 0; f < FM; ++f)
+      av[f] = decode8_f16(word(fr.a[f], kk), kk < 2 ? splat_lo(sa[f]) : splat_hi(sa[f]));
 #pragma unroll
-    for (int g = 0; g < FN; ++g) bv[g] = decode8_f16(word(fr.w[g], kk), sw[g][kk >> 1]);
+    for (int g = 0; g < FN; ++g)
+      bv[g] = decode8_f16(word(fr.w[g], kk), kk < 2 ? splat_lo(sw[g]) : splat_hi(sw[g]));
 #pragma unroll
     for (int f = 0; f < FM; ++f)
 #pragma unroll
@@ -209,6 +207,210 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_tile(DenseArgs p) {
   wave_tile_kloop<FM, FN>(a_row, a_srow, w_row, w_srow, p.k, kh, acc);
 
   const float alpha = (*p.a.gs) * (*p.w.gs);
+#pragma unroll
+  for (int f = 0; f < FM; ++f)
+#pragma unroll
+    for (int g = 0; g < FN; ++g) {
+      const int64_t col = n0 + g * 32 + lr;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t row = m0 + f * 32 + 8 * (r >> 2) + 4 * kh + (r & 3);
+        if (row < p.m && col < p.n)
+          p.y[row * p.ld_y + col] = (uint16_t)f32_to_bf16_rne(acc[f][g][r] * alpha);
+      }
+    }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Pipelined tile kernel (256 x 256 tiles, K a multiple of 64).  Packed codes and scales of each
+// 64-wide K window travel HBM -> LDS with direct global-to-LDS loads (no registers), kStages
+// windows deep; each wave then reads its fragments from LDS and decodes them in registers.
+// Per stage: A and W codes [row][32 bytes], A scales [row][4 bytes], W scales [row or band][4].
+// Every thread issues exactly kLoadsPerWindow load instructions per window, so the
+// vector-memory counter tells each wave when a window has landed.
+// ---------------------------------------------------------------------------------------------
+constexpr int kStages = 4;
+constexpr int kLoadsPerWindow = 6;
+
+struct LdsStage {
+  uint8_t a[256 * 32];
+  uint8_t w[256 * 32];
+  uint8_t as[256 * 4];
+  uint8_t ws[256 * 4];
+};
+
+typedef const void __attribute__((address_space(1))) *gptr_t;
+typedef void __attribute__((address_space(3))) *lptr_t;
+
+__device__ __forceinline__ void g2lds16(const uint8_t *g, void *l) {
+  __builtin_amdgcn_global_load_lds((gptr_t)g, (lptr_t)l, 16, 0, 0);
+}
+__device__ __forceinline__ void g2lds4(const uint8_t *g, void *l) {
+  __builtin_amdgcn_global_load_lds((gptr_t)g, (lptr_t)l, 4, 0, 0);
+}
+
+// s_waitcnt with only the vector-memory count constrained (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+__device__ __forceinline__ void wait_windows_left(int left) {
+  // loads still allowed in flight: `left` later windows (0 .. kStages - 2)
+  if (left >= 2) wait_vm<2 * kLoadsPerWindow>();
+  else if (left == 1) wait_vm<kLoadsPerWindow>();
+  else wait_vm<0>();
+}
+
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+
+// All fragments and scales of one window for one wave (4 A and 4 W fragments of 32 rows), read
+// from LDS in one asm block that also waits for them: the compiler cannot tell these reads from
+// the in-flight global-to-LDS loads of later stages and would otherwise wait for all of those.
+// The outputs are early-clobber: a read in flight must not land in a later read's address.
+// Fragment f of A is row (wm * 128 + f * 32 + lr), half kh: 1 KiB apart per f; its scale pair
+// is 128 bytes apart per f.  W scale pairs (16x16 tiles) are 8 bytes apart per g.
+template <bool W2D>
+__device__ __forceinline__ void read_stage_frags(const LdsStage &S, int wm, int wn, int lr, int kh,
+                                                 Frags<4, 4> &fr) {
+  const uint32_t base = (uint32_t)(uintptr_t)&S;
+  const uint32_t ra = wm * 128 + lr, rw = wn * 128 + lr;
+  const uint32_t pa = base + offsetof(LdsStage, a) + (ra * 2 + kh) * 16;
+  const uint32_t pw = base + offsetof(LdsStage, w) + (rw * 2 + kh) * 16;
+  const uint32_t pas = base + offsetof(LdsStage, as) + ra * 4 + kh * 2;
+  const uint32_t pws = base + offsetof(LdsStage, ws) +
+                       (W2D ? (wn * 8 + (lr >> 4)) * 4 + kh * 2 : rw * 4 + kh * 2);
+  u32x4_t a0, a1, a2, a3, w0, w1, w2, w3;
+  uint32_t sa0, sa1, sa2, sa3, sw0, sw1, sw2, sw3;
+  if (W2D) {
+    asm volatile(
+        "ds_read_b128 %0, %16\n"
+        "ds_read_b128 %1, %16 offset:1024\n"
+        "ds_read_b128 %2, %16 offset:2048\n"
+        "ds_read_b128 %3, %16 offset:3072\n"
+        "ds_read_b128 %4, %17\n"
+        "ds_read_b128 %5, %17 offset:1024\n"
+        "ds_read_b128 %6, %17 offset:2048\n"
+        "ds_read_b128 %7, %17 offset:3072\n"
+        "ds_read_u16 %8, %18\n"
+        "ds_read_u16 %9, %18 offset:128\n"
+        "ds_read_u16 %10, %18 offset:256\n"
+        "ds_read_u16 %11, %18 offset:384\n"
+        "ds_read_u16 %12, %19\n"
+        "ds_read_u16 %13, %19 offset:8\n"
+        "ds_read_u16 %14, %19 offset:16\n"
+        "ds_read_u16 %15, %19 offset:24\n"
+        "s_waitcnt lgkmcnt(0)\n"
+        : "=&v"(a0), "=&v"(a1), "=&v"(a2), "=&v"(a3), "=&v"(w0), "=&v"(w1), "=&v"(w2),
+          "=&v"(w3), "=&v"(sa0), "=&v"(sa1), "=&v"(sa2), "=&v"(sa3), "=&v"(sw0), "=&v"(sw1),
+          "=&v"(sw2), "=&v"(sw3)
+        : "v"(pa), "v"(pw), "v"(pas), "v"(pws)
+        : "memory");
+  } else {
+    asm volatile(
+        "ds_read_b128 %0, %16\n"
+        "ds_read_b128 %1, %16 offset:1024\n"
+        "ds_read_b128 %2, %16 offset:2048\n"
+        "ds_read_b128 %3, %16 offset:3072\n"
+        "ds_read_b128 %4, %17\n"
+        "ds_read_b128 %5, %17 offset:1024\n"
+        "ds_read_b128 %6, %17 offset:2048\n"
+        "ds_read_b128 %7, %17 offset:3072\n"
+        "ds_read_u16 %8, %18\n"
+        "ds_read_u16 %9, %18 offset:128\n"
+        "ds_read_u16 %10, %18 offset:256\n"
+        "ds_read_u16 %11, %18 offset:384\n"
+        "ds_read_u16 %12, %19\n"
+        "ds_read_u16 %13, %19 offset:128\n"
+        "ds_read_u16 %14, %19 offset:256\n"
+        "ds_read_u16 %15, %19 offset:384\n"
+        "s_waitcnt lgkmcnt(0)\n"
+        : "=&v"(a0), "=&v"(a1), "=&v"(a2), "=&v"(a3), "=&v"(w0), "=&v"(w1), "=&v"(w2),
+          "=&v"(w3), "=&v"(sa0), "=&v"(sa1), "=&v"(sa2), "=&v"(sa3), "=&v"(sw0), "=&v"(sw1),
+          "=&v"(sw2), "=&v"(sw3)
+        : "v"(pa), "v"(pw), "v"(pas), "v"(pws)
+        : "memory");
+  }
+  fr.a[0] = make_uint4(a0[0], a0[1], a0[2], a0[3]);
+  fr.a[1] = make_uint4(a1[0], a1[1], a1[2], a1[3]);
+  fr.a[2] = make_uint4(a2[0], a2[1], a2[2], a2[3]);
+  fr.a[3] = make_uint4(a3[0], a3[1], a3[2], a3[3]);
+  fr.w[0] = make_uint4(w0[0], w0[1], w0[2], w0[3]);
+  fr.w[1] = make_uint4(w1[0], w1[1], w1[2], w1[3]);
+  fr.w[2] = make_uint4(w2[0], w2[1], w2[2], w2[3]);
+  fr.w[3] = make_uint4(w3[0], w3[1], w3[2], w3[3]);
+  fr.sa[0] = sa0; fr.sa[1] = sa1; fr.sa[2] = sa2; fr.sa[3] = sa3;
+  fr.sw[0] = sw0; fr.sw[1] = sw1; fr.sw[2] = sw2; fr.sw[3] = sw3;
+}
+
+template <bool W2D>
+__global__ __launch_bounds__(kGemmThreads) void k_gemm_lds(DenseArgs p) {
+  constexpr int FM = 4, FN = 4, BM = 256, BN = 256;
+  static_assert(kStages == 4, "wait_windows_left assumes four stages");
+  __shared__ LdsStage st[kStages];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int lr = lane & 31, kh = lane >> 5;
+
+  const int logical = xcd_logical(blockIdx.x, gridDim.x);
+  const int in_group = kGroupM * p.tiles_n;
+  const int first_m = (logical / in_group) * kGroupM;
+  const int gsz = min(p.tiles_m - first_m, kGroupM);
+  const int tm = first_m + (logical % in_group) % gsz;
+  const int tn = (logical % in_group) / gsz;
+  const int64_t m_tile = (int64_t)tm * BM, n_tile = (int64_t)tn * BN;
+
+  // This thread's share of every window's loads (rows clamped into the matrix; results of
+  // clamped rows are never stored).
+  const uint8_t *ga[2], *gw[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int c = i * 256 + tid, row = c >> 1, half = c & 1;
+    ga[i] = p.a.codes + min(m_tile + row, p.m - 1) * p.a.ld_codes + half * 16;
+    gw[i] = p.w.codes + min(n_tile + row, p.n - 1) * p.w.ld_codes + half * 16;
+  }
+  const uint8_t *gas = p.a.scales + min(m_tile + tid, p.m - 1) * p.a.ld_scales;
+  const uint8_t *gws = W2D ? p.w.scales + min(n_tile / 16 + (lane & 15), p.n / 16 - 1) * p.w.ld_scales
+                           : p.w.scales + min(n_tile + tid, p.n - 1) * p.w.ld_scales;
+  auto issue = [&](int64_t win, int s) {
+    LdsStage &S = st[s];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      g2lds16(ga[i] + win * 32, S.a + (i * 256 + wave * 64) * 16);
+      g2lds16(gw[i] + win * 32, S.w + (i * 256 + wave * 64) * 16);
+    }
+    g2lds4(gas + win * 4, S.as + wave * 64 * 4);
+    if (W2D) {
+      if (lane < 16) g2lds4(gws + win * 4, S.ws);  // every wave writes the same 64 bytes
+    } else {
+      g2lds4(gws + win * 4, S.ws + wave * 64 * 4);
+    }
+  };
+
+  floatx16_t acc[FM][FN];
+#pragma unroll
+  for (int f = 0; f < FM; ++f)
+#pragma unroll
+    for (int g = 0; g < FN; ++g) acc[f][g] = floatx16_t{};
+
+  const int64_t nwin = p.k / 64;
+  for (int64_t w = 0; w < kStages - 1 && w < nwin; ++w) issue(w, (int)w);
+  for (int64_t w = 0; w < nwin; ++w) {
+    const int64_t later = min((int64_t)kStages - 2, nwin - 1 - w);
+    // This wave's loads of window w are done once at most `later` windows remain in flight;
+    // the barrier then makes window w complete for every wave and frees stage (w - 1).
+    // A plain s_barrier (no fence): the compiler's fence would wait for every load in flight.
+    wait_windows_left((int)later);
+    __builtin_amdgcn_s_barrier();
+    if (w + kStages - 1 < nwin) issue(w + kStages - 1, (int)((w + kStages - 1) % kStages));
+    Frags<FM, FN> fr;
+    read_stage_frags<W2D>(st[w % kStages], wm, wn, lr, kh, fr);
+    compute_window(fr, acc);
+  }
+
+  const float alpha = (*p.a.gs) * (*p.w.gs);
+  const int64_t m0 = m_tile + wm * 32 * FM, n0 = n_tile + wn * 32 * FN;
 #pragma unroll
   for (int f = 0; f < FM; ++f)
 #pragma unroll
@@ -403,8 +605,9 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_small_m(SmallMArgs p) {
     }
 #pragma unroll
     for (int u = 0; u < kSmallMWin; ++u) {
-      const half2_t sw0 = scale_f16x2(ws_[u] & 0xFFu), sw1 = scale_f16x2(ws_[u] >> 8);
-      const half2_t sa0 = scale_f16x2(as_[u] & 0xFFu), sa1 = scale_f16x2(as_[u] >> 8);
+      const half2_t swp = scales_f16x2(ws_[u]), sap = scales_f16x2(as_[u]);
+      const half2_t sw0 = splat_lo(swp), sw1 = splat_hi(swp);
+      const half2_t sa0 = splat_lo(sap), sa1 = splat_hi(sap);
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
         const half8_t wop = decode8_f16(word(wv[u], kk), kk < 2 ? sw0 : sw1);
@@ -454,11 +657,32 @@ static hipError_t launch_tile_fm(const GemmOperand &a, const GemmOperand &w, int
   return hipGetLastError();
 }
 
+static bool aligned4(const void *q) { return ((uintptr_t)q & 3u) == 0; }
+
 hipError_t launch_gemm_tile(const GemmOperand &a, const GemmOperand &w, int64_t m, int64_t n,
                             int64_t k, uint16_t *y, int64_t ld_y, hipStream_t stream) {
   if (m <= 64) return launch_tile_fm<1, 4>(a, w, m, n, k, y, ld_y, stream);
   if (m <= 128) return launch_tile_fm<2, 4>(a, w, m, n, k, y, ld_y, stream);
-  return launch_tile_fm<4, 4>(a, w, m, n, k, y, ld_y, stream);
+  // The pipelined kernel needs whole 64-wide K windows and 4-byte aligned scale rows.
+  const bool lds_ok = (k % 64 == 0) && aligned4(a.scales) && aligned4(w.scales) &&
+                      (a.ld_scales % 4 == 0) && (w.ld_scales % 4 == 0);
+  if (!lds_ok) return launch_tile_fm<4, 4>(a, w, m, n, k, y, ld_y, stream);
+  DenseArgs p;
+  p.a = a;
+  p.w = w;
+  p.m = m;
+  p.n = n;
+  p.k = k;
+  p.y = y;
+  p.ld_y = ld_y;
+  p.tiles_m = (int)((m + 255) / 256);
+  p.tiles_n = (int)((n + 255) / 256);
+  const unsigned grid = (unsigned)p.tiles_m * (unsigned)p.tiles_n;
+  if (w.block_rows == 16)
+    hipLaunchKernelGGL(k_gemm_lds<true>, dim3(grid), dim3(kGemmThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL(k_gemm_lds<false>, dim3(grid), dim3(kGemmThreads), 0, stream, p);
+  return hipGetLastError();
 }
 
 hipError_t launch_gemm_small_m(const GemmOperand &a, const GemmOperand &w, int64_t m, int64_t n,

@@ -340,4 +340,19 @@ __device__ __forceinline__ half2_t scale_f16x2(uint32_t b) {
   return r;
 }
 
+// Two E4M3 scale bytes (low byte first) -> fp16 pair, exact (OCP E4M3 values are fp16 values),
+// with the hardware FP8 conversion (unit scale).
+__device__ __forceinline__ half2_t scales_f16x2(uint32_t two_bytes) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(two_bytes, 1.0f, false);
+}
+
+__device__ __forceinline__ half2_t splat_lo(half2_t v) {
+  half2_t r = {v[0], v[0]};
+  return r;
+}
+__device__ __forceinline__ half2_t splat_hi(half2_t v) {
+  half2_t r = {v[1], v[1]};
+  return r;
+}
+
 }  // namespace nvfp4

@@ -13,7 +13,6 @@
 // The order of the K terms inside one MFMA is free (the dot product does not care), so each
 // lane loads 16 contiguous bytes (32 codes, two scale blocks) of one row per 64-wide K window
 // straight into registers and feeds them to four K=16 MFMAs; A and W use the same mapping.
-#include <stddef.h>
 
 #include "nvfp4_device.hpp"
 #include "launch.hpp"
@@ -223,15 +222,16 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_tile(DenseArgs p) {
 
 // ---------------------------------------------------------------------------------------------
 // Pipelined tile kernel (256 x 256 tiles, K a multiple of 64).  Packed codes and scales of each
-// 64-wide K window travel HBM -> LDS with direct global-to-LDS loads (no registers), kStages
-// windows deep; each wave then reads its fragments from LDS and decodes them in registers.
-// Per stage: A and W codes [row][32 bytes], A scales [row][4 bytes], W scales [row or band][4].
-// Every thread issues exactly kLoadsPerWindow load instructions per window, so the
-// vector-memory counter tells each wave when a window has landed.
+// 64-wide K window are loaded from HBM into registers two windows ahead, written to one of two
+// LDS stages one window ahead, and read back by the waves that use them (each 32-row fragment
+// of A or W is used by two of the four waves).  All LDS traffic is ordinary loads and stores,
+// so the compiler places the waits for it where the data is first used.
+// Per stage: A and W codes [row][32 bytes], A scales [row][4 bytes], W scales [row][4 bytes]
+// (1D) or one copy per wave of the 16 band rows (2D).  The two 16-byte halves of a code row
+// are swapped on rows where bit 2 xor bit 3 of the row is set: a fragment read (one half of 8
+// or 16 consecutive rows per LDS cycle) then covers every bank once, and a store of 16
+// consecutive chunks still fills 256 contiguous bytes.
 // ---------------------------------------------------------------------------------------------
-constexpr int kStages = 4;
-constexpr int kLoadsPerWindow = 6;
-
 struct LdsStage {
   uint8_t a[256 * 32];
   uint8_t w[256 * 32];
@@ -239,116 +239,136 @@ struct LdsStage {
   uint8_t ws[256 * 4];
 };
 
-typedef const void __attribute__((address_space(1))) *gptr_t;
-typedef void __attribute__((address_space(3))) *lptr_t;
-
-__device__ __forceinline__ void g2lds16(const uint8_t *g, void *l) {
-  __builtin_amdgcn_global_load_lds((gptr_t)g, (lptr_t)l, 16, 0, 0);
-}
-__device__ __forceinline__ void g2lds4(const uint8_t *g, void *l) {
-  __builtin_amdgcn_global_load_lds((gptr_t)g, (lptr_t)l, 4, 0, 0);
-}
-
-// s_waitcnt with only the vector-memory count constrained (gfx9 encoding).
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt field");
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
-
-__device__ __forceinline__ void wait_windows_left(int left) {
-  // loads still allowed in flight: `left` later windows (0 .. kStages - 2)
-  if (left >= 2) wait_vm<2 * kLoadsPerWindow>();
-  else if (left == 1) wait_vm<kLoadsPerWindow>();
-  else wait_vm<0>();
-}
-
+// One thread's share of a window: chunk c = i * 256 + tid of A and of W (row c / 2, 16-byte
+// half c % 2), and the 4 scale bytes of A row tid and of W row tid (1D) or band tid % 16 (2D).
 typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+struct WindowRegs {
+  u32x4_t a0, a1, w0, w1;
+  uint32_t as, ws;
+};
 
-// All fragments and scales of one window for one wave (4 A and 4 W fragments of 32 rows), read
-// from LDS in one asm block that also waits for them: the compiler cannot tell these reads from
-// the in-flight global-to-LDS loads of later stages and would otherwise wait for all of those.
-// The outputs are early-clobber: a read in flight must not land in a later read's address.
-// Fragment f of A is row (wm * 128 + f * 32 + lr), half kh: 1 KiB apart per f; its scale pair
-// is 128 bytes apart per f.  W scale pairs (16x16 tiles) are 8 bytes apart per g.
-template <bool W2D>
-__device__ __forceinline__ void read_stage_frags(const LdsStage &S, int wm, int wn, int lr, int kh,
-                                                 Frags<4, 4> &fr) {
-  const uint32_t base = (uint32_t)(uintptr_t)&S;
-  const uint32_t ra = wm * 128 + lr, rw = wn * 128 + lr;
-  const uint32_t pa = base + offsetof(LdsStage, a) + (ra * 2 + kh) * 16;
-  const uint32_t pw = base + offsetof(LdsStage, w) + (rw * 2 + kh) * 16;
-  const uint32_t pas = base + offsetof(LdsStage, as) + ra * 4 + kh * 2;
-  const uint32_t pws = base + offsetof(LdsStage, ws) +
-                       (W2D ? (wn * 8 + (lr >> 4)) * 4 + kh * 2 : rw * 4 + kh * 2);
-  u32x4_t a0, a1, a2, a3, w0, w1, w2, w3;
-  uint32_t sa0, sa1, sa2, sa3, sw0, sw1, sw2, sw3;
-  if (W2D) {
-    asm volatile(
-        "ds_read_b128 %0, %16\n"
-        "ds_read_b128 %1, %16 offset:1024\n"
-        "ds_read_b128 %2, %16 offset:2048\n"
-        "ds_read_b128 %3, %16 offset:3072\n"
-        "ds_read_b128 %4, %17\n"
-        "ds_read_b128 %5, %17 offset:1024\n"
-        "ds_read_b128 %6, %17 offset:2048\n"
-        "ds_read_b128 %7, %17 offset:3072\n"
-        "ds_read_u16 %8, %18\n"
-        "ds_read_u16 %9, %18 offset:128\n"
-        "ds_read_u16 %10, %18 offset:256\n"
-        "ds_read_u16 %11, %18 offset:384\n"
-        "ds_read_u16 %12, %19\n"
-        "ds_read_u16 %13, %19 offset:8\n"
-        "ds_read_u16 %14, %19 offset:16\n"
-        "ds_read_u16 %15, %19 offset:24\n"
-        "s_waitcnt lgkmcnt(0)\n"
-        : "=&v"(a0), "=&v"(a1), "=&v"(a2), "=&v"(a3), "=&v"(w0), "=&v"(w1), "=&v"(w2),
-          "=&v"(w3), "=&v"(sa0), "=&v"(sa1), "=&v"(sa2), "=&v"(sa3), "=&v"(sw0), "=&v"(sw1),
-          "=&v"(sw2), "=&v"(sw3)
-        : "v"(pa), "v"(pw), "v"(pas), "v"(pws)
-        : "memory");
-  } else {
-    asm volatile(
-        "ds_read_b128 %0, %16\n"
-        "ds_read_b128 %1, %16 offset:1024\n"
-        "ds_read_b128 %2, %16 offset:2048\n"
-        "ds_read_b128 %3, %16 offset:3072\n"
-        "ds_read_b128 %4, %17\n"
-        "ds_read_b128 %5, %17 offset:1024\n"
-        "ds_read_b128 %6, %17 offset:2048\n"
-        "ds_read_b128 %7, %17 offset:3072\n"
-        "ds_read_u16 %8, %18\n"
-        "ds_read_u16 %9, %18 offset:128\n"
-        "ds_read_u16 %10, %18 offset:256\n"
-        "ds_read_u16 %11, %18 offset:384\n"
-        "ds_read_u16 %12, %19\n"
-        "ds_read_u16 %13, %19 offset:128\n"
-        "ds_read_u16 %14, %19 offset:256\n"
-        "ds_read_u16 %15, %19 offset:384\n"
-        "s_waitcnt lgkmcnt(0)\n"
-        : "=&v"(a0), "=&v"(a1), "=&v"(a2), "=&v"(a3), "=&v"(w0), "=&v"(w1), "=&v"(w2),
-          "=&v"(w3), "=&v"(sa0), "=&v"(sa1), "=&v"(sa2), "=&v"(sa3), "=&v"(sw0), "=&v"(sw1),
-          "=&v"(sw2), "=&v"(sw3)
-        : "v"(pa), "v"(pw), "v"(pas), "v"(pws)
-        : "memory");
-  }
-  fr.a[0] = make_uint4(a0[0], a0[1], a0[2], a0[3]);
-  fr.a[1] = make_uint4(a1[0], a1[1], a1[2], a1[3]);
-  fr.a[2] = make_uint4(a2[0], a2[1], a2[2], a2[3]);
-  fr.a[3] = make_uint4(a3[0], a3[1], a3[2], a3[3]);
-  fr.w[0] = make_uint4(w0[0], w0[1], w0[2], w0[3]);
-  fr.w[1] = make_uint4(w1[0], w1[1], w1[2], w1[3]);
-  fr.w[2] = make_uint4(w2[0], w2[1], w2[2], w2[3]);
-  fr.w[3] = make_uint4(w3[0], w3[1], w3[2], w3[3]);
-  fr.sa[0] = sa0; fr.sa[1] = sa1; fr.sa[2] = sa2; fr.sa[3] = sa3;
-  fr.sw[0] = sw0; fr.sw[1] = sw1; fr.sw[2] = sw2; fr.sw[3] = sw3;
+__device__ __forceinline__ void load_window_regs(WindowRegs &r, const uint8_t *const (&ga)[2],
+                                                 const uint8_t *const (&gw)[2],
+                                                 const uint8_t *gas, const uint8_t *gws,
+                                                 int64_t win) {
+  r.a0 = *(const u32x4_t *)(ga[0] + win * 32);
+  r.a1 = *(const u32x4_t *)(ga[1] + win * 32);
+  r.w0 = *(const u32x4_t *)(gw[0] + win * 32);
+  r.w1 = *(const u32x4_t *)(gw[1] + win * 32);
+  r.as = *(const uint32_t *)(gas + win * 4);
+  r.ws = *(const uint32_t *)(gws + win * 4);
+}
+
+// Byte offset of half `h` of code row `row` in a stage.
+__device__ __forceinline__ int code_offset(int row, int h) {
+  return row * 32 + ((h ^ (row >> 2) ^ (row >> 3)) & 1) * 16;
+}
+
+__device__ __forceinline__ void store_window_regs(const WindowRegs &r, LdsStage &S, int tid) {
+  // chunk c = i * 256 + tid is half c % 2 of row c / 2
+  const int o0 = code_offset(tid >> 1, tid & 1), o1 = code_offset(128 + (tid >> 1), tid & 1);
+  *(u32x4_t *)(S.a + o0) = r.a0;
+  *(u32x4_t *)(S.a + o1) = r.a1;
+  *(u32x4_t *)(S.w + o0) = r.w0;
+  *(u32x4_t *)(S.w + o1) = r.w1;
+  *(uint32_t *)(S.as + tid * 4) = r.as;
+  *(uint32_t *)(S.ws + tid * 4) = r.ws;
+}
+
+// Wait for this wave's LDS stores, then for every wave of the workgroup.  The asm's memory
+// clobber keeps the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 template <bool W2D>
-__global__ __launch_bounds__(kGemmThreads) void k_gemm_lds(DenseArgs p) {
-  constexpr int FM = 4, FN = 4, BM = 256, BN = 256;
-  static_assert(kStages == 4, "wait_windows_left assumes four stages");
-  __shared__ LdsStage st[kStages];
+__device__ __forceinline__ void read_stage_frags(const LdsStage &S, int wave, int wm, int wn,
+                                                 int lr, int kh, Frags<4, 4> &fr) {
+  const int ra = wm * 128 + lr, rw = wn * 128 + lr;
+#pragma unroll
+  for (int f = 0; f < 4; ++f) {
+    fr.a[f] = *(const uint4 *)(S.a + code_offset(ra + f * 32, kh));
+    fr.sa[f] = *(const uint16_t *)(S.as + (ra + f * 32) * 4 + kh * 2);
+  }
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    fr.w[g] = *(const uint4 *)(S.w + code_offset(rw + g * 32, kh));
+    fr.sw[g] = W2D ? *(const uint16_t *)(S.ws + wave * 256 + (wn * 8 + g * 2 + (lr >> 4)) * 4 +
+                                         kh * 2)
+                   : *(const uint16_t *)(S.ws + (rw + g * 32) * 4 + kh * 2);
+  }
+}
+
+// Decoded operands of one K=16 step: 4 A fragments then 4 W fragments (8 fp16 each).
+struct StepOps {
+  half8_t v[8];
+};
+
+__device__ __forceinline__ void window_scales(const Frags<4, 4> &fr, half2_t (&sa)[4],
+                                              half2_t (&sw)[4]) {
+#pragma unroll
+  for (int f = 0; f < 4; ++f) sa[f] = scales_f16x2(fr.sa[f]);
+#pragma unroll
+  for (int g = 0; g < 4; ++g) sw[g] = scales_f16x2(fr.sw[g]);
+}
+
+// Step kk (0..3) uses code word kk of every fragment; words 0-1 belong to the lane's first
+// scale block, words 2-3 to its second.
+__device__ __forceinline__ void decode_step(const Frags<4, 4> &fr, const half2_t (&sa)[4],
+                                            const half2_t (&sw)[4], int kk, StepOps &d) {
+#pragma unroll
+  for (int f = 0; f < 4; ++f)
+    d.v[f] = decode8_f16(word(fr.a[f], kk), kk < 2 ? splat_lo(sa[f]) : splat_hi(sa[f]));
+#pragma unroll
+  for (int g = 0; g < 4; ++g)
+    d.v[4 + g] = decode8_f16(word(fr.w[g], kk), kk < 2 ? splat_lo(sw[g]) : splat_hi(sw[g]));
+}
+
+__device__ __forceinline__ void mfma_step(const StepOps &d, floatx16_t (&acc)[4][4]) {
+#pragma unroll
+  for (int f = 0; f < 4; ++f)
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+      acc[f][g] = __builtin_amdgcn_mfma_f32_32x32x16_f16(d.v[f], d.v[4 + g], acc[f][g], 0, 0, 0);
+}
+
+// Ask the scheduler to alternate one MFMA with four VALU instructions (the decode of the next
+// step), so that the conversions run while the matrix core works.
+__device__ __forceinline__ void interleave_step() {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+  }
+}
+
+// Step with memory work: each of the first `nmem` MFMAs is followed by one instruction of the
+// memory kind `mem_mask` (0x020 vector-memory read, 0x100 LDS read, 0x200 LDS write) besides
+// its four VALU instructions, so that a burst of memory instructions never blocks the wave.
+template <int MEM_MASK, int NMEM, int MEM_MASK2 = 0, int NMEM2 = 0>
+__device__ __forceinline__ void interleave_step_mem() {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if (i < NMEM) __builtin_amdgcn_sched_group_barrier(MEM_MASK, 1, 0);
+    if (i < NMEM2) __builtin_amdgcn_sched_group_barrier(MEM_MASK2, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+  }
+}
+
+// Ends a step: nothing moves across this point, and the step's operands stay live until here.
+// Without this the register allocator hands an MFMA's source registers to the next step's
+// decode as soon as the last MFMA reading them has issued; the VALU write then waits for the
+// MFMA, and decode and matrix work no longer overlap.
+__device__ __forceinline__ void end_step(const StepOps &d) {
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) asm volatile("" ::"v"(d.v[i]));
+}
+
+template <bool W2D>
+__global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_gemm_lds(DenseArgs p) {
+  __shared__ __align__(16) LdsStage st[2];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int lr = lane & 31, kh = lane >> 5;
@@ -359,7 +379,7 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_lds(DenseArgs p) {
   const int gsz = min(p.tiles_m - first_m, kGroupM);
   const int tm = first_m + (logical % in_group) % gsz;
   const int tn = (logical % in_group) / gsz;
-  const int64_t m_tile = (int64_t)tm * BM, n_tile = (int64_t)tn * BN;
+  const int64_t m_tile = (int64_t)tm * 256, n_tile = (int64_t)tn * 256;
 
   // This thread's share of every window's loads (rows clamped into the matrix; results of
   // clamped rows are never stored).
@@ -373,53 +393,81 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_lds(DenseArgs p) {
   const uint8_t *gas = p.a.scales + min(m_tile + tid, p.m - 1) * p.a.ld_scales;
   const uint8_t *gws = W2D ? p.w.scales + min(n_tile / 16 + (lane & 15), p.n / 16 - 1) * p.w.ld_scales
                            : p.w.scales + min(n_tile + tid, p.n - 1) * p.w.ld_scales;
-  auto issue = [&](int64_t win, int s) {
-    LdsStage &S = st[s];
+  const int64_t nwin = p.k / 64;  // >= 1
+  // Window `win` is clamped to the last one so that the loop has no branch (a clamped load is
+  // never stored).
+  floatx16_t acc[4][4];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      g2lds16(ga[i] + win * 32, S.a + (i * 256 + wave * 64) * 16);
-      g2lds16(gw[i] + win * 32, S.w + (i * 256 + wave * 64) * 16);
-    }
-    g2lds4(gas + win * 4, S.as + wave * 64 * 4);
-    if (W2D) {
-      if (lane < 16) g2lds4(gws + win * 4, S.ws);  // every wave writes the same 64 bytes
-    } else {
-      g2lds4(gws + win * 4, S.ws + wave * 64 * 4);
-    }
-  };
+  for (int f = 0; f < 4; ++f)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) acc[f][g] = floatx16_t{};
 
-  floatx16_t acc[FM][FN];
-#pragma unroll
-  for (int f = 0; f < FM; ++f)
-#pragma unroll
-    for (int g = 0; g < FN; ++g) acc[f][g] = floatx16_t{};
+  // Window 0 goes to stage 0 and window 1 stays in registers.  At the start of window w,
+  // window w + 1 is stored to stage (w + 1) % 2 (every wave finished reading it before the
+  // previous barrier) and window w + 2 is loaded; after the barrier in the middle of window w,
+  // window w + 1 is read back.
+  WindowRegs r;
+  load_window_regs(r, ga, gw, gas, gws, 0);
+  store_window_regs(r, st[0], tid);
+  load_window_regs(r, ga, gw, gas, gws, min((int64_t)1, nwin - 1));
+  lds_barrier();
+  Frags<4, 4> cur, nxt;
+  read_stage_frags<W2D>(st[0], wave, wm, wn, lr, kh, cur);
+  half2_t sa[4], sw[4];
+  window_scales(cur, sa, sw);
+  StepOps ev, od;
+  decode_step(cur, sa, sw, 0, ev);
 
-  const int64_t nwin = p.k / 64;
-  for (int64_t w = 0; w < kStages - 1 && w < nwin; ++w) issue(w, (int)w);
-  for (int64_t w = 0; w < nwin; ++w) {
-    const int64_t later = min((int64_t)kStages - 2, nwin - 1 - w);
-    // This wave's loads of window w are done once at most `later` windows remain in flight;
-    // the barrier then makes window w complete for every wave and frees stage (w - 1).
-    // A plain s_barrier (no fence): the compiler's fence would wait for every load in flight.
-    wait_windows_left((int)later);
-    __builtin_amdgcn_s_barrier();
-    if (w + kStages - 1 < nwin) issue(w + kStages - 1, (int)((w + kStages - 1) % kStages));
-    Frags<FM, FN> fr;
-    read_stage_frags<W2D>(st[w % kStages], wm, wn, lr, kh, fr);
-    compute_window(fr, acc);
+  for (int64_t w = 0; w + 1 < nwin; ++w) {
+    store_window_regs(r, st[(w + 1) & 1], tid);
+    load_window_regs(r, ga, gw, gas, gws, min(w + 2, nwin - 1));
+    decode_step(cur, sa, sw, 1, od);
+    mfma_step(ev, acc);
+    interleave_step_mem<0x200, 6, 0x020, 6>();
+    end_step(ev);
+    lds_barrier();
+    read_stage_frags<W2D>(st[(w + 1) & 1], wave, wm, wn, lr, kh, nxt);
+    decode_step(cur, sa, sw, 2, ev);
+    mfma_step(od, acc);
+    interleave_step_mem<0x100, 16>();
+    end_step(od);
+    decode_step(cur, sa, sw, 3, od);
+    mfma_step(ev, acc);
+    interleave_step();
+    end_step(ev);
+    window_scales(nxt, sa, sw);
+    decode_step(nxt, sa, sw, 0, ev);
+    mfma_step(od, acc);
+    interleave_step();
+    end_step(od);
+    cur = nxt;
   }
+  decode_step(cur, sa, sw, 1, od);
+  mfma_step(ev, acc);
+  interleave_step();
+  end_step(ev);
+  decode_step(cur, sa, sw, 2, ev);
+  mfma_step(od, acc);
+  interleave_step();
+  end_step(od);
+  decode_step(cur, sa, sw, 3, od);
+  mfma_step(ev, acc);
+  interleave_step();
+  end_step(ev);
+  mfma_step(od, acc);
 
   const float alpha = (*p.a.gs) * (*p.w.gs);
-  const int64_t m0 = m_tile + wm * 32 * FM, n0 = n_tile + wn * 32 * FN;
+  const int64_t m0 = m_tile + wm * 128, n0 = n_tile + wn * 128;
+  const bool full = m_tile + 256 <= p.m && n_tile + 256 <= p.n;
 #pragma unroll
-  for (int f = 0; f < FM; ++f)
+  for (int f = 0; f < 4; ++f)
 #pragma unroll
-    for (int g = 0; g < FN; ++g) {
+    for (int g = 0; g < 4; ++g) {
       const int64_t col = n0 + g * 32 + lr;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int64_t row = m0 + f * 32 + 8 * (r >> 2) + 4 * kh + (r & 3);
-        if (row < p.m && col < p.n)
+        if (full || (row < p.m && col < p.n))
           p.y[row * p.ld_y + col] = (uint16_t)f32_to_bf16_rne(acc[f][g][r] * alpha);
       }
     }

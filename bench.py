@@ -38,6 +38,9 @@ def parse():
     p.add_argument("--no-extra", action="store_true", help="headline workload only")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--only", default="", help="comma list of extra workloads to run")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="after the headline, run 5 plain device copies of the 128 MiB input "
+                        "(reference dispatches for scaling the FETCH_SIZE / WRITE_SIZE counters)")
     return p.parse_args()
 
 
@@ -77,7 +80,48 @@ def headline(args, torch, np, nv, W):
     ms = timed(step, args.steps, args.warmup, torch)
     nbytes = rows * cols * 2 + rows * cols // 2 + rows * cols // 16 + 4
     gbs = nbytes / (ms * 1e-3) / 1e9
+    if args.copy_calibration:
+        dst = torch.empty_like(x0)
+        for i in range(5):
+            dst.copy_(xs[i % nbuf])
+        torch.cuda.synchronize()
     return {"ms": ms, "bytes": nbytes, "gbs": gbs, "x_host": x_host}
+
+
+TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                            "k_quantize_persistent_activation_8192x8192_traffic.md")
+QUANTIZE_SOURCES = ("quantize.hip", "nvfp4_device.hpp", "api.hip")
+
+
+def quantize_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(os.path.dirname(os.path.abspath(__file__)), "nvfp4_w4a4_quantized_amax_amd",
+                        "csrc")
+    for name in QUANTIZE_SOURCES:
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per launch of the headline kernel from the committed counter summary, or None
+    when there is none or the kernel sources changed since the counters were taken."""
+    try:
+        text = open(TRAFFIC_FILE).read()
+    except OSError:
+        return None
+    fields = {}
+    for line in text.splitlines():
+        if line.startswith("- ") and ": " in line:
+            k, v = line[2:].split(": ", 1)
+            fields[k.strip()] = v.strip().strip("`")
+    if fields.get("source_sha256") != quantize_source_hash():
+        return None
+    try:
+        return int(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def extra_workloads(args, torch, np, nv, W, only):
@@ -195,7 +239,7 @@ def main():
                                "seed 1) -> NVFP4 1D-16", "rows": 8192, "cols": 8192,
                    "global_batch": 8192, "seq_len": 8192, "parallelism": "none"},
         "roofline": {"bound": "hbm", "achieved": h["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": h["gbs"] / HBM_PEAK_GBS, "traffic": None,
+                     "frac": h["gbs"] / HBM_PEAK_GBS, "traffic": measured_traffic(),
                      "kernel": "k_quantize_persistent (nvfp4_quantize_1d, single-read path)",
                      "algorithmic_bytes_per_launch": h["bytes"]},
     }

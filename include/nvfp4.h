@@ -103,6 +103,9 @@ size_t nvfp4_grouped_gemm_workspace_bytes(int64_t tokens, int64_t k, int64_t tot
  *   out    : out->codes / scales / global_scale receive the result; out->rows == rows,
  *            out->cols == cols, out->block_rows == 1; codes 16-byte aligned, ld_codes % 16 == 0.
  * Computes amax (pass 1) then block scales and codes (pass 2).  cols % 16 == 0.
+ * Large tensors run as one workgroup per compute unit that read the tensor once and wait for
+ * each other between the passes; should other work on the device keep some of them from
+ * starting for about a second, the call writes NaN as the global scale instead of hanging.
  * ------------------------------------------------------------------------------------------- */
 nvfp4_status nvfp4_quantize_1d(const void *x, int64_t rows, int64_t cols, int64_t ld_x,
                                const nvfp4_tensor *out, void *ws, size_t ws_bytes, void *stream);

@@ -196,14 +196,17 @@ __global__ __launch_bounds__(kQThreads) void k_encode_1d(const uint4 *__restrict
 }
 
 // ---------------------------------------------------------------------------------------------
-// Single-read path: one persistent workgroup per CU (cooperative launch, so all are resident).
-// Phase 1 reads each wave's tiles once, keeping the first RT of them in registers, and publishes
-// the workgroup's partial max.  A grid barrier without read-modify-write atomics follows: every
-// workgroup stores (epoch << 16 | max) into its own 64-bit slot, and one wave per workgroup
-// polls all slots until every slot carries this call's epoch (a per-call 48-bit number, so stale slots never match).  The poll is bounded; if it ever
-// ran out, the call's outputs would be wrong but the kernel still ends.  Phase 2 builds the tables
-// and encodes the register-resident tiles without touching memory again; tiles beyond RT per wave
-// are read a second time.
+// Single-read path: one persistent workgroup per CU.  It is launched only when the occupancy
+// query shows that one such workgroup fits on every CU, so all of them become resident (at the
+// latest when other work on the device drains).  Phase 1 reads each wave's tiles once, keeping
+// the first RT of them in registers and the next LT in LDS, and publishes the workgroup's
+// partial max.  A grid barrier without read-modify-write atomics follows: every workgroup
+// stores (epoch << 16 | max) into its own 64-bit slot, and one wave per workgroup polls all
+// slots until every slot carries this call's epoch (a per-call 48-bit number, so stale slots
+// never match).  The poll is bounded; if it ever ran out, the global scale is written as NaN
+// and a status word is set, but the kernel still ends.  Phase 2 builds the tables and encodes
+// the resident tiles without touching memory again; tiles beyond RT + LT per wave are read a
+// second time.
 // ---------------------------------------------------------------------------------------------
 constexpr uint32_t kSpinLimit = 1u << 20;
 

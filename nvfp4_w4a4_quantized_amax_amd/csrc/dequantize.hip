@@ -37,16 +37,18 @@ __global__ __launch_bounds__(256) void k_dequantize(const uint8_t *__restrict__ 
       v[2 * j + 1] = (g[j][1] * sb) * gs;
     }
     if (OUT_F32) {
-      float4 *p = (float4 *)((float *)y + r * ld_y + c8 * 8);
-      p[0] = make_float4(v[0], v[1], v[2], v[3]);
-      p[1] = make_float4(v[4], v[5], v[6], v[7]);
+      float *p = (float *)y + r * ld_y + c8 * 8;
+      ntstore16(p, make_uint4(__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
+                              __float_as_uint(v[3])));
+      ntstore16(p + 4, make_uint4(__float_as_uint(v[4]), __float_as_uint(v[5]),
+                                  __float_as_uint(v[6]), __float_as_uint(v[7])));
     } else {
       uint4 o;
       o.x = f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16);
       o.y = f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16);
       o.z = f32_to_bf16_rne(v[4]) | (f32_to_bf16_rne(v[5]) << 16);
       o.w = f32_to_bf16_rne(v[6]) | (f32_to_bf16_rne(v[7]) << 16);
-      *(uint4 *)((uint16_t *)y + r * ld_y + c8 * 8) = o;
+      ntstore16((uint16_t *)y + r * ld_y + c8 * 8, o);
     }
   }
 }

@@ -215,7 +215,7 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_tile(DenseArgs p) {
       for (int r = 0; r < 16; ++r) {
         const int64_t row = m0 + f * 32 + 8 * (r >> 2) + 4 * kh + (r & 3);
         if (row < p.m && col < p.n)
-          p.y[row * p.ld_y + col] = (uint16_t)f32_to_bf16_rne(acc[f][g][r] * alpha);
+          ntstore_u16(p.y + row * p.ld_y + col, f32_to_bf16_rne(acc[f][g][r] * alpha));
       }
     }
 }
@@ -468,7 +468,7 @@ __global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(1,
       for (int r = 0; r < 16; ++r) {
         const int64_t row = m0 + f * 32 + 8 * (r >> 2) + 4 * kh + (r & 3);
         if (full || (row < p.m && col < p.n))
-          p.y[row * p.ld_y + col] = (uint16_t)f32_to_bf16_rne(acc[f][g][r] * alpha);
+          ntstore_u16(p.y + row * p.ld_y + col, f32_to_bf16_rne(acc[f][g][r] * alpha));
       }
     }
 }
@@ -591,7 +591,7 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_grouped(GroupedArgs p) {
         for (int r = 0; r < 16; ++r) {
           const int64_t row = m0 + f * 32 + 8 * (r >> 2) + 4 * kh + (r & 3);
           if (row < r_end && col < p.n)
-            p.y[row * p.ld_y + col] = (uint16_t)f32_to_bf16_rne(acc[f][g][r] * alpha);
+            ntstore_u16(p.y + row * p.ld_y + col, f32_to_bf16_rne(acc[f][g][r] * alpha));
         }
       }
   }
@@ -673,7 +673,7 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_small_m(SmallMArgs p) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int64_t n = n0 + 4 * q + r;
-        if (n < p.n) p.y[(int64_t)i16 * p.ld_y + n] = (uint16_t)f32_to_bf16_rne(s[r] * alpha);
+        if (n < p.n) ntstore_u16(p.y + (int64_t)i16 * p.ld_y + n, f32_to_bf16_rne(s[r] * alpha));
       }
     }
   }

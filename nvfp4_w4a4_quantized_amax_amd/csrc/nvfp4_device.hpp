@@ -63,6 +63,23 @@ __device__ __forceinline__ uint32_t fdiv(uint32_t n, FastDiv f) {
 }
 
 // 16-byte load with the non-temporal hint (streamed once, not worth keeping in the caches).
+// Streaming (nontemporal) stores for outputs the kernel does not read back: such lines do not
+// stay dirty in L2, so the end of the kernel has less to write back.
+__device__ __forceinline__ void ntstore8(uint8_t *p, uint2 v) {
+  typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+  __builtin_nontemporal_store(u32x2{v.x, v.y}, (u32x2 *)p);
+}
+__device__ __forceinline__ void ntstore16(void *p, uint4 v) {
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w}, (u32x4 *)p);
+}
+__device__ __forceinline__ void ntstore_u8(uint8_t *p, uint32_t v) {
+  __builtin_nontemporal_store((uint8_t)v, p);
+}
+__device__ __forceinline__ void ntstore_u16(uint16_t *p, uint32_t v) {
+  __builtin_nontemporal_store((uint16_t)v, p);
+}
+
 __device__ __forceinline__ uint4 ntload16(const uint4 *p) {
   typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
   const u32x4 t = __builtin_nontemporal_load((const u32x4 *)p);

@@ -148,8 +148,8 @@ __device__ __forceinline__ void encode_block_1d(const uint4 &a, const uint4 &b, 
     co = (size_t)r * (size_t)o.ld_codes + (size_t)cb * 8u;
     so = (size_t)r * (size_t)o.ld_scales + (size_t)cb;
   }
-  *(uint2 *)(o.codes + co) = packed;
-  o.scales[so] = (uint8_t)code;
+  ntstore8(o.codes + co, packed);
+  ntstore_u8(o.scales + so, (uint32_t)code);
 }
 
 template <bool CONTIG>
@@ -392,8 +392,8 @@ __global__ __launch_bounds__(kQThreads) void k_encode_2d(const uint16_t *__restr
     float k;
     const int code = scale_code(m, tab, &k);
     const uint2 packed = make_uint2(encode8(v0, k, code, tab.gs), encode8(v1, k, code, tab.gs));
-    *(uint2 *)(o.codes + (band * 16 + r) * o.ld_codes + tc * 8) = packed;
-    if (r == 0) o.scales[band * o.ld_scales + tc] = (uint8_t)code;
+    ntstore8(o.codes + (band * 16 + r) * o.ld_codes + tc * 8, packed);
+    if (r == 0) ntstore_u8(o.scales + band * o.ld_scales + tc, (uint32_t)code);
   }
 }
 
@@ -430,8 +430,8 @@ __global__ __launch_bounds__(kSmallThreads) void k_quantize_small(const uint16_t
     float k;
     const int code = scale_code(absmax16(v0, v1), tab, &k);
     const uint2 packed = make_uint2(encode8(v0, k, code, tab.gs), encode8(v1, k, code, tab.gs));
-    *(uint2 *)(o.codes + (int64_t)r * o.ld_codes + cb * 8) = packed;
-    o.scales[(int64_t)r * o.ld_scales + cb] = (uint8_t)code;
+    ntstore8(o.codes + (int64_t)r * o.ld_codes + cb * 8, packed);
+    ntstore_u8(o.scales + (int64_t)r * o.ld_scales + cb, (uint32_t)code);
   }
 }
 

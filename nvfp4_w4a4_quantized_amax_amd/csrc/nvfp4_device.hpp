@@ -22,17 +22,19 @@ constexpr int kE4M3MaxCode = 0x7E;  // 448
 // Per-tensor tables, rebuilt from the global scale by every workgroup that encodes.
 // ---------------------------------------------------------------------------------------------
 struct QuantTables {
-  float gs;           // FP32 global scale
-  float inv6gs;       // approx 1 / (6 gs), only used to guess a block-scale code
-  // thresh[s] (s = 1..126): smallest bf16 magnitude pattern whose block scale code is >= s;
-  // thresh[0] = 0, thresh[127] = 0xFFFF (never reached).  Stored in pairs:
-  // thresh2[s] = thresh[s] | thresh[s + 1] << 16, so one read gives both neighbours.
-  uint32_t thresh2[128];
-  // mult[s + 1] (s = 0..126): float multiplier k with RNE_fp4(RN_fp32(x * k)) equal to the exact
-  // nearest-code rule for every bf16 x, for block scale code s; a negative value (-k) means no
-  // such k was found and the block takes the exact slow path.  Scale code 0 has k = 0.
-  // mult[0] and mult[128] are padding (0), so codes s-1, s, s+1 can be read without a check.
-  float mult[129];
+  float gs;       // FP32 global scale
+  float inv6gs;   // approx 1 / (6 gs), only used to guess a block-scale code
+  float pad[2];
+  // ent[c], c = 0..127, everything a block whose guessed scale code is c needs, in one 16-byte
+  // read:
+  //   x = thresh[c] | thresh[c + 1] << 16, thresh[s] (s = 1..126) being the smallest bf16
+  //       magnitude pattern whose block scale code is >= s (thresh[0] = 0, thresh[127] = 0xFFFF,
+  //       never reached);
+  //   y, z, w = float bits of the element multipliers of codes c - 1, c and c + 1.
+  // The multiplier k of scale code s is a float with RNE_fp4(RN_fp32(x * k)) equal to the exact
+  // nearest-code rule for every bf16 x; a negative value (-k) means no such k was found and the
+  // block takes the exact slow path.  Codes 0, -1 and 127 have k = 0.
+  uint4 ent[128];
 };
 
 // Workspace header (8 KiB).  The two-pass path leaves one partial maximum (|bf16| bit pattern)
@@ -205,6 +207,15 @@ struct TableScratch {
 // for amax in the supported range).  So the multiplier only has to be checked for the 8 E4M3
 // mantissas (1 + m/8) * gs; the multiplier of any code is that of its mantissa times a power of
 // two.  Subnormal E4M3 codes normalize onto the same mantissas.
+// Element multiplier of block-scale code s (0 for s outside 1..126, and for an unusable gs).
+__device__ __forceinline__ float code_multiplier(int s, const TableScratch &sc, bool usable) {
+  if (!usable || s < 1 || s > 126) return 0.0f;
+  const uint32_t vb = __float_as_uint(e4m3_to_float((uint32_t)s));
+  const int m = (int)((vb >> 20) & 7u);
+  const int E = (int)((vb >> 23) & 0xFFu) - 127;
+  return ldexpf(sc.kbase[m], -E);
+}
+
 __device__ inline void build_tables(QuantTables &t, TableScratch &sc, float gs) {
   const int tid = threadIdx.x;
   const double gsd = (double)gs;
@@ -238,21 +249,15 @@ __device__ inline void build_tables(QuantTables &t, TableScratch &sc, float gs) 
     sc.kbase[tid] = multiplier_is_exact(ku, S) ? ku : (multiplier_is_exact(kd, S) ? kd : -k0);
   }
   __syncthreads();
-  // Phase D: every code's multiplier = its mantissa's base multiplier scaled by 2^-exponent;
-  // thresholds paired with their upper neighbour.
+  // Phase D: each entry holds its threshold pair and the multipliers of its code and both
+  // neighbours (a code's multiplier is its mantissa's base multiplier scaled by 2^-exponent).
   if (tid < 128) {
     const int s = tid;
-    float k = 0.0f;
-    if (usable && s >= 1 && s <= 126) {
-      const uint32_t vb = __float_as_uint(e4m3_to_float((uint32_t)s));
-      const int m = (int)((vb >> 20) & 7u);
-      const int E = (int)((vb >> 23) & 0xFFu) - 127;
-      k = ldexpf(sc.kbase[m], -E);
-    }
-    t.mult[s + 1] = (s == 127) ? 0.0f : k;
-    t.thresh2[s] = (uint32_t)sc.thresh[s] | ((s == 127 ? 0xFFFFu : (uint32_t)sc.thresh[s + 1]) << 16);
+    const uint32_t th = (uint32_t)sc.thresh[s] | ((s == 127 ? 0xFFFFu : (uint32_t)sc.thresh[s + 1]) << 16);
+    t.ent[s] = make_uint4(th, __float_as_uint(code_multiplier(s - 1, sc, usable)),
+                          __float_as_uint(code_multiplier(s, sc, usable)),
+                          __float_as_uint(code_multiplier(s + 1, sc, usable)));
   }
-  if (tid == 0) t.mult[0] = 0.0f;
   __syncthreads();
 }
 
@@ -270,20 +275,28 @@ __device__ __forceinline__ float inv6gs_of(float gs) {
 // ---------------------------------------------------------------------------------------------
 
 // E4M3 code of a block whose |max| bf16 pattern is `bam`, and its element multiplier: a guess
-// from bam * inv6gs (within one code of the answer), corrected with the exact thresholds.  The
-// threshold pair and the three candidate multipliers are read independently of each other.
-__device__ __forceinline__ int scale_code(uint32_t bam, const QuantTables &tab, float *k_out) {
-  const float t = __uint_as_float(bam << 16) * tab.inv6gs;
+// from bam * inv6gs (within one code of the answer), corrected with the exact thresholds of
+// one table entry, which also holds the three candidate multipliers.
+__device__ __forceinline__ int scale_code(uint32_t bam, const QuantTables &tab, float inv6gs,
+                                          float *k_out) {
+  const float t = __uint_as_float(bam << 16) * inv6gs;
   const int c_norm = (int)(__float_as_uint(t) >> 20) - 960;
   const int c_sub = (int)(t * 512.0f);
   int cand = (t >= 0x1p-6f) ? c_norm : c_sub;
   cand = min(max(cand, 0), kE4M3MaxCode);
-  const uint32_t th = tab.thresh2[cand];
-  const float k_dn = tab.mult[cand], k_mid = tab.mult[cand + 1], k_up = tab.mult[cand + 2];
-  const bool up = bam >= (th >> 16);
-  const bool dn = bam < (th & 0xFFFFu);
-  *k_out = up ? k_up : (dn ? k_dn : k_mid);
+  // One 16-byte read (left to itself the compiler turns the selects below into branches around
+  // separate 4-byte reads).
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 ev = __builtin_nontemporal_load((const u32x4 *)&tab.ent[cand]);
+  const uint4 e = make_uint4(ev[0], ev[1], ev[2], ev[3]);
+  const bool up = bam >= (e.x >> 16);
+  const bool dn = bam < (e.x & 0xFFFFu);
+  *k_out = __uint_as_float(up ? e.w : (dn ? e.y : e.z));
   return cand + (up ? 1 : 0) - (dn ? 1 : 0);
+}
+
+__device__ __forceinline__ int scale_code(uint32_t bam, const QuantTables &tab, float *k_out) {
+  return scale_code(bam, tab, tab.inv6gs, k_out);
 }
 
 // Exact magnitude code of |x| (as a float) for block scale value sbv: compare with each
@@ -320,17 +333,28 @@ __device__ __noinline__ uint32_t encode8_exact(uint4 v, int code, float gs) {
   return r;
 }
 
-// Eight E2M1 codes (one 32-bit word, element 0 in the low nibble) for 8 packed bf16 values.
-__device__ __forceinline__ uint32_t encode8(uint4 v, float k, int code, float gs) {
-  if (k >= 0.0f) {
-    uint32_t r = 0;
-    r = cvt_fp4x2<0>(r, bf16_lo(v.x) * k, bf16_hi(v.x) * k);
-    r = cvt_fp4x2<1>(r, bf16_lo(v.y) * k, bf16_hi(v.y) * k);
-    r = cvt_fp4x2<2>(r, bf16_lo(v.z) * k, bf16_hi(v.z) * k);
-    r = cvt_fp4x2<3>(r, bf16_lo(v.w) * k, bf16_hi(v.w) * k);
-    return r;
+// Eight E2M1 codes (one 32-bit word, element 0 in the low nibble) for 8 packed bf16 values,
+// for a block whose multiplier k is exact (k >= 0).
+__device__ __forceinline__ uint32_t encode8_fast(uint4 v, float k) {
+  uint32_t r = 0;
+  r = cvt_fp4x2<0>(r, bf16_lo(v.x) * k, bf16_hi(v.x) * k);
+  r = cvt_fp4x2<1>(r, bf16_lo(v.y) * k, bf16_hi(v.y) * k);
+  r = cvt_fp4x2<2>(r, bf16_lo(v.z) * k, bf16_hi(v.z) * k);
+  r = cvt_fp4x2<3>(r, bf16_lo(v.w) * k, bf16_hi(v.w) * k);
+  return r;
+}
+
+// The 16 codes of one block (a: values 0..7, b: values 8..15).  The multiplier path runs
+// unconditionally; the rare blocks whose scale has no exact multiplier (k < 0) are redone on
+// the exact path.
+__device__ __forceinline__ uint2 encode16(const uint4 &a, const uint4 &b, float k, int code,
+                                          float gs) {
+  uint2 r = make_uint2(encode8_fast(a, k), encode8_fast(b, k));
+  if (k < 0.0f) {
+    r.x = encode8_exact(a, code, gs);
+    r.y = encode8_exact(b, code, gs);
   }
-  return encode8_exact(v, code, gs);
+  return r;
 }
 
 // ---------------------------------------------------------------------------------------------

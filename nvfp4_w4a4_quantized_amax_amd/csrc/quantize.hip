@@ -131,13 +131,15 @@ struct EncOut {
   int64_t ld_scales;
 };
 
+// Same, for a block whose |max| bf16 pattern `bam` is already known.
 template <bool CONTIG>
-__device__ __forceinline__ void encode_block_1d(const uint4 &a, const uint4 &b, uint32_t blk,
-                                                FastDiv bpr, const EncOut &o,
-                                                const QuantTables &tab) {
+__device__ __forceinline__ void encode_block_1d_bam(const uint4 &a, const uint4 &b, uint32_t bam,
+                                                    uint32_t blk, FastDiv bpr, const EncOut &o,
+                                                    const QuantTables &tab, float inv6gs,
+                                                    float gs) {
   float k;
-  const int code = scale_code(absmax16(a, b), tab, &k);
-  const uint2 packed = make_uint2(encode8(a, k, code, tab.gs), encode8(b, k, code, tab.gs));
+  const int code = scale_code(bam, tab, inv6gs, &k);
+  const uint2 packed = encode16(a, b, k, code, gs);
   size_t co, so;
   if (CONTIG) {
     co = (size_t)blk * 8u;
@@ -150,6 +152,13 @@ __device__ __forceinline__ void encode_block_1d(const uint4 &a, const uint4 &b, 
   }
   ntstore8(o.codes + co, packed);
   ntstore_u8(o.scales + so, (uint32_t)code);
+}
+
+template <bool CONTIG>
+__device__ __forceinline__ void encode_block_1d(const uint4 &a, const uint4 &b, uint32_t blk,
+                                                FastDiv bpr, const EncOut &o,
+                                                const QuantTables &tab) {
+  encode_block_1d_bam<CONTIG>(a, b, absmax16(a, b), blk, bpr, o, tab, tab.inv6gs, tab.gs);
 }
 
 template <bool CONTIG>
@@ -219,8 +228,10 @@ __global__ __launch_bounds__(WAVES * 64, 1) void k_quantize_persistent(
   __shared__ TableScratch scr;
   __shared__ uint32_t red[WAVES];
   __shared__ uint32_t s_amax;
-  // LDS-resident tiles: [tile][half][wave][lane], one 16-byte half-block per lane.
+  // LDS-resident tiles: [tile][half][wave][lane], one 16-byte half-block per lane, and each
+  // block's |max| pattern (found in phase 1, used again in phase 2).
   __shared__ uint4 s_tiles[LT * 2 * WAVES][kWave];
+  __shared__ uint16_t s_bam[LT * WAVES][kWave];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const uint32_t S = gridDim.x * WAVES;
   const uint32_t n_tiles = (n_blocks + kTileBlocks - 1) / kTileBlocks;
@@ -232,7 +243,7 @@ __global__ __launch_bounds__(WAVES * 64, 1) void k_quantize_persistent(
   uint32_t m = 0;
 
   // Phase 1a: LDS tiles, staged through registers in batches of kLdsBatch tiles.
-  constexpr int kLdsBatch = 4;
+  constexpr int kLdsBatch = (LT % 4 == 0) ? 4 : 3;
   static_assert(LT % kLdsBatch == 0, "LDS tiles come in whole batches");
 #pragma unroll 1
   for (int i0 = 0; i0 < LT; i0 += kLdsBatch) {
@@ -251,7 +262,9 @@ __global__ __launch_bounds__(WAVES * 64, 1) void k_quantize_persistent(
     }
 #pragma unroll
     for (int u = 0; u < kLdsBatch; ++u) {
-      m = max(m, absmax16(t[2 * u], t[2 * u + 1]));
+      const uint32_t bm = absmax16(t[2 * u], t[2 * u + 1]);
+      m = max(m, bm);
+      s_bam[(i0 + u) * WAVES + wave][lane] = (uint16_t)bm;
       s_tiles[(2 * (i0 + u)) * WAVES + wave][lane] = t[2 * u];
       s_tiles[(2 * (i0 + u) + 1) * WAVES + wave][lane] = t[2 * u + 1];
     }
@@ -277,8 +290,15 @@ __global__ __launch_bounds__(WAVES * 64, 1) void k_quantize_persistent(
       m = max(m, absmax16(x[idx], x[idx + 1]));
     }
   }
+  // Block maxima of the register tiles, two 16-bit patterns per register.
+  uint32_t bamr[(RT + 1) / 2];
 #pragma unroll
-  for (int i = 0; i < RT; ++i) m = max(m, absmax16(reg[2 * i], reg[2 * i + 1]));
+  for (int i = 0; i < RT; ++i) {
+    const uint32_t bm = absmax16(reg[2 * i], reg[2 * i + 1]);
+    m = max(m, bm);
+    if (i % 2 == 0) bamr[i / 2] = bm;
+    else bamr[i / 2] |= bm << 16;
+  }
   m = block_max_u32(m, red);
 
   // Grid barrier on per-workgroup slots.  A slot carries its own payload (the partial max), so
@@ -317,6 +337,7 @@ __global__ __launch_bounds__(WAVES * 64, 1) void k_quantize_persistent(
   const float gs = global_scale_from_amax_bits(s_amax);
   if (blockIdx.x == 0 && threadIdx.x == 0) *gs_out = gs;
   build_tables(tab, scr, gs);
+  const float inv6gs = tab.inv6gs;
 
   // Phase 2: encode the register tiles; each freed register pair immediately starts the re-read
   // of one overflow tile.  Then the LDS tiles, then the prefetched overflow tiles; any further
@@ -325,7 +346,9 @@ __global__ __launch_bounds__(WAVES * 64, 1) void k_quantize_persistent(
   for (int i = 0; i < RT; ++i) {
     const uint32_t b = tile_block(LT + i);
     if ((uint32_t)(LT + i) < cnt && b < n_blocks)
-      encode_block_1d<CONTIG>(reg[2 * i], reg[2 * i + 1], b, bpr, o, tab);
+      encode_block_1d_bam<CONTIG>(reg[2 * i], reg[2 * i + 1],
+                                  (i % 2 == 0) ? (bamr[i / 2] & 0xFFFFu) : (bamr[i / 2] >> 16), b,
+                                  bpr, o, tab, inv6gs, gs);
     const uint32_t b2 = tile_block(LT + RT + i);
     if ((uint32_t)(LT + RT + i) < cnt && b2 < n_blocks) {
       const size_t idx = block_index<CONTIG>(b2, bpr, ld_x8);
@@ -337,8 +360,9 @@ __global__ __launch_bounds__(WAVES * 64, 1) void k_quantize_persistent(
   for (int i = 0; i < LT; ++i) {
     const uint32_t b = tile_block(i);
     if ((uint32_t)i < cnt && b < n_blocks)
-      encode_block_1d<CONTIG>(s_tiles[(2 * i) * WAVES + wave][lane],
-                              s_tiles[(2 * i + 1) * WAVES + wave][lane], b, bpr, o, tab);
+      encode_block_1d_bam<CONTIG>(s_tiles[(2 * i) * WAVES + wave][lane],
+                                  s_tiles[(2 * i + 1) * WAVES + wave][lane],
+                                  s_bam[i * WAVES + wave][lane], b, bpr, o, tab, inv6gs, gs);
   }
 #pragma unroll
   for (int i = 0; i < RT; ++i) {
@@ -391,7 +415,7 @@ __global__ __launch_bounds__(kQThreads) void k_encode_2d(const uint16_t *__restr
     if (!valid) continue;
     float k;
     const int code = scale_code(m, tab, &k);
-    const uint2 packed = make_uint2(encode8(v0, k, code, tab.gs), encode8(v1, k, code, tab.gs));
+    const uint2 packed = encode16(v0, v1, k, code, tab.gs);
     ntstore8(o.codes + (band * 16 + r) * o.ld_codes + tc * 8, packed);
     if (r == 0) ntstore_u8(o.scales + band * o.ld_scales + tc, (uint32_t)code);
   }
@@ -429,7 +453,7 @@ __global__ __launch_bounds__(kSmallThreads) void k_quantize_small(const uint16_t
     const uint4 v0 = p[0], v1 = p[1];
     float k;
     const int code = scale_code(absmax16(v0, v1), tab, &k);
-    const uint2 packed = make_uint2(encode8(v0, k, code, tab.gs), encode8(v1, k, code, tab.gs));
+    const uint2 packed = encode16(v0, v1, k, code, tab.gs);
     ntstore8(o.codes + (int64_t)r * o.ld_codes + cb * 8, packed);
     ntstore_u8(o.scales + (int64_t)r * o.ld_scales + cb, (uint32_t)code);
   }
@@ -500,9 +524,15 @@ hipError_t launch_quantize(const void *x, int64_t rows, int64_t cols, int64_t ld
 // Persistent single-read launch (one workgroup per CU).  Returns hipErrorNotSupported, having
 // launched nothing, when the device cannot hold one such workgroup per CU or the path is turned
 // off, so the caller can use the two-kernel path.
+// 16 waves per CU; each wave keeps RT tiles in registers (8 VGPRs each) and LT tiles in LDS
+// (16 waves x 4 x 2 KiB = 128 KiB).  An 8192 x 8192 bf16 tensor is 16 tiles per wave, so 12 of
+// them are read only once.  (Holding every tile needs 8 waves per CU, which leaves the encode
+// phase too few waves to hide its latencies: slower overall.)
 constexpr int kPWaves = 16;
-constexpr int kPResident = 8;   // tiles kept in registers per wave (64 VGPRs)
-constexpr int kPLds = 4;        // tiles kept in LDS per wave (16 waves x 4 x 2 KiB = 128 KiB)
+constexpr int kPResidentC = 8, kPLdsC = 4;
+constexpr int kPResidentS = 8, kPLdsS = 4;
+#define K_PERSISTENT_C k_quantize_persistent<kPWaves, kPResidentC, kPLdsC, true>
+#define K_PERSISTENT_S k_quantize_persistent<kPWaves, kPResidentS, kPLdsS, false>
 
 struct DeviceInfo {
   int cus = 0;
@@ -526,11 +556,11 @@ static DeviceInfo device_info() {
         hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) == hipSuccess) {
       d.coop = coop != 0;
       if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-              &d.fits_contig, (const void *)k_quantize_persistent<kPWaves, kPResident, kPLds, true>,
+              &d.fits_contig, (const void *)K_PERSISTENT_C,
               kPWaves * 64, 0) != hipSuccess)
         d.fits_contig = 0;
       if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-              &d.fits_strided, (const void *)k_quantize_persistent<kPWaves, kPResident, kPLds, false>,
+              &d.fits_strided, (const void *)K_PERSISTENT_S,
               kPWaves * 64, 0) != hipSuccess)
         d.fits_strided = 0;
     }
@@ -583,21 +613,18 @@ hipError_t launch_quantize_persistent(const void *x, int64_t rows, int64_t cols,
   const uint4 *xp = (const uint4 *)x;
   void *args[] = {(void *)&xp, (void *)&n_blocks, (void *)&f, (void *)&ld_x8, (void *)&o,
                   (void *)&slots, (void *)&epoch, (void *)&gs_out, (void *)&status};
-  const void *fn = contig ? (const void *)k_quantize_persistent<kPWaves, kPResident, kPLds, true>
-                          : (const void *)k_quantize_persistent<kPWaves, kPResident, kPLds, false>;
+  const void *fn = contig ? (const void *)K_PERSISTENT_C : (const void *)K_PERSISTENT_S;
   if (d.cooperative_api)
     return hipLaunchCooperativeKernel(fn, dim3(d.cus), dim3(kPWaves * 64), args, 0, stream);
   // Plain launch: the occupancy check above guarantees one workgroup per CU fits, so on a device
   // that is not running other work all of them are resident at once; if they ever are not, the
   // bounded barrier ends the kernel with a NaN global scale instead of hanging.
   if (contig)
-    hipLaunchKernelGGL((k_quantize_persistent<kPWaves, kPResident, kPLds, true>), dim3(d.cus),
-                       dim3(kPWaves * 64), 0, stream, xp, n_blocks, f, ld_x8, o, slots, epoch,
-                       gs_out, status);
+    hipLaunchKernelGGL((K_PERSISTENT_C), dim3(d.cus), dim3(kPWaves * 64), 0, stream, xp, n_blocks,
+                       f, ld_x8, o, slots, epoch, gs_out, status);
   else
-    hipLaunchKernelGGL((k_quantize_persistent<kPWaves, kPResident, kPLds, false>), dim3(d.cus),
-                       dim3(kPWaves * 64), 0, stream, xp, n_blocks, f, ld_x8, o, slots, epoch,
-                       gs_out, status);
+    hipLaunchKernelGGL((K_PERSISTENT_S), dim3(d.cus), dim3(kPWaves * 64), 0, stream, xp, n_blocks,
+                       f, ld_x8, o, slots, epoch, gs_out, status);
   return hipGetLastError();
 }
 

@@ -211,12 +211,25 @@ nvfp4_status nvfp4_gemm_w4a4(const void *a_bf16, int64_t m, int64_t k, int64_t l
     A.ld_scales = L.ld_scales;
     A.gs = (const float *)(base + L.gs_off);
   }
+  GemmOperand W{w->codes, w->ld_codes, w->scales, w->ld_scales, w->global_scale, w->block_rows};
+  if (a_bf16 && m <= kSmallM) {
+    // Decode shapes: the quantization of A runs inside the product kernel (the quantized A is
+    // written only where the caller asked for it).
+    GemmOperand AQ = A;
+    if (!a_q) {
+      AQ.codes = nullptr;
+      AQ.scales = nullptr;
+      AQ.gs = nullptr;
+    }
+    const hipError_t e = launch_gemm_decode_fused(a_bf16, ld_a, AQ, W, m, n, k, (uint16_t *)y,
+                                                  ld_y, st);
+    if (e != hipErrorNotSupported) return hip_status(e);
+  }
   if (a_bf16) {
     s = run_quantize_1d(a_bf16, m, k, ld_a, (uint8_t *)A.codes, A.ld_codes, (uint8_t *)A.scales,
                         A.ld_scales, (float *)A.gs, ws, st);
     if (s) return s;
   }
-  GemmOperand W{w->codes, w->ld_codes, w->scales, w->ld_scales, w->global_scale, w->block_rows};
   if (m <= kSmallM)
     return hip_status(launch_gemm_small_m(A, W, m, n, k, (uint16_t *)y, ld_y, st));
   return hip_status(launch_gemm_tile(A, W, m, n, k, (uint16_t *)y, ld_y, st));

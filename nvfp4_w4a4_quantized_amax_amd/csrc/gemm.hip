@@ -611,9 +611,17 @@ struct SmallMArgs {
   int64_t m, n, k;
   uint16_t *y;
   int64_t ld_y;
+  int scale_pairs;  // both scale arrays 2-byte aligned with even row strides
+  // Decode kernel with the activation quantization fused in: bf16 A (m x k, row stride ld_a),
+  // and where workgroup 0 writes the quantized A (each pointer may be NULL: not written; the
+  // row strides are a.ld_codes / a.ld_scales).
+  const uint16_t *a_bf16;
+  int64_t ld_a;
+  uint8_t *aq_codes, *aq_scales;
+  float *aq_gs;
 };
 
-constexpr int kSmallMWin = 4;
+constexpr int kSmallMWin = 8;
 
 template <bool W2D>
 __global__ __launch_bounds__(kGemmThreads) void k_gemm_small_m(SmallMArgs p) {
@@ -645,11 +653,22 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_small_m(SmallMArgs p) {
       const int64_t remb = in ? kblocks - win * 8 - q * 2 : 0;   // scale blocks left
       wv[u] = load16_masked(w_row + win * 64, rem);
       av[u] = a_ok ? load16_masked(a_row + win * 64, rem) : make_uint4(0, 0, 0, 0);
-      const uint32_t w0 = remb > 0 ? w_srow[win * 8] : 0u, w1 = remb > 1 ? w_srow[win * 8 + 1] : 0u;
-      const uint32_t a0 = (a_ok && remb > 0) ? a_srow[win * 8] : 0u;
-      const uint32_t a1 = (a_ok && remb > 1) ? a_srow[win * 8 + 1] : 0u;
-      ws_[u] = w0 | (w1 << 8);
-      as_[u] = a0 | (a1 << 8);
+      // Scale pairs as one 16-bit load when both blocks exist and the scale rows are 2-byte
+      // aligned (lane offsets are even); otherwise byte by byte.
+      uint32_t wsv = 0, asv = 0;
+      if (!p.scale_pairs) {
+        wsv = (remb > 0 ? w_srow[win * 8] : 0u) | (remb > 1 ? (uint32_t)w_srow[win * 8 + 1] << 8 : 0u);
+        if (a_ok)
+          asv = (remb > 0 ? a_srow[win * 8] : 0u) | (remb > 1 ? (uint32_t)a_srow[win * 8 + 1] << 8 : 0u);
+      } else if (remb > 1) {
+        wsv = *(const uint16_t *)(w_srow + win * 8);
+        if (a_ok) asv = *(const uint16_t *)(a_srow + win * 8);
+      } else if (remb == 1) {
+        wsv = w_srow[win * 8];
+        if (a_ok) asv = a_srow[win * 8];
+      }
+      ws_[u] = wsv;
+      as_[u] = asv;
     }
 #pragma unroll
     for (int u = 0; u < kSmallMWin; ++u) {
@@ -676,6 +695,196 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_small_m(SmallMArgs p) {
         if (n < p.n) ntstore_u16(p.y + (int64_t)i16 * p.ld_y + n, f32_to_bf16_rne(s[r] * alpha));
       }
     }
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Decode-shaped kernel (m <= 16, K <= 4096): one workgroup of 16 waves per CU walks the 16-row
+// bands of W.  Wave w owns the w-th sixteenth of K for every band: it decodes its slice of A
+// (all m rows) to fp16 once and keeps it in registers, so the loop only streams W, with the
+// next band's W always in flight (its loads are issued before the current band is multiplied,
+// and the first band's before A is decoded).  The sixteen partial sums of a band meet in LDS.
+// ---------------------------------------------------------------------------------------------
+constexpr int kDecWaves = 16;
+constexpr int kDecWin = 2;  // 128-wide K windows per wave (K <= 16 * 2 * 128)
+
+struct DecodeW {
+  uint4 v[kDecWin];
+  uint32_t s[kDecWin];  // two scale bytes per window (the lane's two 16-value blocks)
+};
+
+template <bool W2D>
+__device__ __forceinline__ void load_decode_w(const SmallMArgs &p, int64_t band, int i16, int q,
+                                              int64_t win0, int nw, DecodeW &r) {
+  const int64_t row = min(band * 16 + i16, p.n - 1);
+  const uint8_t *wrow = p.w.codes + row * p.w.ld_codes + q * 16;
+  const uint8_t *srow = p.w.scales + (W2D ? band : row) * p.w.ld_scales + q * 2;
+  const int64_t kbytes = p.k / 2, kblocks = p.k / 16;
+#pragma unroll
+  for (int u = 0; u < kDecWin; ++u) {
+    const int64_t win = win0 + u;
+    const bool in = u < nw;
+    const int64_t rem = in ? kbytes - win * 64 - q * 16 : 0;
+    const int64_t remb = in ? kblocks - win * 8 - q * 2 : 0;
+    r.v[u] = load16_masked(wrow + win * 64, rem);
+    uint32_t sv = 0;
+    if (p.scale_pairs && remb > 1) {
+      sv = *(const uint16_t *)(srow + win * 8);
+    } else {
+      sv = (remb > 0 ? srow[win * 8] : 0u) | (remb > 1 ? (uint32_t)srow[win * 8 + 1] << 8 : 0u);
+    }
+    r.s[u] = sv;
+  }
+}
+
+// FUSED: A arrives as bf16 and every workgroup quantizes it itself (amax over all of A, the
+// FP32 global scale and the scale tables, then its waves encode their own K slices), exactly as
+// nvfp4_quantize_1d would; workgroup 0 also writes the quantized A when asked to.  A is at most
+// 16 rows, so the redundant work is small and no workgroup waits for another.
+template <bool W2D, bool FUSED>
+__global__ __launch_bounds__(kDecWaves * 64) void k_gemm_decode(SmallMArgs p) {
+  __shared__ floatx4_t s_red[2][kDecWaves][kWave];
+  __shared__ QuantTables tab;
+  __shared__ TableScratch scr;
+  __shared__ uint32_t red[kDecWaves];
+  // Quantized A slice of each wave (fused form): up to 16 rows x 16 blocks.
+  __shared__ __align__(8) uint8_t s_acodes[FUSED ? kDecWaves : 1][16 * 16 * 8];
+  __shared__ uint8_t s_ascales[FUSED ? kDecWaves : 1][16 * 16];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int i16 = lane & 15, q = lane >> 4;
+  const int64_t nwin = (p.k + 127) / 128;
+  const int64_t per = (nwin + kDecWaves - 1) / kDecWaves;  // <= kDecWin, checked by the launcher
+  const int64_t win0 = wave * per;
+  const int nw = (int)max((int64_t)0, min(per, nwin - win0));
+  const int64_t kbytes = p.k / 2, kblocks = p.k / 16;
+  const int64_t nbands = (p.n + 15) / 16;
+
+  DecodeW cur, nxt;
+  int64_t band = blockIdx.x;
+  if (band < nbands) load_decode_w<W2D>(p, band, i16, q, win0, nw, cur);
+
+  // This wave's K slice of A, decoded once: window u, K step kk -> 8 fp16 values of A row i16.
+  half8_t aop[kDecWin][4];
+  float gs_a = 0.0f;
+  if (FUSED) {
+    // Each wave loads its own K slice of all m rows of A, coalesced: step j gives lane l the
+    // 16-value block j * 64 + l of the slice (row = block / bps, bps blocks per row).  Those
+    // registers give this workgroup's share of the global amax and are then encoded in place;
+    // the codes reach the MFMA layout through the wave's own corner of LDS.
+    const int64_t kb0 = win0 * 8;                             // first block of the slice
+    const int bps = (int)max((int64_t)0, min(per * 8, kblocks - kb0));  // blocks per row
+    const int nblk = (int)p.m * bps;                           // <= 16 * 16
+    uint4 xa[4][2];
+    uint32_t mx = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int blk = j * 64 + lane;
+      const uint4 z = make_uint4(0, 0, 0, 0);
+      xa[j][0] = xa[j][1] = z;
+      if (blk < nblk) {
+        const int r = blk / bps, c = blk - r * bps;
+        const uint16_t *src = p.a_bf16 + r * p.ld_a + (kb0 + c) * 16;
+        xa[j][0] = *(const uint4 *)src;
+        xa[j][1] = *(const uint4 *)(src + 8);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) mx = max(mx, absmax16(xa[j][0], xa[j][1]));
+    mx = wave_max_u32(mx);
+    if (lane == 0) red[wave] = mx;
+    __syncthreads();
+    mx = red[0];
+#pragma unroll
+    for (int w2 = 1; w2 < kDecWaves; ++w2) mx = max(mx, red[w2]);
+    gs_a = global_scale_from_amax_bits(mx);
+    build_tables(tab, scr, gs_a);
+    if (p.aq_gs && blockIdx.x == 0 && threadIdx.x == 0) *p.aq_gs = gs_a;
+    const float inv6gs = tab.inv6gs;
+    // Encode; codes and scales of the slice go to this wave's LDS corner (row-major, 16 blocks
+    // per row at most) and, for workgroup 0, to the caller's quantized A.
+    uint8_t *lc = s_acodes[wave], *ls = s_ascales[wave];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int blk = j * 64 + lane;
+      if (blk < nblk) {
+        const int r = blk / bps, c = blk - r * bps;
+        float kq;
+        const int code = scale_code(absmax16(xa[j][0], xa[j][1]), tab, inv6gs, &kq);
+        const uint2 e = encode16(xa[j][0], xa[j][1], kq, code, gs_a);
+        *(uint2 *)(lc + (r * 16 + c) * 8) = e;
+        ls[r * 16 + c] = (uint8_t)code;
+        if (blockIdx.x == 0) {
+          if (p.aq_codes) ntstore8(p.aq_codes + r * p.a.ld_codes + (kb0 + c) * 8, e);
+          if (p.aq_scales) ntstore_u8(p.aq_scales + r * p.a.ld_scales + kb0 + c, (uint32_t)code);
+        }
+      }
+    }
+    __syncthreads();
+    // MFMA layout: lane (i16, q), window u holds blocks 8u + 2q and 8u + 2q + 1 of row i16.
+    const bool a_ok = i16 < p.m;
+#pragma unroll
+    for (int u = 0; u < kDecWin; ++u) {
+      const int c0 = u * 8 + q * 2;
+      const bool v0 = a_ok && c0 < bps, v1 = a_ok && c0 + 1 < bps;
+      const uint2 e0 = v0 ? *(const uint2 *)(lc + (i16 * 16 + c0) * 8) : make_uint2(0, 0);
+      const uint2 e1 = v1 ? *(const uint2 *)(lc + (i16 * 16 + c0 + 1) * 8) : make_uint2(0, 0);
+      const uint32_t sv = (v0 ? (uint32_t)ls[i16 * 16 + c0] : 0u) |
+                          ((v1 ? (uint32_t)ls[i16 * 16 + c0 + 1] : 0u) << 8);
+      const uint4 v = make_uint4(e0.x, e0.y, e1.x, e1.y);
+      const half2_t sp = scales_f16x2(sv);
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+        aop[u][kk] = decode8_f16(word(v, kk), kk < 2 ? splat_lo(sp) : splat_hi(sp));
+    }
+  } else {
+    const bool a_ok = i16 < p.m;
+    const uint8_t *arow = p.a.codes + (a_ok ? i16 : 0) * p.a.ld_codes + q * 16;
+    const uint8_t *asrow = p.a.scales + (a_ok ? i16 : 0) * p.a.ld_scales + q * 2;
+#pragma unroll
+    for (int u = 0; u < kDecWin; ++u) {
+      const int64_t win = win0 + u;
+      const bool in = a_ok && u < nw;
+      const int64_t rem = in ? kbytes - win * 64 - q * 16 : 0;
+      const int64_t remb = in ? kblocks - win * 8 - q * 2 : 0;
+      const uint4 v = load16_masked(arow + win * 64, rem);
+      const uint32_t sv = (remb > 0 ? asrow[win * 8] : 0u) |
+                          (remb > 1 ? (uint32_t)asrow[win * 8 + 1] << 8 : 0u);
+      const half2_t sp = scales_f16x2(sv);
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+        aop[u][kk] = decode8_f16(word(v, kk), kk < 2 ? splat_lo(sp) : splat_hi(sp));
+    }
+  }
+
+  const float alpha = (FUSED ? gs_a : *p.a.gs) * (*p.w.gs);
+  for (int parity = 0; band < nbands; band += gridDim.x, parity ^= 1) {
+    const int64_t next = band + gridDim.x;
+    if (next < nbands) load_decode_w<W2D>(p, next, i16, q, win0, nw, nxt);
+    floatx4_t acc = floatx4_t{};
+#pragma unroll
+    for (int u = 0; u < kDecWin; ++u) {
+      if (u < nw) {
+        const half2_t sp = scales_f16x2(cur.s[u]);
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          const half8_t wop = decode8_f16(word(cur.v[u], kk), kk < 2 ? splat_lo(sp) : splat_hi(sp));
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(wop, aop[u][kk], acc, 0, 0, 0);
+        }
+      }
+    }
+    // Partial sums of the K slices; the buffer alternates with the band so one barrier per band
+    // suffices (a buffer is rewritten only after the next band's barrier).  Waves 0..3 each
+    // finish one of the four output rows a lane holds.
+    s_red[parity][wave][lane] = acc;
+    __syncthreads();
+    if (wave < 4 && i16 < p.m) {
+      float t = 0.0f;
+#pragma unroll
+      for (int w2 = 0; w2 < kDecWaves; ++w2) t += s_red[parity][w2][lane][wave];
+      const int64_t n = band * 16 + 4 * q + wave;
+      if (n < p.n) ntstore_u16(p.y + (int64_t)i16 * p.ld_y + n, f32_to_bf16_rne(t * alpha));
+    }
+    cur = nxt;
   }
 }
 
@@ -733,6 +942,44 @@ hipError_t launch_gemm_tile(const GemmOperand &a, const GemmOperand &w, int64_t 
   return hipGetLastError();
 }
 
+// One workgroup per CU, each taking the same number of 16-row bands.
+static hipError_t launch_decode(const SmallMArgs &p, bool w2d, bool fused, hipStream_t stream) {
+  static int cus = 0;
+  if (cus == 0 && hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, 0) != hipSuccess)
+    cus = 0;
+  const int64_t nbands = (p.n + 15) / 16;
+  const int64_t slots = cus > 0 ? cus : 256;
+  const int64_t per_wg = (nbands + slots - 1) / slots;
+  const unsigned grid = (unsigned)((nbands + per_wg - 1) / per_wg);
+  const dim3 block(kDecWaves * 64);
+  if (w2d && fused) hipLaunchKernelGGL((k_gemm_decode<true, true>), dim3(grid), block, 0, stream, p);
+  if (w2d && !fused) hipLaunchKernelGGL((k_gemm_decode<true, false>), dim3(grid), block, 0, stream, p);
+  if (!w2d && fused) hipLaunchKernelGGL((k_gemm_decode<false, true>), dim3(grid), block, 0, stream, p);
+  if (!w2d && !fused) hipLaunchKernelGGL((k_gemm_decode<false, false>), dim3(grid), block, 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_decode_fused(const void *a_bf16, int64_t ld_a, const GemmOperand &aq,
+                                    const GemmOperand &w, int64_t m, int64_t n, int64_t k,
+                                    uint16_t *y, int64_t ld_y, hipStream_t stream) {
+  if (m < 1 || m > 16 || (k + 127) / 128 > kDecWaves * kDecWin) return hipErrorNotSupported;
+  SmallMArgs p;
+  p.a = aq;
+  p.w = w;
+  p.m = m;
+  p.n = n;
+  p.k = k;
+  p.y = y;
+  p.ld_y = ld_y;
+  p.scale_pairs = ((uintptr_t)w.scales % 2 == 0) && (w.ld_scales % 2 == 0);
+  p.a_bf16 = (const uint16_t *)a_bf16;
+  p.ld_a = ld_a;
+  p.aq_codes = (uint8_t *)aq.codes;
+  p.aq_scales = (uint8_t *)aq.scales;
+  p.aq_gs = (float *)aq.gs;
+  return launch_decode(p, w.block_rows == 16, true, stream);
+}
+
 hipError_t launch_gemm_small_m(const GemmOperand &a, const GemmOperand &w, int64_t m, int64_t n,
                                int64_t k, uint16_t *y, int64_t ld_y, hipStream_t stream) {
   SmallMArgs p;
@@ -743,7 +990,17 @@ hipError_t launch_gemm_small_m(const GemmOperand &a, const GemmOperand &w, int64
   p.k = k;
   p.y = y;
   p.ld_y = ld_y;
-  const unsigned grid = (unsigned)((n + 15) / 16);
+  p.scale_pairs = ((uintptr_t)a.scales % 2 == 0) && (a.ld_scales % 2 == 0) &&
+                  ((uintptr_t)w.scales % 2 == 0) && (w.ld_scales % 2 == 0);
+  const int64_t nbands = (n + 15) / 16;
+  if ((k + 127) / 128 <= kDecWaves * kDecWin) {
+    p.a_bf16 = nullptr;
+    p.ld_a = 0;
+    p.aq_codes = p.aq_scales = nullptr;
+    p.aq_gs = nullptr;
+    return launch_decode(p, w.block_rows == 16, false, stream);
+  }
+  const unsigned grid = (unsigned)nbands;
   if (w.block_rows == 16)
     hipLaunchKernelGGL(k_gemm_small_m<true>, dim3(grid), dim3(kGemmThreads), 0, stream, p);
   else

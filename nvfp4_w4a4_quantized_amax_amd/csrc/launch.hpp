@@ -42,6 +42,13 @@ struct GemmOperand {
 
 hipError_t launch_gemm_tile(const GemmOperand &a, const GemmOperand &w, int64_t m, int64_t n,
                             int64_t k, uint16_t *y, int64_t ld_y, hipStream_t stream);
+// Decode-shaped product with the activation quantization fused in (1 <= m <= 16, k <= 4096):
+// bf16 A is quantized inside the kernel; aq's codes / scales / gs, where not NULL, receive the
+// quantized A (row strides aq.ld_codes / aq.ld_scales).  hipErrorNotSupported (nothing
+// launched) for other shapes.
+hipError_t launch_gemm_decode_fused(const void *a_bf16, int64_t ld_a, const GemmOperand &aq,
+                                    const GemmOperand &w, int64_t m, int64_t n, int64_t k,
+                                    uint16_t *y, int64_t ld_y, hipStream_t stream);
 // Small M (m <= 16, decode-shaped): W streamed at full width, A decoded in registers.
 hipError_t launch_gemm_small_m(const GemmOperand &a, const GemmOperand &w, int64_t m, int64_t n,
                                int64_t k, uint16_t *y, int64_t ld_y, hipStream_t stream);

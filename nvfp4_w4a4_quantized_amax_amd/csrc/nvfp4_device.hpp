@@ -107,6 +107,32 @@ __device__ __forceinline__ uint32_t absmax8(uint4 v) {
   return max(m & 0xFFFFu, m >> 16);
 }
 
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o, kWave));
+  return v;
+}
+
+// Workgroup-wide max (all threads get the result).  Ends with a barrier.
+__device__ __forceinline__ uint32_t block_max_u32(uint32_t v, uint32_t *red) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  v = wave_max_u32(v);
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  uint32_t b = red[0];
+  for (int w = 1; w < nw; ++w) b = max(b, red[w]);
+  __syncthreads();
+  return b;
+}
+
+__device__ __forceinline__ uint32_t absmax16(const uint4 &a, const uint4 &b) {
+  const uint32_t m = pk_max_u16(pk_max_u16(pk_max_u16(a.x & 0x7FFF7FFFu, a.y & 0x7FFF7FFFu),
+                                           pk_max_u16(a.z & 0x7FFF7FFFu, a.w & 0x7FFF7FFFu)),
+                                pk_max_u16(pk_max_u16(b.x & 0x7FFF7FFFu, b.y & 0x7FFF7FFFu),
+                                           pk_max_u16(b.z & 0x7FFF7FFFu, b.w & 0x7FFF7FFFu)));
+  return max(m & 0xFFFFu, m >> 16);
+}
+
 // Value of an OCP E4M3 byte (0..0x7E): exponent field e, mantissa m; e = 0 is m * 2^-9.
 __device__ __forceinline__ float e4m3_to_float(uint32_t b) {
   uint32_t e = b >> 3;

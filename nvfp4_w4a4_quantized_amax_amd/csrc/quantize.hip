@@ -45,32 +45,6 @@ __device__ __forceinline__ size_t block_index(uint32_t b, FastDiv bpr, int64_t l
   return (size_t)r * (size_t)ld_x8 + (size_t)cb * 2u;
 }
 
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o, kWave));
-  return v;
-}
-
-// Workgroup-wide max (all threads get the result).  Ends with a barrier.
-__device__ __forceinline__ uint32_t block_max_u32(uint32_t v, uint32_t *red) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  v = wave_max_u32(v);
-  if (lane == 0) red[wave] = v;
-  __syncthreads();
-  uint32_t b = red[0];
-  for (int w = 1; w < nw; ++w) b = max(b, red[w]);
-  __syncthreads();
-  return b;
-}
-
-__device__ __forceinline__ uint32_t absmax16(const uint4 &a, const uint4 &b) {
-  const uint32_t m = pk_max_u16(pk_max_u16(pk_max_u16(a.x & 0x7FFF7FFFu, a.y & 0x7FFF7FFFu),
-                                           pk_max_u16(a.z & 0x7FFF7FFFu, a.w & 0x7FFF7FFFu)),
-                                pk_max_u16(pk_max_u16(b.x & 0x7FFF7FFFu, b.y & 0x7FFF7FFFu),
-                                           pk_max_u16(b.z & 0x7FFF7FFFu, b.w & 0x7FFF7FFFu)));
-  return max(m & 0xFFFFu, m >> 16);
-}
-
 // ---------------------------------------------------------------------------------------------
 // Pass 1
 // ---------------------------------------------------------------------------------------------

@@ -281,8 +281,8 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-template <bool W2D>
-__device__ __forceinline__ void read_stage_frags(const LdsStage &S, int wave, int wm, int wn,
+template <bool W2D, class Stage>
+__device__ __forceinline__ void read_stage_frags(const Stage &S, int wave, int wm, int wn,
                                                  int lr, int kh, Frags<4, 4> &fr) {
   const int ra = wm * 128 + lr, rw = wn * 128 + lr;
 #pragma unroll
@@ -592,6 +592,212 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_grouped(GroupedArgs p) {
           const int64_t row = m0 + f * 32 + 8 * (r >> 2) + 4 * kh + (r & 3);
           if (row < r_end && col < p.n)
             ntstore_u16(p.y + row * p.ld_y + col, f32_to_bf16_rne(acc[f][g][r] * alpha));
+        }
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Grouped kernel with the pipelined K loop (K a multiple of 64, 4-byte aligned scale rows):
+// 128 x 256 tiles (tile rows waste less on the small experts than 256), two waves of 128 x 128
+// per workgroup, two workgroups per CU.  The K loop is the dense kernel's: windows staged
+// through two LDS stages, decode interleaved with the MFMAs.  A rows are gathered through
+// row_index while they are loaded.
+// ---------------------------------------------------------------------------------------------
+struct LdsStageG {
+  uint8_t a[128 * 32];
+  uint8_t w[256 * 32];
+  uint8_t as[128 * 4];
+  uint8_t ws[256 * 4];  // 1D: one row per W row; 2D: each wave's copy of the 16 band rows
+};
+
+// One thread's share of a window (128 threads): A chunks c = i * 128 + tid (i < 2) and W chunks
+// c = i * 128 + tid (i < 4), chunk c being half c % 2 of row c / 2; the scale bytes of A row tid
+// and of W rows tid and 128 + tid (1D) or band tid % 16 (2D, ws1 unused).
+struct WindowRegsG {
+  u32x4_t a0, a1, w0, w1, w2, w3;
+  uint32_t as, ws0, ws1;
+};
+
+template <bool W2D>
+__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_gemm_grouped_lds(GroupedArgs p) {
+  constexpr int BM = 128, BN = 256, NT = 128;
+  __shared__ __align__(16) LdsStageG st[2];
+  __shared__ int s_off[kMaxGroups + 1];
+  __shared__ int s_start[kMaxGroups + 1];  // first tile id of each group
+  __shared__ int s_part[NT];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wn = wave;
+  const int lr = lane & 31, kh = lane >> 5;
+  const int E = p.num_groups;
+  // Tile list: offsets clamped into [0, total_rows] against bad input, per-group tile counts,
+  // exclusive scan.
+  for (int e = tid; e <= E; e += NT) s_off[e] = min(max(p.offsets[e], 0), (int)p.total_rows);
+  __syncthreads();
+  constexpr int kPer = (kMaxGroups + NT - 1) / NT;
+  int local[kPer];
+  int sum = 0;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int e = tid * kPer + j;
+    int t = 0;
+    if (e < E) t = ((max(s_off[e + 1] - s_off[e], 0) + BM - 1) / BM) * p.tiles_n;
+    local[j] = t;
+    sum += t;
+  }
+  s_part[tid] = sum;
+  __syncthreads();
+  for (int o = 1; o < NT; o <<= 1) {
+    const int v = tid >= o ? s_part[tid - o] : 0;
+    __syncthreads();
+    s_part[tid] += v;
+    __syncthreads();
+  }
+  int run = s_part[tid] - sum;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int e = tid * kPer + j;
+    if (e < E) s_start[e] = run;
+    run += local[j];
+  }
+  if (tid == NT - 1) s_start[E] = s_part[NT - 1];
+  __syncthreads();
+  const int total_tiles = s_start[E];
+  const int64_t nwin = p.k / 64;  // >= 1
+
+  for (int t = blockIdx.x; t < total_tiles; t += gridDim.x) {
+    int lo = 0, hi = E;  // last group with s_start[e] <= t
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (s_start[mid] <= t) lo = mid;
+      else hi = mid;
+    }
+    const int e = lo;
+    const int local_t = t - s_start[e];
+    const int r_begin = s_off[e], r_end = s_off[e + 1];
+    const int mt = (r_end - r_begin + BM - 1) / BM;
+    const int tm = local_t % mt, tn = local_t / mt;
+    const int64_t m_tile = (int64_t)r_begin + (int64_t)tm * BM, n_tile = (int64_t)tn * BN;
+    const int64_t wbase = (int64_t)e * p.w_group_rows;
+
+    // Source rows of this thread's loads (A gathered through row_index; rows clamped into the
+    // group / expert, results of clamped rows are never stored).
+    auto a_src = [&](int64_t r) __attribute__((always_inline)) {
+      const int64_t gr = min(m_tile + r, (int64_t)r_end - 1);
+      return p.row_index ? (int64_t)p.row_index[gr] : gr;
+    };
+    const uint8_t *ga[2], *gw[4];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int c = i * NT + tid;
+      ga[i] = p.a.codes + a_src(c >> 1) * p.a.ld_codes + (c & 1) * 16;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = i * NT + tid;
+      gw[i] = p.w.codes + (wbase + min(n_tile + (c >> 1), p.n - 1)) * p.w.ld_codes + (c & 1) * 16;
+    }
+    const uint8_t *gas = p.a.scales + a_src(tid) * p.a.ld_scales;
+    const uint8_t *gws0, *gws1;
+    if (W2D) {
+      gws0 = p.w.scales +
+             ((wbase + n_tile) / 16 + min((int64_t)(lane & 15), (p.n - n_tile) / 16 - 1)) * p.w.ld_scales;
+      gws1 = gws0;
+    } else {
+      gws0 = p.w.scales + (wbase + min(n_tile + tid, p.n - 1)) * p.w.ld_scales;
+      gws1 = p.w.scales + (wbase + min(n_tile + NT + tid, p.n - 1)) * p.w.ld_scales;
+    }
+    auto load = [&](int64_t win, WindowRegsG &r) __attribute__((always_inline)) {
+      r.a0 = *(const u32x4_t *)(ga[0] + win * 32);
+      r.a1 = *(const u32x4_t *)(ga[1] + win * 32);
+      r.w0 = *(const u32x4_t *)(gw[0] + win * 32);
+      r.w1 = *(const u32x4_t *)(gw[1] + win * 32);
+      r.w2 = *(const u32x4_t *)(gw[2] + win * 32);
+      r.w3 = *(const u32x4_t *)(gw[3] + win * 32);
+      r.as = *(const uint32_t *)(gas + win * 4);
+      r.ws0 = *(const uint32_t *)(gws0 + win * 4);
+      r.ws1 = W2D ? 0u : *(const uint32_t *)(gws1 + win * 4);
+    };
+    auto store = [&](const WindowRegsG &r, LdsStageG &S) __attribute__((always_inline)) {
+      *(u32x4_t *)(S.a + code_offset(tid >> 1, tid & 1)) = r.a0;
+      *(u32x4_t *)(S.a + code_offset(64 + (tid >> 1), tid & 1)) = r.a1;
+      *(u32x4_t *)(S.w + code_offset(tid >> 1, tid & 1)) = r.w0;
+      *(u32x4_t *)(S.w + code_offset(64 + (tid >> 1), tid & 1)) = r.w1;
+      *(u32x4_t *)(S.w + code_offset(128 + (tid >> 1), tid & 1)) = r.w2;
+      *(u32x4_t *)(S.w + code_offset(192 + (tid >> 1), tid & 1)) = r.w3;
+      *(uint32_t *)(S.as + tid * 4) = r.as;
+      *(uint32_t *)(S.ws + tid * 4) = r.ws0;  // 2D: wave * 256 + lane * 4
+      if (!W2D) *(uint32_t *)(S.ws + (NT + tid) * 4) = r.ws1;
+    };
+
+    floatx16_t acc[4][4];
+#pragma unroll
+    for (int f = 0; f < 4; ++f)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) acc[f][g] = floatx16_t{};
+
+    __syncthreads();  // the previous tile's last fragment reads are done with both stages
+    WindowRegsG r;
+    load(0, r);
+    store(r, st[0]);
+    load(min((int64_t)1, nwin - 1), r);
+    lds_barrier();
+    Frags<4, 4> cur, nxt;
+    read_stage_frags<W2D>(st[0], wave, 0, wn, lr, kh, cur);
+    half2_t sa[4], sw[4];
+    window_scales(cur, sa, sw);
+    StepOps ev, od;
+    decode_step(cur, sa, sw, 0, ev);
+    for (int64_t w = 0; w + 1 < nwin; ++w) {
+      store(r, st[(w + 1) & 1]);
+      load(min(w + 2, nwin - 1), r);
+      decode_step(cur, sa, sw, 1, od);
+      mfma_step(ev, acc);
+      interleave_step_mem<0x200, 9, 0x020, 9>();
+      end_step(ev);
+      lds_barrier();
+      read_stage_frags<W2D>(st[(w + 1) & 1], wave, 0, wn, lr, kh, nxt);
+      decode_step(cur, sa, sw, 2, ev);
+      mfma_step(od, acc);
+      interleave_step_mem<0x100, 16>();
+      end_step(od);
+      decode_step(cur, sa, sw, 3, od);
+      mfma_step(ev, acc);
+      interleave_step();
+      end_step(ev);
+      window_scales(nxt, sa, sw);
+      decode_step(nxt, sa, sw, 0, ev);
+      mfma_step(od, acc);
+      interleave_step();
+      end_step(od);
+      cur = nxt;
+    }
+    decode_step(cur, sa, sw, 1, od);
+    mfma_step(ev, acc);
+    interleave_step();
+    end_step(ev);
+    decode_step(cur, sa, sw, 2, ev);
+    mfma_step(od, acc);
+    interleave_step();
+    end_step(od);
+    decode_step(cur, sa, sw, 3, od);
+    mfma_step(ev, acc);
+    interleave_step();
+    end_step(ev);
+    mfma_step(od, acc);
+
+    const float alpha = (*p.a.gs) * p.w.gs[e];
+    const int64_t n0 = n_tile + wn * 128;
+#pragma unroll
+    for (int f = 0; f < 4; ++f)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int64_t col = n0 + g * 32 + lr;
+#pragma unroll
+        for (int r2 = 0; r2 < 16; ++r2) {
+          const int64_t row = m_tile + f * 32 + 8 * (r2 >> 2) + 4 * kh + (r2 & 3);
+          if (row < r_end && col < p.n)
+            ntstore_u16(p.y + row * p.ld_y + col, f32_to_bf16_rne(acc[f][g][r2] * alpha));
         }
       }
   }
@@ -1028,6 +1234,21 @@ hipError_t launch_grouped_gemm(const GemmOperand &a, const int32_t *row_index,
   p.tiles_n = (int)((n + 64 * FN - 1) / (64 * FN));
   // Upper bound of the tile count: every group may add one partial m-tile.
   const int64_t max_tiles = ((total_rows + 64 * FM - 1) / (64 * FM) + num_groups) * p.tiles_n;
+  const bool pipelined = k % 64 == 0 && aligned4(a.scales) && a.ld_scales % 4 == 0 &&
+                         aligned4(w.scales) && w.ld_scales % 4 == 0;
+  if (pipelined) {
+    // Two 2-wave workgroups per CU walk the tile list.
+    static int cus = 0;
+    if (cus == 0 && hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, 0) != hipSuccess)
+      cus = 0;
+    const int64_t slots = 2 * (int64_t)(cus > 0 ? cus : 256);
+    const unsigned g = (unsigned)(max_tiles < slots ? (max_tiles < 1 ? 1 : max_tiles) : slots);
+    if (w.block_rows == 16)
+      hipLaunchKernelGGL((k_gemm_grouped_lds<true>), dim3(g), dim3(128), 0, stream, p);
+    else
+      hipLaunchKernelGGL((k_gemm_grouped_lds<false>), dim3(g), dim3(128), 0, stream, p);
+    return hipGetLastError();
+  }
   int64_t grid = max_tiles < 1024 ? max_tiles : 1024;
   if (grid < 1) grid = 1;
   if (w.block_rows == 16)

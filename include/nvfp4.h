@@ -32,6 +32,10 @@
  *    need it (cols always; rows for 16x16 tiles).
  * Codes, scales and gs are bit-exact for finite inputs with amax in [2^-96, bf16 max].
  * Inputs must be finite (NaN/Inf give unspecified codes, never a fault).
+ *
+ * Empty problems: a call with zero rows (rows == 0, m == 0, total_rows == 0) and otherwise
+ * valid sizes computes and writes nothing (not even a global scale) and returns NVFP4_OK; its
+ * data pointers may then be NULL.
  */
 #ifndef NVFP4_H
 #define NVFP4_H
@@ -85,8 +89,8 @@ int nvfp4_version(void);
  * Workspace.  Every call that takes `ws` needs at least the matching number of bytes, 256-byte
  * aligned; its contents need no initialization and carry nothing from one call to the next.  Its
  * first 8 KiB hold the per-workgroup partial maxima of the amax pass (and the grid-barrier slots
- * of the single-read quantizer); the rest holds the quantized activations of the GEMM calls.  Calls that may overlap in time
- * (different streams) need different workspaces.
+ * of the single-read quantizer); the rest holds the quantized activations of the GEMM calls.
+ * Calls that may overlap in time (different streams) need different workspaces.
  * ------------------------------------------------------------------------------------------- */
 size_t nvfp4_quantize_workspace_bytes(int64_t rows, int64_t cols);
 size_t nvfp4_gemm_workspace_bytes(int64_t m, int64_t n, int64_t k);

@@ -120,6 +120,8 @@ size_t nvfp4_grouped_gemm_workspace_bytes(int64_t tokens, int64_t k, int64_t tot
 
 nvfp4_status nvfp4_quantize_1d(const void *x, int64_t rows, int64_t cols, int64_t ld_x,
                                const nvfp4_tensor *out, void *ws, size_t ws_bytes, void *stream) {
+  if (!out) return NVFP4_ERR_NULL;
+  if (rows == 0 && cols > 0 && cols % 16 == 0) return NVFP4_OK;  // nothing to compute or write
   nvfp4_status s = check_bf16_input(x, rows, cols, ld_x);
   if (s) return s;
   s = check_tensor(out, rows, cols, true);
@@ -134,6 +136,8 @@ nvfp4_status nvfp4_quantize_1d(const void *x, int64_t rows, int64_t cols, int64_
 
 nvfp4_status nvfp4_quantize_2d(const void *w, int64_t rows, int64_t cols, int64_t ld_w,
                                const nvfp4_tensor *out, void *ws, size_t ws_bytes, void *stream) {
+  if (!out) return NVFP4_ERR_NULL;
+  if (rows == 0 && cols > 0 && cols % 16 == 0) return NVFP4_OK;  // nothing to compute or write
   nvfp4_status s = check_bf16_input(w, rows, cols, ld_w);
   if (s) return s;
   if (rows % 16) return NVFP4_ERR_SHAPE;
@@ -151,6 +155,7 @@ nvfp4_status nvfp4_quantize_2d(const void *w, int64_t rows, int64_t cols, int64_
 nvfp4_status nvfp4_dequantize(const nvfp4_tensor *q, void *y, int64_t ld_y, int out_dtype,
                               void *stream) {
   if (!q) return NVFP4_ERR_NULL;
+  if (q->rows == 0 && q->cols > 0 && q->cols % 16 == 0) return NVFP4_OK;  // empty
   nvfp4_status s = check_tensor(q, q->rows, q->cols, false);
   if (s) return s;
   if (!y) return NVFP4_ERR_NULL;
@@ -167,8 +172,10 @@ nvfp4_status nvfp4_dequantize(const nvfp4_tensor *q, void *y, int64_t ld_y, int 
 nvfp4_status nvfp4_gemm_w4a4(const void *a_bf16, int64_t m, int64_t k, int64_t ld_a,
                              const nvfp4_tensor *a_q, const nvfp4_tensor *w, void *y,
                              int64_t ld_y, void *ws, size_t ws_bytes, void *stream) {
-  if (!w || !y) return NVFP4_ERR_NULL;
+  if (!w) return NVFP4_ERR_NULL;
   if (m < 0 || k <= 0 || k % 16) return NVFP4_ERR_SHAPE;
+  if (m == 0) return NVFP4_OK;  // empty product: nothing to compute or write
+  if (!y) return NVFP4_ERR_NULL;
   const int64_t n = w->rows;
   nvfp4_status s = check_tensor(w, n, k, true);
   if (s) return s;
@@ -241,10 +248,13 @@ nvfp4_status nvfp4_grouped_gemm_w4a4(const void *a_bf16, int64_t tokens, int64_t
                                      const int32_t *offsets, int32_t num_groups,
                                      const nvfp4_tensor *w, int64_t n, void *y, int64_t ld_y,
                                      void *ws, size_t ws_bytes, void *stream) {
-  if (!w || !y || !offsets) return NVFP4_ERR_NULL;
+  if (!w) return NVFP4_ERR_NULL;
   if (num_groups < 1) return NVFP4_ERR_SHAPE;
   if (num_groups > 1024) return NVFP4_ERR_UNSUPPORTED;
   if (tokens < 0 || total_rows < 0 || k <= 0 || k % 16 || n < 1) return NVFP4_ERR_SHAPE;
+  if (total_rows == 0) return NVFP4_OK;  // no routed rows: nothing to compute or write
+  if (tokens == 0) return NVFP4_ERR_SHAPE;  // rows to fill but no tokens to take them from
+  if (!y || !offsets) return NVFP4_ERR_NULL;
   if (total_rows >= ((int64_t)1 << 30) || tokens >= ((int64_t)1 << 30)) return NVFP4_ERR_SHAPE;
   if (!row_index && tokens != total_rows) return NVFP4_ERR_SHAPE;
   nvfp4_status s = check_tensor(w, (int64_t)num_groups * n, k, true);
@@ -269,7 +279,6 @@ nvfp4_status nvfp4_grouped_gemm_w4a4(const void *a_bf16, int64_t tokens, int64_t
   if (ws_bytes < nvfp4_grouped_gemm_workspace_bytes(tokens, k, total_rows, num_groups) ||
       !aligned(ws, kAlign))
     return NVFP4_ERR_WORKSPACE;
-  if (total_rows == 0 || tokens == 0) return NVFP4_OK;
 
   hipStream_t st = (hipStream_t)stream;
   uint8_t *base = (uint8_t *)ws;

@@ -62,7 +62,7 @@ def test_ragged_shapes(nv, rows, cols):
 
 def test_activation_distribution_band(nv):
     """The activation workload's distribution (Laplace x log-normal column gains) on a 512-row
-    band, both through the two-pass path."""
+    band (the single-read path)."""
     x = W.activation(seed=1, rows=512, cols=8192)["x"]
     check_1d(nv, x, "activation band")
 
@@ -100,9 +100,9 @@ def test_adversarial_ties_and_zeros(nv):
     x = W.to_bf16_bits(adversarial_rows())
     x = np.concatenate([x, x[::-1]], axis=1)  # two blocks per row
     check_1d(nv, x, "adversarial")
-    # the same values in a tensor large enough for the two-pass path
+    # the same values in a tensor large enough for the multi-workgroup path
     big = np.tile(x, (512, 4))
-    check_1d(nv, big, "adversarial two-pass")
+    check_1d(nv, big, "adversarial, large")
 
 
 @pytest.mark.parametrize("amax_sig", [21, 42, 63, 105, 128, 255])
@@ -115,7 +115,7 @@ def test_short_global_scales(nv, amax_sig):
     x[np.abs(x) > amax_sig * 2.0 ** -3] = 0
     x = W.to_bf16_bits(x)
     check_1d(nv, x, f"short gs {amax_sig}")
-    check_1d(nv, np.tile(x, (200, 1)), f"short gs {amax_sig} two-pass")
+    check_1d(nv, np.tile(x, (200, 1)), f"short gs {amax_sig}, large")
 
 
 def test_extremes(nv):
@@ -151,8 +151,9 @@ def test_quantize_2d(nv, rows, cols):
 
 
 def test_activation_full_size_sampled(nv):
-    """The 8192 x 8192 activation workload through the two-pass path: the global scale against
-    the oracle's (from the full amax), every byte of 96 sampled rows against the oracle."""
+    """The 8192 x 8192 activation workload (the single-read path, as timed by the benchmark):
+    the global scale against the oracle's (from the full amax), every byte of 96 sampled rows
+    against the oracle."""
     x = W.activation()["x"]
     q = nv.quantize_1d(dev_bf16(x))
     c, s, g = host_q(q)
@@ -163,3 +164,34 @@ def test_activation_full_size_sampled(nv):
     oc, os_ = O.encode_1d(x[rows], og)
     assert_codes_equal(s[rows], os_, "full-size scales")
     assert_codes_equal(c[rows], oc, "full-size codes")
+
+
+def test_empty_tensors(nv):
+    """Zero-row inputs through the binding: every call succeeds and leaves its outputs alone."""
+    x = torch.empty((0, 64), dtype=torch.bfloat16, device="cuda")
+    q = nv.quantize_1d(x)
+    assert q.codes.shape == (0, 32) and q.scales.shape == (0, 4)
+    q2 = nv.quantize_2d(x)
+    assert q2.scales.shape == (0, 4)
+    assert nv.dequantize(q).shape == (0, 64)
+    w = nv.quantize_2d(dev_bf16(W.to_bf16_bits(np.ones((32, 64)))))
+    assert nv.gemm_w4a4(x, w).shape == (0, 32)
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("path", ["two_pass", "cooperative"])
+def test_other_quantize_paths(path):
+    """The two-kernel path (taken when one workgroup per CU cannot be resident) and the
+    cooperative launch of the single-read kernel, selected through NVFP4_QUANT_PATH in a
+    separate process (the library reads it once per process)."""
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import os
+    import subprocess
+    import sys
+    here = os.path.dirname(os.path.abspath(__file__))
+    env = dict(os.environ, NVFP4_QUANT_PATH=path)
+    r = subprocess.run([sys.executable, "-u", os.path.join(here, "quantize_path_check.py")],
+                       env=env, capture_output=True, text=True, timeout=110)
+    assert r.returncode == 0, r.stdout[-2000:] + r.stderr[-2000:]
+    assert r.stdout.count(" ok") == 3, r.stdout

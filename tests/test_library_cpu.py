@@ -132,3 +132,23 @@ def test_grouped_validation():
     assert grouped(FAKE, 32, 128, None, FAKE, 64, FAKE, 8, qt(8 * 40, 128, 16), 40) == \
         nv.ERR_SHAPE                                                               # n % 16
     assert grouped(FAKE, 32, 128, None, FAKE, 64, FAKE, 8, w, 64, ws=None) == nv.ERR_WORKSPACE
+
+
+def test_empty_problems_need_no_buffers():
+    """Zero rows: nothing is computed or written, NVFP4_OK is returned and the data pointers
+    may be NULL (no GPU work is launched, so this runs without a device)."""
+    def empty(rows, cols, br):
+        return nv.CTensor(None, cols // 2, None, cols // 16, None, rows, cols, br, 0)
+    q1, q2 = empty(0, 64, 1), empty(0, 64, 16)
+    assert L.nvfp4_quantize_1d(None, 0, 64, 64, ctypes.byref(q1), None, 0, None) == nv.OK
+    assert L.nvfp4_quantize_2d(None, 0, 64, 64, ctypes.byref(q2), None, 0, None) == nv.OK
+    assert L.nvfp4_dequantize(ctypes.byref(q1), None, 64, nv.OUT_F32, None) == nv.OK
+    w = empty(32, 64, 16)
+    assert L.nvfp4_gemm_w4a4(None, 0, 64, 64, None, ctypes.byref(w), None, 32, None, 0,
+                             None) == nv.OK
+    assert L.nvfp4_grouped_gemm_w4a4(None, 4, 64, 64, None, None, 0, None, 2, ctypes.byref(w),
+                                     16, None, 16, None, 0, None) == nv.OK
+    # but bad sizes are still rejected, and rows to fill without tokens is an error
+    assert L.nvfp4_quantize_1d(None, 0, 40, 64, ctypes.byref(q1), None, 0, None) != nv.OK
+    assert L.nvfp4_grouped_gemm_w4a4(None, 0, 64, 64, None, None, 5, None, 2, ctypes.byref(w),
+                                     16, None, 16, None, 0, None) == nv.ERR_SHAPE

@@ -27,10 +27,9 @@ struct QuantTables {
   float pad[2];
   // ent[c], c = 0..127, everything a block whose guessed scale code is c needs, in one 16-byte
   // read:
-  //   x = thresh[c] | thresh[c + 1] << 16, thresh[s] (s = 1..126) being the smallest bf16
-  //       magnitude pattern whose block scale code is >= s (thresh[0] = 0, thresh[127] = 0xFFFF,
-  //       never reached);
-  //   y, z, w = float bits of the element multipliers of codes c - 1, c and c + 1.
+  //   x = thresh[c + 1], thresh[s] (s = 1..126) being the smallest bf16 magnitude pattern whose
+  //       block scale code is >= s (thresh[127] = 0xFFFF, never reached);
+  //   y, z = float bits of the element multipliers of codes c and c + 1; w unused.
   // The multiplier k of scale code s is a float with RNE_fp4(RN_fp32(x * k)) equal to the exact
   // nearest-code rule for every bf16 x; a negative value (-k) means no such k was found and the
   // block takes the exact slow path.  Codes 0, -1 and 127 have k = 0.
@@ -275,14 +274,13 @@ __device__ inline void build_tables(QuantTables &t, TableScratch &sc, float gs) 
     sc.kbase[tid] = multiplier_is_exact(ku, S) ? ku : (multiplier_is_exact(kd, S) ? kd : -k0);
   }
   __syncthreads();
-  // Phase D: each entry holds its threshold pair and the multipliers of its code and both
-  // neighbours (a code's multiplier is its mantissa's base multiplier scaled by 2^-exponent).
+  // Phase D: each entry holds the threshold of the next code and the multipliers of its code
+  // and the next (a code's multiplier is its mantissa's base multiplier scaled by 2^-exponent).
   if (tid < 128) {
     const int s = tid;
-    const uint32_t th = (uint32_t)sc.thresh[s] | ((s == 127 ? 0xFFFFu : (uint32_t)sc.thresh[s + 1]) << 16);
-    t.ent[s] = make_uint4(th, __float_as_uint(code_multiplier(s - 1, sc, usable)),
-                          __float_as_uint(code_multiplier(s, sc, usable)),
-                          __float_as_uint(code_multiplier(s + 1, sc, usable)));
+    const uint32_t th = s == 127 ? 0xFFFFu : (uint32_t)sc.thresh[s + 1];
+    t.ent[s] = make_uint4(th, __float_as_uint(code_multiplier(s, sc, usable)),
+                          __float_as_uint(code_multiplier(s + 1, sc, usable)), 0u);
   }
   __syncthreads();
 }
@@ -300,9 +298,11 @@ __device__ __forceinline__ float inv6gs_of(float gs) {
 // Block-scale code and element codes
 // ---------------------------------------------------------------------------------------------
 
-// E4M3 code of a block whose |max| bf16 pattern is `bam`, and its element multiplier: a guess
-// from bam * inv6gs (within one code of the answer), corrected with the exact thresholds of
-// one table entry, which also holds the three candidate multipliers.
+// E4M3 code of a block whose |max| bf16 pattern is `bam`, and its element multiplier.  The
+// guess truncates t = bam * inv6gs to an E4M3 code (top three mantissa bits for normal codes,
+// floor(t * 2^9) below 2^-6).  t is within 2^-23 (relative) of the exact bam / (6 gs), so the
+// nearest code is the guess or the next one: one comparison with the exact threshold of the
+// next code decides, and the same table entry holds both candidate multipliers.
 __device__ __forceinline__ int scale_code(uint32_t bam, const QuantTables &tab, float inv6gs,
                                           float *k_out) {
   const float t = __uint_as_float(bam << 16) * inv6gs;
@@ -315,10 +315,9 @@ __device__ __forceinline__ int scale_code(uint32_t bam, const QuantTables &tab, 
   typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
   const u32x4 ev = __builtin_nontemporal_load((const u32x4 *)&tab.ent[cand]);
   const uint4 e = make_uint4(ev[0], ev[1], ev[2], ev[3]);
-  const bool up = bam >= (e.x >> 16);
-  const bool dn = bam < (e.x & 0xFFFFu);
-  *k_out = __uint_as_float(up ? e.w : (dn ? e.y : e.z));
-  return cand + (up ? 1 : 0) - (dn ? 1 : 0);
+  const bool up = bam >= e.x;
+  *k_out = __uint_as_float(up ? e.z : e.y);
+  return cand + (up ? 1 : 0);
 }
 
 __device__ __forceinline__ int scale_code(uint32_t bam, const QuantTables &tab, float *k_out) {

@@ -951,7 +951,6 @@ template <bool W2D, bool FUSED>
 __global__ __launch_bounds__(kDecWaves * 64) void k_gemm_decode(SmallMArgs p) {
   __shared__ floatx4_t s_red[2][kDecWaves][kWave];
   __shared__ QuantTables tab;
-  __shared__ TableScratch scr;
   __shared__ uint32_t red[kDecWaves];
   // Quantized A slice of each wave (fused form): up to 16 rows x 16 blocks.
   __shared__ __align__(8) uint8_t s_acodes[FUSED ? kDecWaves : 1][16 * 16 * 8];
@@ -1003,7 +1002,7 @@ __global__ __launch_bounds__(kDecWaves * 64) void k_gemm_decode(SmallMArgs p) {
 #pragma unroll
     for (int w2 = 1; w2 < kDecWaves; ++w2) mx = max(mx, red[w2]);
     gs_a = global_scale_from_amax_bits(mx);
-    build_tables(tab, scr, gs_a);
+    build_tables(tab, gs_a);
     if (p.aq_gs && blockIdx.x == 0 && threadIdx.x == 0) *p.aq_gs = gs_a;
     const float inv6gs = tab.inv6gs;
     // Encode; codes and scales of the slice go to this wave's LDS corner (row-major, 16 blocks

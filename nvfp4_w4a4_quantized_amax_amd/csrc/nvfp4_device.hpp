@@ -217,70 +217,56 @@ __device__ __forceinline__ uint32_t scale_threshold(int s, double gsd) {
   return min(th, 0xFFFFu);
 }
 
-struct TableScratch {
-  float kbase[8];    // multiplier for block scale (1 + m/8) * gs, m = 0..7; negative: slow path
-  uint32_t fail[8];
-  uint16_t thresh[128];
-};
-
 // Fill `t` (in LDS) for global scale gs.  Must be called by every thread of a workgroup of at
-// least 128 threads; ends with a barrier.  A usable gs lies in (0, 3e38); otherwise every block
-// gets scale 0.
+// least 128 threads; ends with a barrier (the only one).  A usable gs lies in (0, 3e38);
+// otherwise every block gets scale 0.
 //
 // Scaling a block scale by 2^j scales the critical bf16 values around each midpoint by 2^j and
 // RN(1/S) by 2^-j, leaving x * k and every decision unchanged (no value leaves the normal range
 // for amax in the supported range).  So the multiplier only has to be checked for the 8 E4M3
 // mantissas (1 + m/8) * gs; the multiplier of any code is that of its mantissa times a power of
 // two.  Subnormal E4M3 codes normalize onto the same mantissas.
-// Element multiplier of block-scale code s (0 for s outside 1..126, and for an unusable gs).
-__device__ __forceinline__ float code_multiplier(int s, const TableScratch &sc, bool usable) {
-  if (!usable || s < 1 || s > 126) return 0.0f;
-  const uint32_t vb = __float_as_uint(e4m3_to_float((uint32_t)s));
-  const int m = (int)((vb >> 20) & 7u);
-  const int E = (int)((vb >> 23) & 0xFFu) - 127;
-  return ldexpf(sc.kbase[m], -E);
-}
-
-__device__ inline void build_tables(QuantTables &t, TableScratch &sc, float gs) {
+//
+// Threads 0..127 (two whole waves) each write one entry.  Both waves run the 8 x 7 multiplier
+// checks themselves (lane 7m + i checks mantissa m at E2M1 midpoint i), combine them with a
+// ballot, repair a failing mantissa in the wave (rare) and pass the base multipliers around
+// with shuffles, so nothing has to meet in LDS before the entries are written.
+__device__ inline void build_tables(QuantTables &t, float gs) {
   const int tid = threadIdx.x;
   const double gsd = (double)gs;
   const bool usable = gs > 0.0f && gs < 3.0e38f;
-  // Phase A: thresholds (threads 0..127), base multipliers (threads 0..7 also).
   if (tid < 128) {
-    const int s = tid;
-    sc.thresh[s] = (uint16_t)((s == 0) ? 0u : ((s == 127 || !usable) ? 0xFFFFu : scale_threshold(s, gsd)));
-  }
-  if (tid < 8) {
-    sc.kbase[tid] = usable ? (float)(1.0 / ((1.0 + tid * 0.125) * gsd)) : 0.0f;
-    sc.fail[tid] = 0;
+    const int lane = tid & 63;
+    const int m = lane / 7, i = lane - m * 7;
+    const bool checker = usable && lane < 56;
+    const double S = (1.0 + m * 0.125) * gsd;
+    float kb = checker ? (float)(1.0 / S) : 0.0f;
+    const bool ok = checker ? multiplier_ok_at(kb, S, i) : true;
+    const unsigned long long bad = __ballot(!ok);
+    if (checker && i == 0 && ((bad >> (7 * m)) & 0x7Full)) {
+      // The rounded reciprocal fails somewhere: try the neighbouring floats, else take the exact
+      // path (negative multiplier).
+      const float ku = __uint_as_float(__float_as_uint(kb) + 1u);
+      const float kd = __uint_as_float(__float_as_uint(kb) - 1u);
+      kb = multiplier_is_exact(ku, S) ? ku : (multiplier_is_exact(kd, S) ? kd : -kb);
+    }
+    // Multiplier of block-scale code c: its mantissa's base multiplier (held by lane 7m) scaled
+    // by 2^-exponent; 0 outside 1..126.
+    auto code_multiplier = [&](int c) {
+      const uint32_t vb = __float_as_uint(e4m3_to_float((uint32_t)min(max(c, 1), 126)));
+      const int mc = (int)((vb >> 20) & 7u);
+      const int E = (int)((vb >> 23) & 0xFFu) - 127;
+      const float base = __shfl(kb, 7 * mc, kWave);
+      return (usable && c >= 1 && c <= 126) ? ldexpf(base, -E) : 0.0f;
+    };
+    const int c = tid;
+    const uint32_t th = (c + 1 > 126 || !usable) ? 0xFFFFu : scale_threshold(c + 1, gsd);
+    const float k0 = code_multiplier(c), k1 = code_multiplier(c + 1);
+    t.ent[c] = make_uint4(th, __float_as_uint(k0), __float_as_uint(k1), 0u);
   }
   if (tid == 0) {
     t.gs = gs;
     t.inv6gs = usable ? (float)(1.0 / (6.0 * gsd)) : 0.0f;
-  }
-  __syncthreads();
-  // Phase B: 8 mantissas x 7 midpoints, one check per thread.
-  if (usable && tid < 56) {
-    const int m = tid / 7, i = tid - m * 7;
-    if (!multiplier_ok_at(sc.kbase[m], (1.0 + m * 0.125) * gsd, i)) sc.fail[m] = 1;
-  }
-  __syncthreads();
-  // Phase C (rare): a failing mantissa tries the neighbouring floats, else takes the exact path.
-  if (usable && tid < 8 && sc.fail[tid]) {
-    const float k0 = sc.kbase[tid];
-    const double S = (1.0 + tid * 0.125) * gsd;
-    const float ku = __uint_as_float(__float_as_uint(k0) + 1u);
-    const float kd = __uint_as_float(__float_as_uint(k0) - 1u);
-    sc.kbase[tid] = multiplier_is_exact(ku, S) ? ku : (multiplier_is_exact(kd, S) ? kd : -k0);
-  }
-  __syncthreads();
-  // Phase D: each entry holds the threshold of the next code and the multipliers of its code
-  // and the next (a code's multiplier is its mantissa's base multiplier scaled by 2^-exponent).
-  if (tid < 128) {
-    const int s = tid;
-    const uint32_t th = s == 127 ? 0xFFFFu : (uint32_t)sc.thresh[s + 1];
-    t.ent[s] = make_uint4(th, __float_as_uint(code_multiplier(s, sc, usable)),
-                          __float_as_uint(code_multiplier(s + 1, sc, usable)), 0u);
   }
   __syncthreads();
 }

@@ -83,14 +83,14 @@ __global__ __launch_bounds__(kQThreads) void k_amax(const uint4 *__restrict__ x,
 
 // Prologue of every encode workgroup: global amax from the slots, FP32 global scale, tables.
 __device__ __forceinline__ float tables_from_slots(const uint32_t *__restrict__ slots, int n_slots,
-                                                   QuantTables &tab, TableScratch &scr,
+                                                   QuantTables &tab,
                                                    uint32_t *red, float *__restrict__ gs_out) {
   uint32_t m = 0;
   for (int i = threadIdx.x; i < n_slots; i += blockDim.x) m = max(m, slots[i]);
   m = block_max_u32(m, red);
   const float gs = global_scale_from_amax_bits(m);
   if (blockIdx.x == 0 && threadIdx.x == 0) *gs_out = gs;
-  build_tables(tab, scr, gs);
+  build_tables(tab, gs);
   return gs;
 }
 
@@ -142,9 +142,8 @@ __global__ __launch_bounds__(kQThreads) void k_encode_1d(const uint4 *__restrict
                                                          const uint32_t *__restrict__ slots,
                                                          int n_slots, float *__restrict__ gs_out) {
   __shared__ QuantTables tab;
-  __shared__ TableScratch scr;
   __shared__ uint32_t red[kQWaves];
-  tables_from_slots(slots, n_slots, tab, scr, red, gs_out);
+  tables_from_slots(slots, n_slots, tab, red, gs_out);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const uint32_t S = gridDim.x * kQWaves;
   const uint32_t n_tiles = (n_blocks + kTileBlocks - 1) / kTileBlocks;
@@ -199,7 +198,6 @@ __global__ __launch_bounds__(WAVES * 64, 1) void k_quantize_persistent(
     unsigned long long *__restrict__ slots, unsigned long long epoch,
     float *__restrict__ gs_out, uint32_t *__restrict__ status) {
   __shared__ QuantTables tab;
-  __shared__ TableScratch scr;
   __shared__ uint32_t red[WAVES];
   __shared__ uint32_t s_amax;
   // LDS-resident tiles: [tile][half][wave][lane], one 16-byte half-block per lane, and each
@@ -310,7 +308,7 @@ __global__ __launch_bounds__(WAVES * 64, 1) void k_quantize_persistent(
   __syncthreads();
   const float gs = global_scale_from_amax_bits(s_amax);
   if (blockIdx.x == 0 && threadIdx.x == 0) *gs_out = gs;
-  build_tables(tab, scr, gs);
+  build_tables(tab, gs);
   const float inv6gs = tab.inv6gs;
 
   // Phase 2: encode the register tiles; each freed register pair immediately starts the re-read
@@ -364,9 +362,8 @@ __global__ __launch_bounds__(kQThreads) void k_encode_2d(const uint16_t *__restr
                                                          const uint32_t *__restrict__ slots,
                                                          int n_slots, float *__restrict__ gs_out) {
   __shared__ QuantTables tab;
-  __shared__ TableScratch scr;
   __shared__ uint32_t red[kQWaves];
-  tables_from_slots(slots, n_slots, tab, scr, red, gs_out);
+  tables_from_slots(slots, n_slots, tab, red, gs_out);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t tiles_c = cols / 16;
   const int64_t groups_c = (tiles_c + 3) / 4;
@@ -405,7 +402,6 @@ __global__ __launch_bounds__(kSmallThreads) void k_quantize_small(const uint16_t
                                                                   int64_t ld_x, EncOut o,
                                                                   float *__restrict__ gs_out) {
   __shared__ QuantTables tab;
-  __shared__ TableScratch scr;
   __shared__ uint32_t red[kSmallThreads / kWave];
   const int cpr = cols / 8;
   const int n_chunks = rows * cpr;
@@ -417,7 +413,7 @@ __global__ __launch_bounds__(kSmallThreads) void k_quantize_small(const uint16_t
   m = block_max_u32(m, red);
   const float gs = global_scale_from_amax_bits(m);
   if (threadIdx.x == 0) *gs_out = gs;
-  build_tables(tab, scr, gs);
+  build_tables(tab, gs);
   // One lane per 16-value block.
   const int bpr = cols / 16;
   const int n_blocks = rows * bpr;

@@ -282,17 +282,31 @@ __global__ __launch_bounds__(WAVES * 64, 1) void k_quantize_persistent(
   if (wave == 0) {
     uint32_t mx = 0;
     bool done = false;
-    // Relaxed device-coherent polls until every slot carries this call's epoch.
+    // Relaxed device-coherent polls until every slot carries this call's epoch.  Lane l watches
+    // slots l, l + 64, ...; each round issues all of its loads at once and reloads only the
+    // slots it has not yet seen, so the polls put little load on the few lines they share with
+    // every other workgroup.
+    constexpr int kPoll = (kMaxPersistentSlots + kWave - 1) / kWave;
+    uint32_t pending = 0, lm = 0;
+#pragma unroll
+    for (int r = 0; r < kPoll; ++r)
+      if (lane + kWave * r < (int)gridDim.x) pending |= 1u << r;
     for (uint32_t it = 0; it < kSpinLimit && !done; ++it) {
-      bool ok = true;
-      uint32_t lm = 0;
-      for (uint32_t j = lane; j < gridDim.x; j += 64) {
-        const unsigned long long v =
-            __hip_atomic_load(slots + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        ok = ok && ((v & ~0xFFFFull) == tag);
-        lm = max(lm, (uint32_t)(v & 0xFFFFu));
+      unsigned long long v[kPoll];
+#pragma unroll
+      for (int r = 0; r < kPoll; ++r)
+        v[r] = ((pending >> r) & 1u)
+                   ? __hip_atomic_load(slots + lane + kWave * r, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT)
+                   : 0ull;
+#pragma unroll
+      for (int r = 0; r < kPoll; ++r) {
+        if (((pending >> r) & 1u) && (v[r] & ~0xFFFFull) == tag) {
+          lm = max(lm, (uint32_t)(v[r] & 0xFFFFu));
+          pending &= ~(1u << r);
+        }
       }
-      if (__all(ok)) {
+      if (__all(pending == 0)) {
         mx = wave_max_u32(lm);
         done = true;
       } else {

@@ -47,6 +47,9 @@ What the pages leave open, and the reading taken here (each is listed in the des
   R9  inputs are finite (NaN/Inf raise here).
   R10 GEMM acceptance: |Y - Y64| <= 1e-3 * ||Y64[m, :]||_2 + 2^-8 * |Y64[m, n]|: the stated
       relative budget for the fp32 accumulation plus half a bf16 ulp for the bf16 output.
+  R13 W4A16 (the weight-only contrast the pages draw): Y = A . W_hat^T with A's bf16 values
+      taken exactly and W_hat the exact reconstruction of the NVFP4 weight; no activation
+      scale.  Accepted with R10's bound.
 
 Exactness: every threshold below is a product of at most 31 significant bits (a midpoint with
 <= 7 bits times the 24-bit gs), so float64 holds it exactly and every comparison is the exact
@@ -328,6 +331,21 @@ def grouped_gemm64(a_q, row_index, offsets, w_list):
             w = dequantize(wq[0], wq[1], wq[2], wq[3], out="f64")
             y[lo:hi] = a[lo:hi] @ w.T
     return y
+
+
+def gemm64_w4a16(a_bf16_bits, w_q):
+    """Weight-only product W4A16 (reading R13): the weights are stored in NVFP4 and
+    reconstructed to 16-bit floating point, the activations stay 16-bit
+    ([P1] "The Meaning and Advantages of W4A4": W4A16 dequantizes the 4-bit weights for a
+    high-precision multiply; [P2] "What does W4A4 mean?"; [P3] "What W4A4, W4A8, and W4A16
+    Mean").
+
+    a_bf16_bits: uint16 M x K (bf16 bit patterns), used at their exact values.
+    w_q: (codes, scales, gs, block_rows) of the N x K weight.
+    Y = A . W_hat^T in float64, W_hat the exact reconstruction (code value * block scale * gs)."""
+    a = _as_f64(a_bf16_bits)
+    w = dequantize(w_q[0], w_q[1], w_q[2], w_q[3], out="f64")
+    return a @ w.T
 
 
 def row_tolerance(y64, rel=1e-3):

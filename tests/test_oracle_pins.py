@@ -446,3 +446,58 @@ def test_dequantize_bf16_is_rne_of_fp32():
     b = O.dequantize(codes, scales, gs, 1, out="bf16")
     want = torch.from_numpy(f32).to(torch.bfloat16).view(torch.int16).numpy().astype(np.uint16)
     assert np.array_equal(b, want)
+
+
+# ---------------------------------------------------------------------------------------------
+# W4A16 (weights NVFP4, activations bf16)
+# ---------------------------------------------------------------------------------------------
+
+
+def test_w4a16_permutation_closed_form():
+    """W = P (a permutation with no fixed points and no 2-cycles, so a transposed operand
+    differs) quantized with 1D blocks: each row's one nonzero block has bamax 1 = amax, scale
+    448 and code 6, so W_hat = 2688 gs_W P and Y[m, i] = 2688 gs_W A[m, pi(i)] exactly."""
+    n = 96
+    pi = (np.arange(n) * 5 + 7) % n          # 5 is invertible mod 96; pi^2 != id
+    assert np.all(pi != np.arange(n)) and np.any(pi[pi] != np.arange(n))
+    p = np.zeros((n, n))
+    p[np.arange(n), pi] = 1.0
+    wq = O.quantize_1d(W.to_bf16_bits(p))
+    assert wq[2] == np.float32(1 / 2688)
+    rng = np.random.default_rng(31)
+    a = rand_bf16(rng, (5, n), 3.0)
+    y = O.gemm64_w4a16(a, wq + (1,))
+    af = O.bf16_bits_to_f64(a)
+    assert np.array_equal(y, af[:, pi] * (2688 * float(wq[2])))
+
+
+def test_w4a16_exact_small_brute_force():
+    """A (4 x 48, bf16) times a 2D-quantized W (16 x 48): exact rational triple loop over the
+    bf16 values of A and the brute-force reconstruction of W."""
+    rng = np.random.default_rng(32)
+    a = rand_bf16(rng, (4, 48), 2.0)
+    w = rand_bf16(rng, (16, 48), 0.05)
+    wq = O.quantize_2d(w)
+    _, _, _, wv = brute_quantize(w, 16)
+    y = O.gemm64_w4a16(a, wq + (16,))
+    for m in range(4):
+        for n in range(16):
+            exact = sum(frac_of_bf16(a[m, k]) * wv[n][k] for k in range(48))
+            assert abs(Fraction(y[m, n]) - exact) <= abs(exact) * Fraction(1, 2 ** 45) + Fraction(1, 2 ** 200)
+
+
+def test_w4a16_equals_w4a4_on_representable_activations():
+    """When A is itself an NVFP4 reconstruction that bf16 holds exactly (global scale a power
+    of two, so every value has at most 6 significant bits), the weight-only product of those
+    bf16 values equals the W4A4 product of the quantized A."""
+    rng = np.random.default_rng(33)
+    x = rng.standard_normal((6, 64))
+    x[0, 0] = 2688 * 2.0 ** -3                # amax = 2688 * 2^-3 -> gs = 2^-3 exactly
+    x = np.clip(x, -x[0, 0], x[0, 0])
+    aq = O.quantize_1d(W.to_bf16_bits(x))
+    assert aq[2] == np.float32(2.0 ** -3)
+    a_hat = O.dequantize(*aq, 1, out="f64")
+    a_bits = W.to_bf16_bits(a_hat)
+    assert np.array_equal(O.bf16_bits_to_f64(a_bits), a_hat)
+    wq = O.quantize_2d(rand_bf16(rng, (32, 64), 0.02)) + (16,)
+    assert np.array_equal(O.gemm64_w4a16(a_bits, wq), O.gemm64(aq + (1,), wq))

@@ -14,7 +14,8 @@ enough distinct input/output buffers (4 x 168 MiB) that no step finds its input 
 Infinity Cache left there by the previous step.
 
 "workloads" adds the other shapes the library serves (decode-, prefill- and MoE-shaped W4A4
-GEMMs, activation quantization inside the call), each timed the same way with its own roofline.
+GEMMs, activation quantization inside the call; the weight-only W4A16 form of the decode
+shapes), each timed the same way with its own roofline.
 "cpu_baseline" times the CPU oracle (test infrastructure, float64 numpy) on the same headline
 input on the host.
 """
@@ -144,6 +145,13 @@ def extra_workloads(args, torch, np, nv, W, only):
             nbytes = n * k // 2 + (n // 16) * (k // 16) + 4 + m * k * 2 + m * n * 2
             gbs = nbytes / (ms * 1e-3) / 1e9
             out[f"decode_m{m}"] = {
+                "shape": [m, n, k], "ms": ms, "bound": "hbm", "achieved": gbs,
+                "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                "tflops": 2 * m * n * k / (ms * 1e-3) / 1e12}
+            # Weight-only form of the same product: the bf16 A is used as is.
+            ms = timed(lambda i: nv.gemm_w4a16(a, wqs[i % nw], y=y), steps, warm, torch)
+            gbs = nbytes / (ms * 1e-3) / 1e9
+            out[f"decode_w4a16_m{m}"] = {
                 "shape": [m, n, k], "ms": ms, "bound": "hbm", "achieved": gbs,
                 "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
                 "tflops": 2 * m * n * k / (ms * 1e-3) / 1e12}

@@ -152,6 +152,25 @@ nvfp4_status nvfp4_gemm_w4a4(const void *a_bf16, int64_t m, int64_t k, int64_t l
                              int64_t ld_y, void *ws, size_t ws_bytes, void *stream);
 
 /* ---------------------------------------------------------------------------------------------
+ * nvfp4_gemm_w4a16 — weight-only product: NVFP4 weights, 16-bit activations ("NVFP4 Dynamic
+ * Quantization in Practice", section "The Meaning and Advantages of W4A4": in W4A16 the 4-bit
+ * weights are reconstructed to 16-bit floating point for the multiply, which mainly relieves
+ * memory-bound steps; "What is NVFP4?", section "What does W4A4 mean?"), FP32 accumulation,
+ * bf16 output:
+ *   Y[m, n] = RN_bf16( RN_fp32( gsW * sum_k A[m, k] * (cW * sbW)[n, k] ) ).
+ * No activation scale: A's bf16 values are used as they are.
+ *   a_bf16 : device bf16 m x k, row stride ld_a elements; 16-byte aligned, ld_a % 8 == 0.
+ *   w      : quantized weights, n = w->rows, w->cols == k, block_rows 1 or 16; codes 16-byte
+ *            aligned, ld_codes % 16 == 0.  k % 16 == 0.
+ *   y      : device bf16 m x n, row stride ld_y; 4-byte aligned, ld_y % 2 == 0.
+ * Decode shapes only: 1 <= m <= 16, else NVFP4_ERR_UNSUPPORTED (m == 0 returns NVFP4_OK).
+ * No workspace.  Accuracy: the bound of nvfp4_gemm_w4a4, Y64 being the exact product of the
+ * bf16 A and the dequantized W.
+ * ------------------------------------------------------------------------------------------- */
+nvfp4_status nvfp4_gemm_w4a16(const void *a_bf16, int64_t m, int64_t k, int64_t ld_a,
+                              const nvfp4_tensor *w, void *y, int64_t ld_y, void *stream);
+
+/* ---------------------------------------------------------------------------------------------
  * nvfp4_grouped_gemm_w4a4 — the mixture-of-experts form ("NVFP4 Dynamic Quantization in
  * Practice", section "The Practical Significance of Full Gemma-4 Quantization Coverage": tokens
  * are routed to a few experts while all experts stay resident).

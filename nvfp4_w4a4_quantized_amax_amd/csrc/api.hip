@@ -242,6 +242,26 @@ nvfp4_status nvfp4_gemm_w4a4(const void *a_bf16, int64_t m, int64_t k, int64_t l
   return hip_status(launch_gemm_tile(A, W, m, n, k, (uint16_t *)y, ld_y, st));
 }
 
+nvfp4_status nvfp4_gemm_w4a16(const void *a_bf16, int64_t m, int64_t k, int64_t ld_a,
+                              const nvfp4_tensor *w, void *y, int64_t ld_y, void *stream) {
+  if (!w) return NVFP4_ERR_NULL;
+  if (m < 0 || k <= 0 || k % 16) return NVFP4_ERR_SHAPE;
+  if (m == 0) return NVFP4_OK;
+  if (!a_bf16 || !y) return NVFP4_ERR_NULL;
+  const int64_t n = w->rows;
+  nvfp4_status s = check_tensor(w, n, k, true);
+  if (s) return s;
+  if (n < 1 || n >= ((int64_t)1 << 30)) return NVFP4_ERR_SHAPE;
+  if (ld_y < n) return NVFP4_ERR_SHAPE;
+  if (!aligned(y, 4) || ld_y % 2) return NVFP4_ERR_ALIGN;
+  s = check_bf16_input(a_bf16, m, k, ld_a);
+  if (s) return s;
+  if (m > kSmallM) return NVFP4_ERR_UNSUPPORTED;
+  GemmOperand W{w->codes, w->ld_codes, w->scales, w->ld_scales, w->global_scale, w->block_rows};
+  return hip_status(launch_gemm_w4a16(a_bf16, ld_a, W, m, n, k, (uint16_t *)y, ld_y,
+                                      (hipStream_t)stream));
+}
+
 nvfp4_status nvfp4_grouped_gemm_w4a4(const void *a_bf16, int64_t tokens, int64_t k,
                                      int64_t ld_a, const nvfp4_tensor *a_q,
                                      const int32_t *row_index, int64_t total_rows,

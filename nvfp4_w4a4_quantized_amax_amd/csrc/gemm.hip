@@ -1094,6 +1094,137 @@ __global__ __launch_bounds__(kDecWaves * 64) void k_gemm_decode(SmallMArgs p) {
 }
 
 // ---------------------------------------------------------------------------------------------
+// Weight-only W4A16 ("NVFP4 Dynamic Quantization in Practice", section "The Meaning and
+// Advantages of W4A4": the 4-bit weights are reconstructed to 16-bit floating point and multiplied
+// with 16-bit activations):  Y = RN_bf16(gsW * sum_k A[m, k] * (cW * sbW)[n, k]),  m <= 16.
+// The bf16 activations feed the bf16 MFMA unchanged; W is decoded exactly to bf16 (code * block
+// scale); gsW factors out of the sum.  Same lane <-> K mapping as the W4A4 decode kernels: lane
+// (row i16, group q) covers K values 128 * window + 32 * q + [0, 32) of its row, step kk the
+// eight at + 8 * kk.
+// ---------------------------------------------------------------------------------------------
+__device__ __forceinline__ bf16x8_t load_a_bf16x8(const uint16_t *row, int64_t k0, int64_t k,
+                                                  bool ok) {
+  // k % 16 == 0 and k0 % 8 == 0: the eight values are all in the row or all past its end.
+  const bf16x8_t z = {};
+  return ok && k0 < k ? *(const bf16x8_t *)(row + k0) : z;
+}
+
+// K <= 4096: the persistent decode form (one workgroup of 16 waves per CU walks the bands, each
+// wave holds its K slice of A in registers for the whole call, the next band's W is in flight).
+template <bool W2D>
+__global__ __launch_bounds__(kDecWaves * 64) void k_gemm_w4a16_decode(SmallMArgs p) {
+  __shared__ floatx4_t s_red[2][kDecWaves][kWave];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int i16 = lane & 15, q = lane >> 4;
+  const int64_t nwin = (p.k + 127) / 128;
+  const int64_t per = (nwin + kDecWaves - 1) / kDecWaves;  // <= kDecWin, checked by the launcher
+  const int64_t win0 = wave * per;
+  const int nw = (int)max((int64_t)0, min(per, nwin - win0));
+  const int64_t nbands = (p.n + 15) / 16;
+
+  DecodeW cur, nxt;
+  int64_t band = blockIdx.x;
+  if (band < nbands) load_decode_w<W2D>(p, band, i16, q, win0, nw, cur);
+
+  const bool a_ok = i16 < p.m;
+  const uint16_t *arow = p.a_bf16 + (a_ok ? i16 : 0) * p.ld_a;
+  bf16x8_t aop[kDecWin][4];
+#pragma unroll
+  for (int u = 0; u < kDecWin; ++u)
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+      aop[u][kk] = load_a_bf16x8(arow, (win0 + u) * 128 + q * 32 + kk * 8, p.k, a_ok && u < nw);
+
+  const float alpha = *p.w.gs;
+  for (int parity = 0; band < nbands; band += gridDim.x, parity ^= 1) {
+    const int64_t next = band + gridDim.x;
+    if (next < nbands) load_decode_w<W2D>(p, next, i16, q, win0, nw, nxt);
+    floatx4_t acc = floatx4_t{};
+#pragma unroll
+    for (int u = 0; u < kDecWin; ++u) {
+      if (u < nw) {
+        const floatx2_t sf = scales_f32x2(cur.s[u]);
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          const bf16x8_t wop = decode8_bf16(word(cur.v[u], kk), kk < 2 ? sf[0] : sf[1]);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wop, aop[u][kk], acc, 0, 0, 0);
+        }
+      }
+    }
+    s_red[parity][wave][lane] = acc;
+    __syncthreads();
+    if (wave < 4 && i16 < p.m) {
+      float t = 0.0f;
+#pragma unroll
+      for (int w2 = 0; w2 < kDecWaves; ++w2) t += s_red[parity][w2][lane][wave];
+      const int64_t n = band * 16 + 4 * q + wave;
+      if (n < p.n) ntstore_u16(p.y + (int64_t)i16 * p.ld_y + n, f32_to_bf16_rne(t * alpha));
+    }
+    cur = nxt;
+  }
+}
+
+// Any K: one workgroup of 16 waves per band; wave w takes windows w, w + 16, ..., loading W and
+// A for up to kW16Chunk of them at a time (A comes from L2: it is at most 16 rows).
+constexpr int kW16Chunk = 4;
+
+template <bool W2D>
+__global__ __launch_bounds__(kDecWaves * 64) void k_gemm_w4a16_stream(SmallMArgs p) {
+  __shared__ floatx4_t s_red[kDecWaves][kWave];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int i16 = lane & 15, q = lane >> 4;
+  const int64_t band = blockIdx.x;
+  const int64_t row = min(band * 16 + i16, p.n - 1);
+  const uint8_t *wrow = p.w.codes + row * p.w.ld_codes + q * 16;
+  const uint8_t *srow = p.w.scales + (W2D ? band : row) * p.w.ld_scales + q * 2;
+  const bool a_ok = i16 < p.m;
+  const uint16_t *arow = p.a_bf16 + (a_ok ? i16 : 0) * p.ld_a;
+  const int64_t nwin = (p.k + 127) / 128;
+  const int64_t kbytes = p.k / 2, kblocks = p.k / 16;
+  floatx4_t acc = floatx4_t{};
+  for (int64_t c0 = wave; c0 < nwin; c0 += kDecWaves * kW16Chunk) {
+    uint4 wv[kW16Chunk];
+    uint32_t ws_[kW16Chunk];
+    bf16x8_t av[kW16Chunk][4];
+#pragma unroll
+    for (int u = 0; u < kW16Chunk; ++u) {
+      const int64_t win = c0 + (int64_t)u * kDecWaves;
+      const bool in = win < nwin;
+      const int64_t rem = in ? kbytes - win * 64 - q * 16 : 0;
+      const int64_t remb = in ? kblocks - win * 8 - q * 2 : 0;
+      wv[u] = load16_masked(wrow + win * 64, rem);
+      uint32_t sv = 0;
+      if (p.scale_pairs && remb > 1)
+        sv = *(const uint16_t *)(srow + win * 8);
+      else
+        sv = (remb > 0 ? srow[win * 8] : 0u) | (remb > 1 ? (uint32_t)srow[win * 8 + 1] << 8 : 0u);
+      ws_[u] = sv;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+        av[u][kk] = load_a_bf16x8(arow, win * 128 + q * 32 + kk * 8, p.k, a_ok && in);
+    }
+#pragma unroll
+    for (int u = 0; u < kW16Chunk; ++u) {
+      const floatx2_t sf = scales_f32x2(ws_[u]);
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const bf16x8_t wop = decode8_bf16(word(wv[u], kk), kk < 2 ? sf[0] : sf[1]);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wop, av[u][kk], acc, 0, 0, 0);
+      }
+    }
+  }
+  s_red[wave][lane] = acc;
+  __syncthreads();
+  if (wave < 4 && i16 < p.m) {
+    float t = 0.0f;
+#pragma unroll
+    for (int w2 = 0; w2 < kDecWaves; ++w2) t += s_red[w2][lane][wave];
+    const int64_t n = band * 16 + 4 * q + wave;
+    if (n < p.n) ntstore_u16(p.y + (int64_t)i16 * p.ld_y + n, f32_to_bf16_rne(t * (*p.w.gs)));
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
 // Host launchers
 // ---------------------------------------------------------------------------------------------
 template <int FM, int FN>
@@ -1183,6 +1314,45 @@ hipError_t launch_gemm_decode_fused(const void *a_bf16, int64_t ld_a, const Gemm
   p.aq_scales = (uint8_t *)aq.scales;
   p.aq_gs = (float *)aq.gs;
   return launch_decode(p, w.block_rows == 16, true, stream);
+}
+
+hipError_t launch_gemm_w4a16(const void *a_bf16, int64_t ld_a, const GemmOperand &w, int64_t m,
+                             int64_t n, int64_t k, uint16_t *y, int64_t ld_y, hipStream_t stream) {
+  if (m < 1 || m > 16) return hipErrorNotSupported;
+  SmallMArgs p;
+  p.a = GemmOperand{nullptr, 0, nullptr, 0, nullptr, 1};
+  p.w = w;
+  p.m = m;
+  p.n = n;
+  p.k = k;
+  p.y = y;
+  p.ld_y = ld_y;
+  p.scale_pairs = ((uintptr_t)w.scales % 2 == 0) && (w.ld_scales % 2 == 0);
+  p.a_bf16 = (const uint16_t *)a_bf16;
+  p.ld_a = ld_a;
+  p.aq_codes = p.aq_scales = nullptr;
+  p.aq_gs = nullptr;
+  const bool w2d = w.block_rows == 16;
+  if ((k + 127) / 128 <= kDecWaves * kDecWin) {
+    static int cus = 0;
+    if (cus == 0 && hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, 0) != hipSuccess)
+      cus = 0;
+    const int64_t nbands = (n + 15) / 16;
+    const int64_t slots = cus > 0 ? cus : 256;
+    const int64_t per_wg = (nbands + slots - 1) / slots;
+    const unsigned grid = (unsigned)((nbands + per_wg - 1) / per_wg);
+    if (w2d)
+      hipLaunchKernelGGL(k_gemm_w4a16_decode<true>, dim3(grid), dim3(kDecWaves * 64), 0, stream, p);
+    else
+      hipLaunchKernelGGL(k_gemm_w4a16_decode<false>, dim3(grid), dim3(kDecWaves * 64), 0, stream, p);
+    return hipGetLastError();
+  }
+  const unsigned grid = (unsigned)((n + 15) / 16);
+  if (w2d)
+    hipLaunchKernelGGL(k_gemm_w4a16_stream<true>, dim3(grid), dim3(kDecWaves * 64), 0, stream, p);
+  else
+    hipLaunchKernelGGL(k_gemm_w4a16_stream<false>, dim3(grid), dim3(kDecWaves * 64), 0, stream, p);
+  return hipGetLastError();
 }
 
 hipError_t launch_gemm_small_m(const GemmOperand &a, const GemmOperand &w, int64_t m, int64_t n,

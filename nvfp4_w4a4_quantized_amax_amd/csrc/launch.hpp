@@ -52,6 +52,10 @@ hipError_t launch_gemm_decode_fused(const void *a_bf16, int64_t ld_a, const Gemm
 // Small M (m <= 16, decode-shaped): W streamed at full width, A decoded in registers.
 hipError_t launch_gemm_small_m(const GemmOperand &a, const GemmOperand &w, int64_t m, int64_t n,
                                int64_t k, uint16_t *y, int64_t ld_y, hipStream_t stream);
+// Weight-only product (bf16 A, NVFP4 W, 1 <= m <= 16); hipErrorNotSupported (nothing launched)
+// for other m.
+hipError_t launch_gemm_w4a16(const void *a_bf16, int64_t ld_a, const GemmOperand &w, int64_t m,
+                             int64_t n, int64_t k, uint16_t *y, int64_t ld_y, hipStream_t stream);
 hipError_t launch_grouped_gemm(const GemmOperand &a, const int32_t *row_index,
                                const int32_t *offsets, int32_t num_groups, const GemmOperand &w,
                                int64_t w_group_rows, int64_t n, int64_t k, int64_t total_rows,

@@ -14,6 +14,8 @@ typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef float floatx4_t __attribute__((ext_vector_type(4)));
 typedef float floatx16_t __attribute__((ext_vector_type(16)));
+typedef float floatx2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 
 constexpr int kWave = 64;
 constexpr int kE4M3MaxCode = 0x7E;  // 448
@@ -384,6 +386,24 @@ __device__ __forceinline__ half8_t decode8_f16(uint32_t q, half2_t s2) {
   h3 *= s2;
   half8_t r = {h0[0], h0[1], h1[0], h1[1], h2[0], h2[1], h3[0], h3[1]};
   return r;
+}
+
+// Same decode into bf16, for products with bf16 operands (weight-only W4A16).  gfx950 has no
+// packed bf16 multiply, so the FP4 values are converted to fp32, scaled there and packed to
+// bf16; every step is exact for the same reason as above.
+__device__ __forceinline__ bf16x8_t decode8_bf16(uint32_t q, float s) {
+  const floatx2_t f0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, 1.0f, 0);
+  const floatx2_t f1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, 1.0f, 1);
+  const floatx2_t f2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, 1.0f, 2);
+  const floatx2_t f3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, 1.0f, 3);
+  bf16x8_t r = {(__bf16)(f0[0] * s), (__bf16)(f0[1] * s), (__bf16)(f1[0] * s), (__bf16)(f1[1] * s),
+                (__bf16)(f2[0] * s), (__bf16)(f2[1] * s), (__bf16)(f3[0] * s), (__bf16)(f3[1] * s)};
+  return r;
+}
+
+// Two E4M3 scale bytes (low byte first) -> two floats, exact.
+__device__ __forceinline__ floatx2_t scales_f32x2(uint32_t two_bytes) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(two_bytes, 1.0f, false);
 }
 
 __device__ __forceinline__ half2_t scale_f16x2(uint32_t b) {

@@ -26,6 +26,7 @@ EXPORTED = (
     "nvfp4_status_string", "nvfp4_version", "nvfp4_quantize_workspace_bytes",
     "nvfp4_gemm_workspace_bytes", "nvfp4_grouped_gemm_workspace_bytes", "nvfp4_quantize_1d",
     "nvfp4_quantize_2d", "nvfp4_dequantize", "nvfp4_gemm_w4a4", "nvfp4_grouped_gemm_w4a4",
+    "nvfp4_gemm_w4a16",
 )
 
 
@@ -57,6 +58,8 @@ _lib.nvfp4_dequantize.restype = ctypes.c_int
 _lib.nvfp4_dequantize.argtypes = [_pt, _vp, _i64, ctypes.c_int, _vp]
 _lib.nvfp4_gemm_w4a4.restype = ctypes.c_int
 _lib.nvfp4_gemm_w4a4.argtypes = [_vp, _i64, _i64, _i64, _pt, _pt, _vp, _i64, _vp, _sz, _vp]
+_lib.nvfp4_gemm_w4a16.restype = ctypes.c_int
+_lib.nvfp4_gemm_w4a16.argtypes = [_vp, _i64, _i64, _i64, _pt, _vp, _i64, _vp]
 _lib.nvfp4_grouped_gemm_w4a4.restype = ctypes.c_int
 _lib.nvfp4_grouped_gemm_w4a4.argtypes = [_vp, _i64, _i64, _i64, _pt, _vp, _i64, _vp, _i32, _pt,
                                          _i64, _vp, _i64, _vp, _sz, _vp]
@@ -200,6 +203,20 @@ def gemm_w4a4(a, w, y=None, a_q=None, ws=None):
                                 ctypes.byref(ac) if ac is not None else None, ctypes.byref(wc),
                                 _ptr(y), y.stride(0), _ptr(ws), ws.numel(), _stream(dev)),
            "nvfp4_gemm_w4a4")
+    return y
+
+
+def gemm_w4a16(a, w, y=None):
+    """Weight-only Y = A . W^T (bf16 out): `a` is a bf16 matrix of at most 16 rows, used as is;
+    `w` a quantized weight."""
+    assert a.dtype == torch.bfloat16 and a.dim() == 2 and a.stride(1) == 1
+    m, k = a.shape
+    n = w.rows
+    if y is None:
+        y = torch.empty((m, n), dtype=torch.bfloat16, device=a.device)
+    wc = w.c()
+    _check(_lib.nvfp4_gemm_w4a16(_ptr(a), m, k, a.stride(0), ctypes.byref(wc), _ptr(y),
+                                 y.stride(0), _stream(a.device)), "nvfp4_gemm_w4a16")
     return y
 
 

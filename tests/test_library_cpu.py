@@ -117,6 +117,29 @@ def test_gemm_validation():
     assert gemm(FAKE + 8, 64, 256, 256, None, w) == nv.ERR_ALIGN
 
 
+def w4a16(a, m, k, w, ld_a=None, y=FAKE, ld_y=None):
+    return L.nvfp4_gemm_w4a16(a, m, k, k if ld_a is None else ld_a,
+                              ctypes.byref(w) if w is not None else None, y,
+                              (w.rows if w is not None else 0) if ld_y is None else ld_y, None)
+
+
+def test_w4a16_validation():
+    w = qt(128, 256, 16)
+    assert w4a16(FAKE, 8, 256, None) == nv.ERR_NULL
+    assert w4a16(None, 8, 256, w) == nv.ERR_NULL
+    assert w4a16(FAKE, 8, 256, w, y=None) == nv.ERR_NULL
+    assert w4a16(FAKE, 8, 240, w) == nv.ERR_SHAPE                 # K mismatch
+    assert w4a16(FAKE, 8, 250, qt(128, 250, 1)) == nv.ERR_SHAPE   # K % 16
+    assert w4a16(FAKE, 8, 256, w, ld_y=100) == nv.ERR_SHAPE
+    assert w4a16(FAKE, 8, 256, w, ld_a=100) == nv.ERR_SHAPE        # ld_a < k
+    assert w4a16(FAKE, 8, 256, w, y=FAKE + 2) == nv.ERR_ALIGN
+    assert w4a16(FAKE + 8, 8, 256, w) == nv.ERR_ALIGN              # A not 16-byte aligned
+    assert w4a16(FAKE, 8, 256, w, ld_a=260) == nv.ERR_ALIGN        # ld_a % 8
+    assert w4a16(FAKE, 17, 256, w) == nv.ERR_UNSUPPORTED           # decode shapes only
+    assert w4a16(FAKE, -1, 256, w) == nv.ERR_SHAPE
+    assert w4a16(None, 0, 256, w, y=None) == nv.OK                 # empty: nothing to do
+
+
 def grouped(a, tokens, k, aq, ri, total, off, g, w, n, y=FAKE, ws=FAKE, wsb=1 << 40):
     return L.nvfp4_grouped_gemm_w4a4(a, tokens, k, k, ctypes.byref(aq) if aq else None, ri,
                                      total, off, g, ctypes.byref(w), n, y, n, ws, wsb, None)

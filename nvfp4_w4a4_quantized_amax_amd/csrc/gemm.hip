@@ -242,6 +242,7 @@ struct LdsStage {
 // One thread's share of a window: chunk c = i * 256 + tid of A and of W (row c / 2, 16-byte
 // half c % 2), and the 4 scale bytes of A row tid and of W row tid (1D) or band tid % 16 (2D).
 typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint32_t word(const u32x4_t &v, int i) { return v[i]; }
 struct WindowRegs {
   u32x4_t a0, a1, w0, w1;
   uint32_t as, ws;
@@ -905,49 +906,151 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_small_m(SmallMArgs p) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// Decode-shaped kernel (m <= 16, K <= 4096): one workgroup of 16 waves per CU walks the 16-row
-// bands of W.  Wave w owns the w-th sixteenth of K for every band: it decodes its slice of A
-// (all m rows) to fp16 once and keeps it in registers, so the loop only streams W, with the
-// next band's W always in flight (its loads are issued before the current band is multiplied,
-// and the first band's before A is decoded).  The sixteen partial sums of a band meet in LDS.
+// Decode-shaped kernels (m <= 16, K <= 4096): one workgroup of 16 waves per CU walks the 16-row
+// bands of W (bands b, b + G, b + 2G, ... for a grid of G).  Wave w owns the w-th sixteenth of K
+// for every band and keeps its slice of A, ready for the MFMA, in registers for the whole call,
+// so the loop only streams W.  dec_depth(WIN) bands of W are in flight per workgroup: a band's
+// registers are refilled with the band dec_depth(WIN) steps ahead as soon as they have been
+// multiplied.  The sixteen partial sums of a band meet in LDS.
+//
+// FULL (K a multiple of 128, scale rows 2-byte aligned with even strides, W's codes and scales
+// each under 2 GiB): W is read with buffer loads whose offsets are unsigned 32-bit; windows past
+// a wave's share and bands past the last one get an offset beyond the buffer's size, which the
+// hardware answers with zeros and no memory access.  No load then sits under control flow, the
+// band loop refills its ring unconditionally, and each load stays in flight until its data is
+// used.  Other shapes take masked loads from clamped addresses.
 // ---------------------------------------------------------------------------------------------
 constexpr int kDecWaves = 16;
-constexpr int kDecWin = 2;  // 128-wide K windows per wave (K <= 16 * 2 * 128)
+constexpr int kDecWin = 2;  // 128-wide K windows per wave at most (K <= 16 * 2 * 128)
+// Bands of W in flight per workgroup: as many as the 128 registers of a 16-wave workgroup hold.
+constexpr int dec_depth(int win) { return win == 1 ? 4 : 3; }
+constexpr uint32_t kBufOutOfRange = 0x80000000u;  // above every buffer size used here
 
+template <int WIN>
 struct DecodeW {
-  uint4 v[kDecWin];
-  uint32_t s[kDecWin];  // two scale bytes per window (the lane's two 16-value blocks)
+  u32x4_t v[WIN];
+  // Two scale bytes per window (the lane's two 16-value blocks), kept 16-bit so that no
+  // widening of a loaded value is placed ahead of its use.
+  uint16_t s[WIN];
 };
 
-template <bool W2D>
-__device__ __forceinline__ void load_decode_w(const SmallMArgs &p, int64_t band, int i16, int q,
-                                              int64_t win0, int nw, DecodeW &r) {
+// Buffer resources over W's codes and scales (raw, byte-addressed, sized to the data).
+struct WBufs {
+  __amdgpu_buffer_rsrc_t codes, scales;
+};
+
+__device__ __forceinline__ WBufs make_wbufs(const SmallMArgs &p) {
+  const int64_t srows = p.w.block_rows == 16 ? (p.n + 15) / 16 : p.n;
+  const int32_t cbytes = (int32_t)((p.n - 1) * p.w.ld_codes + p.k / 2);
+  const int32_t sbytes = (int32_t)((srows - 1) * p.w.ld_scales + p.k / 16);
+  WBufs b;
+  b.codes = __builtin_amdgcn_make_buffer_rsrc((void *)p.w.codes, 0, cbytes, 0x00020000);
+  b.scales = __builtin_amdgcn_make_buffer_rsrc((void *)p.w.scales, 0, sbytes, 0x00020000);
+  return b;
+}
+
+template <bool W2D, bool FULL, int WIN>
+__device__ __forceinline__ void load_decode_w(const SmallMArgs &p, const WBufs &buf, int64_t band,
+                                              int64_t nbands, int i16, int q, int64_t win0,
+                                              int nw, DecodeW<WIN> &r) {
+  if (FULL) {
+    const bool valid = band < nbands;
+    const int64_t row = min(band * 16 + i16, p.n - 1);
+    const uint32_t cb = (uint32_t)(row * p.w.ld_codes) + q * 16;
+    const uint32_t sb = (uint32_t)((W2D ? band : row) * p.w.ld_scales) + q * 2;
+#pragma unroll
+    for (int u = 0; u < WIN; ++u) {
+      const bool in = valid && u < nw;
+      const uint32_t co = in ? cb + (uint32_t)(win0 + u) * 64 : kBufOutOfRange;
+      const uint32_t so = in ? sb + (uint32_t)(win0 + u) * 8 : kBufOutOfRange;
+      r.v[u] = __builtin_amdgcn_raw_buffer_load_b128(buf.codes, (int)co, 0, 0);
+      r.s[u] = __builtin_amdgcn_raw_buffer_load_b16(buf.scales, (int)so, 0, 0);
+    }
+    return;
+  }
+  band = min(band, nbands - 1);  // past the last band: a valid address, never used
   const int64_t row = min(band * 16 + i16, p.n - 1);
   const uint8_t *wrow = p.w.codes + row * p.w.ld_codes + q * 16;
   const uint8_t *srow = p.w.scales + (W2D ? band : row) * p.w.ld_scales + q * 2;
   const int64_t kbytes = p.k / 2, kblocks = p.k / 16;
 #pragma unroll
-  for (int u = 0; u < kDecWin; ++u) {
+  for (int u = 0; u < WIN; ++u) {
     const int64_t win = win0 + u;
     const bool in = u < nw;
     const int64_t rem = in ? kbytes - win * 64 - q * 16 : 0;
     const int64_t remb = in ? kblocks - win * 8 - q * 2 : 0;
-    r.v[u] = load16_masked(wrow + win * 64, rem);
+    const uint4 v = load16_masked(wrow + win * 64, rem);
+    r.v[u] = u32x4_t{v.x, v.y, v.z, v.w};
     uint32_t sv = 0;
     if (p.scale_pairs && remb > 1) {
       sv = *(const uint16_t *)(srow + win * 8);
     } else {
       sv = (remb > 0 ? srow[win * 8] : 0u) | (remb > 1 ? (uint32_t)srow[win * 8 + 1] << 8 : 0u);
     }
-    r.s[u] = sv;
+    r.s[u] = (uint16_t)sv;
   }
 }
 
-// FUSED: A arrives as bf16 and every workgroup quantizes it itself (amax over all of A, the
-// FP32 global scale and the scale tables, then its waves encode their own K slices), exactly as
-// nvfp4_quantize_1d would; workgroup 0 also writes the quantized A when asked to.  A is at most
-// 16 rows, so the redundant work is small and no workgroup waits for another.
-template <bool W2D, bool FUSED>
+// Issues the loads of the workgroup's first dec_depth(WIN) bands.
+template <bool W2D, bool FULL, int WIN>
+__device__ __forceinline__ void decode_ring_start(const SmallMArgs &p, const WBufs &buf,
+                                                  int64_t nbands, int i16, int q, int64_t win0,
+                                                  int nw, DecodeW<WIN> (&ring)[dec_depth(WIN)]) {
+#pragma unroll
+  for (int j = 0; j < dec_depth(WIN); ++j)
+    load_decode_w<W2D, FULL, WIN>(p, buf, blockIdx.x + (int64_t)j * gridDim.x, nbands, i16, q,
+                                  win0, nw, ring[j]);
+}
+
+// The band loop: mul(ring slot) returns the wave's 16x16 partial product of that band; the slot
+// is refilled with the band dec_depth(WIN) steps ahead, the partials are summed through LDS (two
+// buffers alternate, so one barrier per band suffices) and waves 0..3 each finish one of the four
+// output rows a lane holds.  The main loop runs while all dec_depth(WIN) steps of a round are
+// real bands, so its refills need no condition; the last, partial round only drains the ring.
+template <bool W2D, bool FULL, int WIN, class Mul>
+__device__ __forceinline__ void decode_band_loop(const SmallMArgs &p, const WBufs &buf,
+                                                 int64_t nbands, int lane, int wave,
+                                                 int64_t win0, int nw, float alpha,
+                                                 DecodeW<WIN> (&ring)[dec_depth(WIN)],
+                                                 floatx4_t (*s_red)[kDecWaves][kWave], Mul mul) {
+  constexpr int D = dec_depth(WIN);
+  const int i16 = lane & 15, q = lane >> 4;
+  const int64_t g = gridDim.x;
+  int parity = 0;
+  auto finish = [&](const floatx4_t &acc, int64_t band) {
+    s_red[parity][wave][lane] = acc;
+    __syncthreads();
+    if (wave < 4 && i16 < p.m) {
+      float t = 0.0f;
+#pragma unroll
+      for (int w2 = 0; w2 < kDecWaves; ++w2) t += s_red[parity][w2][lane][wave];
+      const int64_t n = band * 16 + 4 * q + wave;
+      if (n < p.n) ntstore_u16(p.y + (int64_t)i16 * p.ld_y + n, f32_to_bf16_rne(t * alpha));
+    }
+    parity ^= 1;
+  };
+  int64_t base = blockIdx.x;
+  for (; base + (D - 1) * g < nbands; base += D * g) {
+#pragma unroll
+    for (int j = 0; j < D; ++j) {
+      const int64_t band = base + j * g;
+      const floatx4_t acc = mul(ring[j]);
+      load_decode_w<W2D, FULL, WIN>(p, buf, band + D * g, nbands, i16, q, win0, nw, ring[j]);
+      finish(acc, band);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < D - 1; ++j) {
+    const int64_t band = base + j * g;
+    if (band < nbands) finish(mul(ring[j]), band);
+  }
+}
+
+// W4A4.  FUSED: A arrives as bf16 and every workgroup quantizes it itself (amax over all of A,
+// the FP32 global scale and the scale tables, then its waves encode their own K slices), exactly
+// as nvfp4_quantize_1d would; workgroup 0 also writes the quantized A when asked to.  A is at
+// most 16 rows, so the redundant work is small and no workgroup waits for another.
+template <bool W2D, bool FUSED, bool FULL, int WIN>
 __global__ __launch_bounds__(kDecWaves * 64) void k_gemm_decode(SmallMArgs p) {
   __shared__ floatx4_t s_red[2][kDecWaves][kWave];
   __shared__ QuantTables tab;
@@ -958,41 +1061,40 @@ __global__ __launch_bounds__(kDecWaves * 64) void k_gemm_decode(SmallMArgs p) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int i16 = lane & 15, q = lane >> 4;
   const int64_t nwin = (p.k + 127) / 128;
-  const int64_t per = (nwin + kDecWaves - 1) / kDecWaves;  // <= kDecWin, checked by the launcher
+  const int64_t per = (nwin + kDecWaves - 1) / kDecWaves;  // <= WIN, checked by the launcher
   const int64_t win0 = wave * per;
   const int nw = (int)max((int64_t)0, min(per, nwin - win0));
   const int64_t kbytes = p.k / 2, kblocks = p.k / 16;
   const int64_t nbands = (p.n + 15) / 16;
-
-  DecodeW cur, nxt;
-  int64_t band = blockIdx.x;
-  if (band < nbands) load_decode_w<W2D>(p, band, i16, q, win0, nw, cur);
+  const WBufs buf = make_wbufs(p);
+  // Read before any load of A or W is issued, so that waiting for it waits for nothing else.
+  const float gs_w = *p.w.gs, gs_a_in = FUSED ? 0.0f : *p.a.gs;
 
   // This wave's K slice of A, decoded once: window u, K step kk -> 8 fp16 values of A row i16.
-  half8_t aop[kDecWin][4];
+  half8_t aop[WIN][4];
   float gs_a = 0.0f;
+  DecodeW<WIN> ring[dec_depth(WIN)];
   if (FUSED) {
     // Each wave loads its own K slice of all m rows of A, coalesced: step j gives lane l the
-    // 16-value block j * 64 + l of the slice (row = block / bps, bps blocks per row).  Those
-    // registers give this workgroup's share of the global amax and are then encoded in place;
-    // the codes reach the MFMA layout through the wave's own corner of LDS.
-    const int64_t kb0 = win0 * 8;                             // first block of the slice
+    // 16-value block j * 64 + l of the slice (row = block / bps, bps blocks per row); lanes past
+    // the slice reload its last block (or A's first block when the slice is empty), which leaves
+    // the maximum unchanged.  These loads go out before W's, so waiting for them does not wait
+    // for W.  The registers give this workgroup's share of the global amax and are then encoded
+    // in place; the codes reach the MFMA layout through the wave's own corner of LDS.
+    const int64_t kb0 = win0 * 8;                                       // first block of the slice
     const int bps = (int)max((int64_t)0, min(per * 8, kblocks - kb0));  // blocks per row
-    const int nblk = (int)p.m * bps;                           // <= 16 * 16
+    const int nblk = (int)p.m * bps;                                    // <= 16 * 16
     uint4 xa[4][2];
-    uint32_t mx = 0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int blk = j * 64 + lane;
-      const uint4 z = make_uint4(0, 0, 0, 0);
-      xa[j][0] = xa[j][1] = z;
-      if (blk < nblk) {
-        const int r = blk / bps, c = blk - r * bps;
-        const uint16_t *src = p.a_bf16 + r * p.ld_a + (kb0 + c) * 16;
-        xa[j][0] = *(const uint4 *)src;
-        xa[j][1] = *(const uint4 *)(src + 8);
-      }
+      const int blk = min(j * 64 + lane, max(nblk - 1, 0));
+      const int r = bps > 0 ? blk / bps : 0, c = bps > 0 ? blk - r * bps : 0;
+      const uint16_t *src = p.a_bf16 + r * p.ld_a + (bps > 0 ? kb0 + c : 0) * 16;
+      xa[j][0] = *(const uint4 *)src;
+      xa[j][1] = *(const uint4 *)(src + 8);
     }
+    decode_ring_start<W2D, FULL, WIN>(p, buf, nbands, i16, q, win0, nw, ring);
+    uint32_t mx = 0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) mx = max(mx, absmax16(xa[j][0], xa[j][1]));
     mx = wave_max_u32(mx);
@@ -1028,7 +1130,7 @@ __global__ __launch_bounds__(kDecWaves * 64) void k_gemm_decode(SmallMArgs p) {
     // MFMA layout: lane (i16, q), window u holds blocks 8u + 2q and 8u + 2q + 1 of row i16.
     const bool a_ok = i16 < p.m;
 #pragma unroll
-    for (int u = 0; u < kDecWin; ++u) {
+    for (int u = 0; u < WIN; ++u) {
       const int c0 = u * 8 + q * 2;
       const bool v0 = a_ok && c0 < bps, v1 = a_ok && c0 + 1 < bps;
       const uint2 e0 = v0 ? *(const uint2 *)(lc + (i16 * 16 + c0) * 8) : make_uint2(0, 0);
@@ -1042,55 +1144,56 @@ __global__ __launch_bounds__(kDecWaves * 64) void k_gemm_decode(SmallMArgs p) {
         aop[u][kk] = decode8_f16(word(v, kk), kk < 2 ? splat_lo(sp) : splat_hi(sp));
     }
   } else {
-    const bool a_ok = i16 < p.m;
-    const uint8_t *arow = p.a.codes + (a_ok ? i16 : 0) * p.a.ld_codes + q * 16;
-    const uint8_t *asrow = p.a.scales + (a_ok ? i16 : 0) * p.a.ld_scales + q * 2;
+    // Rows past m read row m - 1 (their products land in columns that are not stored).
+    const int64_t ar = min((int64_t)i16, p.m - 1);
+    const uint8_t *arow = p.a.codes + ar * p.a.ld_codes + q * 16;
+    const uint8_t *asrow = p.a.scales + ar * p.a.ld_scales + q * 2;
+    uint4 av[WIN];
+    uint32_t as[WIN];
 #pragma unroll
-    for (int u = 0; u < kDecWin; ++u) {
-      const int64_t win = win0 + u;
-      const bool in = a_ok && u < nw;
-      const int64_t rem = in ? kbytes - win * 64 - q * 16 : 0;
-      const int64_t remb = in ? kblocks - win * 8 - q * 2 : 0;
-      const uint4 v = load16_masked(arow + win * 64, rem);
-      const uint32_t sv = (remb > 0 ? asrow[win * 8] : 0u) |
-                          (remb > 1 ? (uint32_t)asrow[win * 8 + 1] << 8 : 0u);
-      const half2_t sp = scales_f16x2(sv);
+    for (int u = 0; u < WIN; ++u) {
+      if (FULL) {
+        const int64_t win = min(win0 + u, nwin - 1);
+        av[u] = *(const uint4 *)(arow + win * 64);
+        as[u] = *(const uint16_t *)(asrow + win * 8);
+      } else {
+        const int64_t win = win0 + u;
+        const bool in = u < nw;
+        const int64_t rem = in ? kbytes - win * 64 - q * 16 : 0;
+        const int64_t remb = in ? kblocks - win * 8 - q * 2 : 0;
+        av[u] = load16_masked(arow + win * 64, rem);
+        as[u] = (remb > 0 ? asrow[win * 8] : 0u) |
+                (remb > 1 ? (uint32_t)asrow[win * 8 + 1] << 8 : 0u);
+      }
+    }
+    decode_ring_start<W2D, FULL, WIN>(p, buf, nbands, i16, q, win0, nw, ring);
+#pragma unroll
+    for (int u = 0; u < WIN; ++u) {
+      const half2_t sp = scales_f16x2(as[u]);
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk)
-        aop[u][kk] = decode8_f16(word(v, kk), kk < 2 ? splat_lo(sp) : splat_hi(sp));
+        aop[u][kk] = decode8_f16(word(av[u], kk), kk < 2 ? splat_lo(sp) : splat_hi(sp));
     }
   }
 
-  const float alpha = (FUSED ? gs_a : *p.a.gs) * (*p.w.gs);
-  for (int parity = 0; band < nbands; band += gridDim.x, parity ^= 1) {
-    const int64_t next = band + gridDim.x;
-    if (next < nbands) load_decode_w<W2D>(p, next, i16, q, win0, nw, nxt);
-    floatx4_t acc = floatx4_t{};
+  const float alpha = (FUSED ? gs_a : gs_a_in) * gs_w;
+  decode_band_loop<W2D, FULL, WIN>(
+      p, buf, nbands, lane, wave, win0, nw, alpha, ring, s_red, [&](const DecodeW<WIN> &w) {
+        floatx4_t acc = floatx4_t{};
 #pragma unroll
-    for (int u = 0; u < kDecWin; ++u) {
-      if (u < nw) {
-        const half2_t sp = scales_f16x2(cur.s[u]);
+        for (int u = 0; u < WIN; ++u) {
+          if (FULL || u < nw) {  // FULL: W of windows past the share is zero
+            const half2_t sp = scales_f16x2(w.s[u]);
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          const half8_t wop = decode8_f16(word(cur.v[u], kk), kk < 2 ? splat_lo(sp) : splat_hi(sp));
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(wop, aop[u][kk], acc, 0, 0, 0);
+            for (int kk = 0; kk < 4; ++kk) {
+              const half8_t wop =
+                  decode8_f16(word(w.v[u], kk), kk < 2 ? splat_lo(sp) : splat_hi(sp));
+              acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(wop, aop[u][kk], acc, 0, 0, 0);
+            }
+          }
         }
-      }
-    }
-    // Partial sums of the K slices; the buffer alternates with the band so one barrier per band
-    // suffices (a buffer is rewritten only after the next band's barrier).  Waves 0..3 each
-    // finish one of the four output rows a lane holds.
-    s_red[parity][wave][lane] = acc;
-    __syncthreads();
-    if (wave < 4 && i16 < p.m) {
-      float t = 0.0f;
-#pragma unroll
-      for (int w2 = 0; w2 < kDecWaves; ++w2) t += s_red[parity][w2][lane][wave];
-      const int64_t n = band * 16 + 4 * q + wave;
-      if (n < p.n) ntstore_u16(p.y + (int64_t)i16 * p.ld_y + n, f32_to_bf16_rne(t * alpha));
-    }
-    cur = nxt;
-  }
+        return acc;
+      });
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -1109,59 +1212,57 @@ __device__ __forceinline__ bf16x8_t load_a_bf16x8(const uint16_t *row, int64_t k
   return ok && k0 < k ? *(const bf16x8_t *)(row + k0) : z;
 }
 
-// K <= 4096: the persistent decode form (one workgroup of 16 waves per CU walks the bands, each
-// wave holds its K slice of A in registers for the whole call, the next band's W is in flight).
-template <bool W2D>
+// K <= 4096: the decode form above with bf16 A held in registers.
+template <bool W2D, bool FULL, int WIN>
 __global__ __launch_bounds__(kDecWaves * 64) void k_gemm_w4a16_decode(SmallMArgs p) {
   __shared__ floatx4_t s_red[2][kDecWaves][kWave];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int i16 = lane & 15, q = lane >> 4;
   const int64_t nwin = (p.k + 127) / 128;
-  const int64_t per = (nwin + kDecWaves - 1) / kDecWaves;  // <= kDecWin, checked by the launcher
+  const int64_t per = (nwin + kDecWaves - 1) / kDecWaves;  // <= WIN, checked by the launcher
   const int64_t win0 = wave * per;
   const int nw = (int)max((int64_t)0, min(per, nwin - win0));
   const int64_t nbands = (p.n + 15) / 16;
+  const WBufs buf = make_wbufs(p);
+  const float gs_w = *p.w.gs;  // read before the loads of A and W are issued
 
-  DecodeW cur, nxt;
-  int64_t band = blockIdx.x;
-  if (band < nbands) load_decode_w<W2D>(p, band, i16, q, win0, nw, cur);
-
-  const bool a_ok = i16 < p.m;
-  const uint16_t *arow = p.a_bf16 + (a_ok ? i16 : 0) * p.ld_a;
-  bf16x8_t aop[kDecWin][4];
+  bf16x8_t aop[WIN][4];
+  if (FULL) {
+    // Rows past m read row m - 1, windows past the share the last window: never used.
+    const uint16_t *arow = p.a_bf16 + min((int64_t)i16, p.m - 1) * p.ld_a;
 #pragma unroll
-  for (int u = 0; u < kDecWin; ++u)
+    for (int u = 0; u < WIN; ++u)
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
-      aop[u][kk] = load_a_bf16x8(arow, (win0 + u) * 128 + q * 32 + kk * 8, p.k, a_ok && u < nw);
-
-  const float alpha = *p.w.gs;
-  for (int parity = 0; band < nbands; band += gridDim.x, parity ^= 1) {
-    const int64_t next = band + gridDim.x;
-    if (next < nbands) load_decode_w<W2D>(p, next, i16, q, win0, nw, nxt);
-    floatx4_t acc = floatx4_t{};
+      for (int kk = 0; kk < 4; ++kk)
+        aop[u][kk] = *(const bf16x8_t *)(arow + min(win0 + u, nwin - 1) * 128 + q * 32 + kk * 8);
+  } else {
+    const bool a_ok = i16 < p.m;
+    const uint16_t *arow = p.a_bf16 + (a_ok ? i16 : 0) * p.ld_a;
 #pragma unroll
-    for (int u = 0; u < kDecWin; ++u) {
-      if (u < nw) {
-        const floatx2_t sf = scales_f32x2(cur.s[u]);
+    for (int u = 0; u < WIN; ++u)
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          const bf16x8_t wop = decode8_bf16(word(cur.v[u], kk), kk < 2 ? sf[0] : sf[1]);
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wop, aop[u][kk], acc, 0, 0, 0);
-        }
-      }
-    }
-    s_red[parity][wave][lane] = acc;
-    __syncthreads();
-    if (wave < 4 && i16 < p.m) {
-      float t = 0.0f;
-#pragma unroll
-      for (int w2 = 0; w2 < kDecWaves; ++w2) t += s_red[parity][w2][lane][wave];
-      const int64_t n = band * 16 + 4 * q + wave;
-      if (n < p.n) ntstore_u16(p.y + (int64_t)i16 * p.ld_y + n, f32_to_bf16_rne(t * alpha));
-    }
-    cur = nxt;
+      for (int kk = 0; kk < 4; ++kk)
+        aop[u][kk] = load_a_bf16x8(arow, (win0 + u) * 128 + q * 32 + kk * 8, p.k, a_ok && u < nw);
   }
+  DecodeW<WIN> ring[dec_depth(WIN)];
+  decode_ring_start<W2D, FULL, WIN>(p, buf, nbands, i16, q, win0, nw, ring);
+
+  decode_band_loop<W2D, FULL, WIN>(
+      p, buf, nbands, lane, wave, win0, nw, gs_w, ring, s_red, [&](const DecodeW<WIN> &w) {
+        floatx4_t acc = floatx4_t{};
+#pragma unroll
+        for (int u = 0; u < WIN; ++u) {
+          if (FULL || u < nw) {  // FULL: W of windows past the share is zero
+            const floatx2_t sf = scales_f32x2(w.s[u]);
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+              const bf16x8_t wop = decode8_bf16(word(w.v[u], kk), kk < 2 ? sf[0] : sf[1]);
+              acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wop, aop[u][kk], acc, 0, 0, 0);
+            }
+          }
+        }
+        return acc;
+      });
 }
 
 // Any K: one workgroup of 16 waves per band; wave w takes windows w, w + 16, ..., loading W and
@@ -1279,20 +1380,52 @@ hipError_t launch_gemm_tile(const GemmOperand &a, const GemmOperand &w, int64_t 
 }
 
 // One workgroup per CU, each taking the same number of 16-row bands.
-static hipError_t launch_decode(const SmallMArgs &p, bool w2d, bool fused, hipStream_t stream) {
+static unsigned decode_grid(int64_t n) {
   static int cus = 0;
   if (cus == 0 && hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, 0) != hipSuccess)
     cus = 0;
-  const int64_t nbands = (p.n + 15) / 16;
+  const int64_t nbands = (n + 15) / 16;
   const int64_t slots = cus > 0 ? cus : 256;
   const int64_t per_wg = (nbands + slots - 1) / slots;
-  const unsigned grid = (unsigned)((nbands + per_wg - 1) / per_wg);
-  const dim3 block(kDecWaves * 64);
-  if (w2d && fused) hipLaunchKernelGGL((k_gemm_decode<true, true>), dim3(grid), block, 0, stream, p);
-  if (w2d && !fused) hipLaunchKernelGGL((k_gemm_decode<true, false>), dim3(grid), block, 0, stream, p);
-  if (!w2d && fused) hipLaunchKernelGGL((k_gemm_decode<false, true>), dim3(grid), block, 0, stream, p);
-  if (!w2d && !fused) hipLaunchKernelGGL((k_gemm_decode<false, false>), dim3(grid), block, 0, stream, p);
+  return (unsigned)((nbands + per_wg - 1) / per_wg);
+}
+
+// Full windows: K a multiple of 128, 16-bit scale-pair loads allowed, W's codes and scales each
+// addressable with 31-bit buffer offsets.
+static bool decode_full(const SmallMArgs &p) {
+  const int64_t srows = p.w.block_rows == 16 ? (p.n + 15) / 16 : p.n;
+  const int64_t lim = (int64_t)1 << 31;
+  return p.k % 128 == 0 && p.scale_pairs && (p.n - 1) * p.w.ld_codes + p.k / 2 < lim &&
+         (srows - 1) * p.w.ld_scales + p.k / 16 < lim;
+}
+
+template <bool FUSED, bool FULL, int WIN>
+static void launch_decode_t(const SmallMArgs &p, bool w2d, hipStream_t stream) {
+  const dim3 grid(decode_grid(p.n)), block(kDecWaves * 64);
+  if (w2d)
+    hipLaunchKernelGGL((k_gemm_decode<true, FUSED, FULL, WIN>), grid, block, 0, stream, p);
+  else
+    hipLaunchKernelGGL((k_gemm_decode<false, FUSED, FULL, WIN>), grid, block, 0, stream, p);
+}
+
+template <bool FUSED>
+static hipError_t launch_decode(const SmallMArgs &p, bool w2d, hipStream_t stream) {
+  const bool full = decode_full(p);
+  const bool one = (p.k + 127) / 128 <= kDecWaves;  // one window per wave
+  if (full && one) launch_decode_t<FUSED, true, 1>(p, w2d, stream);
+  if (full && !one) launch_decode_t<FUSED, true, 2>(p, w2d, stream);
+  if (!full && one) launch_decode_t<FUSED, false, 1>(p, w2d, stream);
+  if (!full && !one) launch_decode_t<FUSED, false, 2>(p, w2d, stream);
   return hipGetLastError();
+}
+
+template <bool FULL, int WIN>
+static void launch_w4a16_t(const SmallMArgs &p, bool w2d, hipStream_t stream) {
+  const dim3 grid(decode_grid(p.n)), block(kDecWaves * 64);
+  if (w2d)
+    hipLaunchKernelGGL((k_gemm_w4a16_decode<true, FULL, WIN>), grid, block, 0, stream, p);
+  else
+    hipLaunchKernelGGL((k_gemm_w4a16_decode<false, FULL, WIN>), grid, block, 0, stream, p);
 }
 
 hipError_t launch_gemm_decode_fused(const void *a_bf16, int64_t ld_a, const GemmOperand &aq,
@@ -1313,7 +1446,7 @@ hipError_t launch_gemm_decode_fused(const void *a_bf16, int64_t ld_a, const Gemm
   p.aq_codes = (uint8_t *)aq.codes;
   p.aq_scales = (uint8_t *)aq.scales;
   p.aq_gs = (float *)aq.gs;
-  return launch_decode(p, w.block_rows == 16, true, stream);
+  return launch_decode<true>(p, w.block_rows == 16, stream);
 }
 
 hipError_t launch_gemm_w4a16(const void *a_bf16, int64_t ld_a, const GemmOperand &w, int64_t m,
@@ -1334,17 +1467,12 @@ hipError_t launch_gemm_w4a16(const void *a_bf16, int64_t ld_a, const GemmOperand
   p.aq_gs = nullptr;
   const bool w2d = w.block_rows == 16;
   if ((k + 127) / 128 <= kDecWaves * kDecWin) {
-    static int cus = 0;
-    if (cus == 0 && hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, 0) != hipSuccess)
-      cus = 0;
-    const int64_t nbands = (n + 15) / 16;
-    const int64_t slots = cus > 0 ? cus : 256;
-    const int64_t per_wg = (nbands + slots - 1) / slots;
-    const unsigned grid = (unsigned)((nbands + per_wg - 1) / per_wg);
-    if (w2d)
-      hipLaunchKernelGGL(k_gemm_w4a16_decode<true>, dim3(grid), dim3(kDecWaves * 64), 0, stream, p);
-    else
-      hipLaunchKernelGGL(k_gemm_w4a16_decode<false>, dim3(grid), dim3(kDecWaves * 64), 0, stream, p);
+    const bool full = decode_full(p);
+    const bool one = (k + 127) / 128 <= kDecWaves;
+    if (full && one) launch_w4a16_t<true, 1>(p, w2d, stream);
+    if (full && !one) launch_w4a16_t<true, 2>(p, w2d, stream);
+    if (!full && one) launch_w4a16_t<false, 1>(p, w2d, stream);
+    if (!full && !one) launch_w4a16_t<false, 2>(p, w2d, stream);
     return hipGetLastError();
   }
   const unsigned grid = (unsigned)((n + 15) / 16);
@@ -1373,7 +1501,7 @@ hipError_t launch_gemm_small_m(const GemmOperand &a, const GemmOperand &w, int64
     p.ld_a = 0;
     p.aq_codes = p.aq_scales = nullptr;
     p.aq_gs = nullptr;
-    return launch_decode(p, w.block_rows == 16, false, stream);
+    return launch_decode<false>(p, w.block_rows == 16, stream);
   }
   const unsigned grid = (unsigned)nbands;
   if (w.block_rows == 16)

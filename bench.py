@@ -91,7 +91,7 @@ def headline(args, torch, np, nv, W):
 
 TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
                             "k_quantize_persistent_activation_8192x8192_traffic.md")
-QUANTIZE_SOURCES = ("quantize.hip", "nvfp4_device.hpp", "api.hip")
+QUANTIZE_SOURCES = ("quantize.hip", "nvfp4_device.hpp")
 
 
 def quantize_source_hash():

@@ -28,6 +28,7 @@ import time
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 FP16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 MFMA, TFLOP/s
+FP4_MFMA_PEAK_TFLOPS = 10100.0  # MI355X dense fp4 (and fp6) MFMA, TFLOP/s
 METRIC = "W4A4 GEMM TFLOP/s + NVFP4 quantize GB/s, as % of MI355X roofline"
 
 
@@ -171,6 +172,36 @@ def extra_workloads(args, torch, np, nv, W, only):
                           "unit": "TFLOP/s", "peak": FP16_MFMA_PEAK_TFLOPS,
                           "frac": tf / FP16_MFMA_PEAK_TFLOPS,
                           "note": "includes the dynamic quantization of A inside the call"}
+        del a, wq, y
+
+    if not only or "mxfp4" in only:
+        # MXFP4 (E8M0 per 32 values): the headline activation quantized in one pass, and the
+        # prefill product with both operands MXFP4 on the scaled FP4 MFMA.
+        x = W.activation()["x"]
+        xs = [dev_bf16(torch, np, x)] + [None] * 3
+        for i in range(1, 4):
+            xs[i] = xs[0].clone()
+        qs = [nv.empty_mxtensor(8192, 8192) for _ in range(4)]
+        ms = timed(lambda i: nv.mxfp4_quantize(xs[i % 4], out=qs[i % 4]), steps, warm, torch)
+        nbytes = 8192 * 8192 * 2 + 8192 * 8192 // 2 + 8192 * 8192 // 32
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        out["mxfp4_quantize"] = {"shape": [8192, 8192], "ms": ms, "bound": "hbm",
+                                 "achieved": gbs, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                                 "algorithmic_bytes": nbytes}
+        del xs, qs
+        d = W.prefill()
+        a = dev_bf16(torch, np, d["a"])
+        wq = nv.mxfp4_quantize(dev_bf16(torch, np, d["w"]))
+        m = n = k = 8192
+        y = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+        ws = nv.Workspace.get(nv.lib().nvfp4_mxfp4_gemm_workspace_bytes(m, k), a.device)
+        ps = max(5, steps // 5)
+        ms = timed(lambda i: nv.mxfp4_gemm(a, wq, y=y, ws=ws), ps, warm, torch)
+        tf = 2 * m * n * k / (ms * 1e-3) / 1e12
+        out["mxfp4_prefill"] = {"shape": [m, n, k], "ms": ms, "bound": "mfma", "achieved": tf,
+                                "unit": "TFLOP/s", "peak": FP4_MFMA_PEAK_TFLOPS,
+                                "frac": tf / FP4_MFMA_PEAK_TFLOPS,
+                                "note": "includes the MXFP4 quantization of A inside the call"}
         del a, wq, y
 
     if not only or "moe" in only:

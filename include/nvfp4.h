@@ -195,6 +195,62 @@ nvfp4_status nvfp4_grouped_gemm_w4a4(const void *a_bf16, int64_t tokens, int64_t
                                      const nvfp4_tensor *w, int64_t n, void *y, int64_t ld_y,
                                      void *ws, size_t ws_bytes, void *stream);
 
+/* =============================================================================================
+ * MXFP4, the variant the pages contrast with NVFP4 ("What is NVFP4?", section "NVFP4 versus
+ * MXFP4"; "NVFP4 Explained", section "Why the Block Scale Uses FP8 E4M3" and FAQ "What is the
+ * difference between NVFP4 and MXFP4?"): the same E2M1 elements, one E8M0 power-of-two scale
+ * per 32 consecutive values, no tensor scale.
+ * Readings (identical in the library and the oracle):
+ *  - block scale X = 2^e, e = floor(log2(bamax)) - 2 clamped to [-127, 127] (the conversion rule
+ *    of the MX specification), -127 for an all-zero block; stored byte e + 127;
+ *  - element code = nearest E2M1 value to x / X, ties to the even code, saturating at 6,
+ *    sign bit = signbit(x); packing as NVFP4 (element 2j in the low nibble);
+ *  - scales row-major, rows x cols/32 bytes.
+ * Codes and scales are bit-exact for finite inputs.
+ * ========================================================================================== */
+
+/* One MXFP4 matrix of rows x cols (cols % 32 == 0), cols contiguous; device pointers.
+ *   codes  : packed E2M1 codes, row r at codes + r * ld_codes; 16-byte aligned,
+ *            ld_codes >= cols / 2 and a multiple of 16.
+ *   scales : E8M0 bytes, row r at scales + r * ld_scales, ld_scales >= cols / 32.          */
+typedef struct {
+  uint8_t *codes;
+  int64_t ld_codes;
+  uint8_t *scales;
+  int64_t ld_scales;
+  int64_t rows;
+  int64_t cols;
+} mxfp4_tensor;
+
+/* nvfp4_mxfp4_quantize — x (device bf16 rows x cols, row stride ld_x elements, 16-byte aligned,
+ * ld_x % 8 == 0) into out (out->rows == rows, out->cols == cols).  One pass, no workspace:
+ * every block is scaled on its own. */
+nvfp4_status nvfp4_mxfp4_quantize(const void *x, int64_t rows, int64_t cols, int64_t ld_x,
+                                  const mxfp4_tensor *out, void *stream);
+
+/* nvfp4_mxfp4_dequantize — y = RN_fp32(code value * 2^(byte - 127)) (exact for every value the
+ * quantizer produces from bf16), NVFP4_OUT_BF16 rounds that to bf16.  y: device rows x cols,
+ * row stride ld_y elements, 16-byte aligned, ld_y % 8 == 0. */
+nvfp4_status nvfp4_mxfp4_dequantize(const mxfp4_tensor *q, void *y, int64_t ld_y, int out_dtype,
+                                    void *stream);
+
+/* nvfp4_mxfp4_gemm — Y = A . W^T with both operands MXFP4, FP32 accumulation, bf16 output:
+ *   Y[m, n] = RN_bf16( sum_k (cA * XA)[m, k] * (cW * XW)[n, k] ).
+ * The products run on CDNA4's scaled FP4 MFMA, which applies the E8M0 scales itself.
+ *   a_bf16 : if not NULL, device bf16 activations (m x k, ld_a as for the quantize) quantized
+ *            to MXFP4 inside the call (into a_q's buffers when a_q is not NULL, else into the
+ *            workspace); if NULL, a_q is the already quantized A.
+ *   w      : n = w->rows, w->cols == k.   y : device bf16 m x n, row stride ld_y, 4-byte
+ *            aligned, ld_y % 2 == 0.   k % 32 == 0.
+ *   ws     : nvfp4_mxfp4_gemm_workspace_bytes(m, k) bytes, 256-byte aligned (may be NULL with
+ *            size 0 when a_bf16 is NULL or a_q receives the quantized A).
+ * Accuracy: the bound of nvfp4_gemm_w4a4, Y64 being the exact product of the reconstructed
+ * operands. */
+size_t nvfp4_mxfp4_gemm_workspace_bytes(int64_t m, int64_t k);
+nvfp4_status nvfp4_mxfp4_gemm(const void *a_bf16, int64_t m, int64_t k, int64_t ld_a,
+                              const mxfp4_tensor *a_q, const mxfp4_tensor *w, void *y,
+                              int64_t ld_y, void *ws, size_t ws_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

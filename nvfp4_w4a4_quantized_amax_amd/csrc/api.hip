@@ -39,6 +39,33 @@ PackedLayout packed_layout(int64_t rows, int64_t k) {
 
 constexpr int64_t kSmallM = 16;
 
+// MXFP4 operand checks.
+nvfp4_status check_mx_tensor(const mxfp4_tensor *t, int64_t rows, int64_t cols) {
+  if (!t) return NVFP4_ERR_NULL;
+  if (!t->codes || !t->scales) return NVFP4_ERR_NULL;
+  if (t->rows != rows || t->cols != cols) return NVFP4_ERR_SHAPE;
+  if (cols <= 0 || cols % 32 || rows < 0) return NVFP4_ERR_SHAPE;
+  if (t->ld_codes < cols / 2 || t->ld_scales < cols / 32) return NVFP4_ERR_SHAPE;
+  if (!aligned(t->codes, 16) || t->ld_codes % 16) return NVFP4_ERR_ALIGN;
+  return NVFP4_OK;
+}
+
+// Quantized-A storage of the MXFP4 product in a workspace (scale rows padded to 4 bytes).
+struct MxLayout {
+  size_t codes_off, scales_off, end;
+  int64_t ld_codes, ld_scales;
+};
+
+MxLayout mx_layout(int64_t rows, int64_t k) {
+  MxLayout L;
+  L.ld_codes = (int64_t)round_up((size_t)(k / 2), 16);
+  L.ld_scales = (int64_t)round_up((size_t)(k / 32), 4);
+  L.codes_off = 0;
+  L.scales_off = round_up((size_t)rows * (size_t)L.ld_codes, kAlign);
+  L.end = round_up(L.scales_off + (size_t)rows * (size_t)L.ld_scales, kAlign);
+  return L;
+}
+
 // Shape/pointer checks of a quantized operand.
 nvfp4_status check_tensor(const nvfp4_tensor *t, int64_t rows, int64_t cols, bool need_16b) {
   if (!t) return NVFP4_ERR_NULL;
@@ -326,6 +353,89 @@ nvfp4_status nvfp4_grouped_gemm_w4a4(const void *a_bf16, int64_t tokens, int64_t
   GemmOperand W{w->codes, w->ld_codes, w->scales, w->ld_scales, w->global_scale, w->block_rows};
   return hip_status(launch_grouped_gemm(A, row_index, offsets, num_groups, W, n, n, k, total_rows,
                                         (uint16_t *)y, ld_y, st));
+}
+
+size_t nvfp4_mxfp4_gemm_workspace_bytes(int64_t m, int64_t k) {
+  if (m <= 0 || k <= 0) return 0;
+  return mx_layout(m, k).end;
+}
+
+nvfp4_status nvfp4_mxfp4_quantize(const void *x, int64_t rows, int64_t cols, int64_t ld_x,
+                                  const mxfp4_tensor *out, void *stream) {
+  if (!out) return NVFP4_ERR_NULL;
+  if (rows == 0 && cols > 0 && cols % 32 == 0) return NVFP4_OK;  // nothing to compute or write
+  nvfp4_status s = check_bf16_input(x, rows, cols, ld_x);
+  if (s) return s;
+  s = check_mx_tensor(out, rows, cols);
+  if (s) return s;
+  return hip_status(launch_mx_quantize(x, rows, cols, ld_x, out->codes, out->ld_codes,
+                                       out->scales, out->ld_scales, (hipStream_t)stream));
+}
+
+nvfp4_status nvfp4_mxfp4_dequantize(const mxfp4_tensor *q, void *y, int64_t ld_y, int out_dtype,
+                                    void *stream) {
+  if (!q) return NVFP4_ERR_NULL;
+  if (q->rows == 0 && q->cols > 0 && q->cols % 32 == 0) return NVFP4_OK;  // empty
+  nvfp4_status s = check_mx_tensor(q, q->rows, q->cols);
+  if (s) return s;
+  if (!y) return NVFP4_ERR_NULL;
+  if (out_dtype != NVFP4_OUT_BF16 && out_dtype != NVFP4_OUT_F32) return NVFP4_ERR_UNSUPPORTED;
+  if (ld_y < q->cols) return NVFP4_ERR_SHAPE;
+  if (!aligned(y, 16) || ld_y % 8) return NVFP4_ERR_ALIGN;
+  if (q->rows * (q->cols / 8) >= (int64_t)1 << 31) return NVFP4_ERR_SHAPE;
+  return hip_status(launch_mx_dequantize(q->codes, q->ld_codes, q->scales, q->ld_scales, q->rows,
+                                         q->cols, y, ld_y, out_dtype == NVFP4_OUT_F32,
+                                         (hipStream_t)stream));
+}
+
+nvfp4_status nvfp4_mxfp4_gemm(const void *a_bf16, int64_t m, int64_t k, int64_t ld_a,
+                              const mxfp4_tensor *a_q, const mxfp4_tensor *w, void *y,
+                              int64_t ld_y, void *ws, size_t ws_bytes, void *stream) {
+  if (!w) return NVFP4_ERR_NULL;
+  if (m < 0 || k <= 0 || k % 32) return NVFP4_ERR_SHAPE;
+  if (m == 0) return NVFP4_OK;  // empty product: nothing to compute or write
+  if (!y) return NVFP4_ERR_NULL;
+  const int64_t n = w->rows;
+  nvfp4_status s = check_mx_tensor(w, n, k);
+  if (s) return s;
+  if (n < 1 || n >= ((int64_t)1 << 30) || m >= ((int64_t)1 << 30)) return NVFP4_ERR_SHAPE;
+  if (ld_y < n) return NVFP4_ERR_SHAPE;
+  if (!aligned(y, 4) || ld_y % 2) return NVFP4_ERR_ALIGN;
+  if (a_q) {
+    s = check_mx_tensor(a_q, m, k);
+    if (s) return s;
+  }
+  if (a_bf16) {
+    s = check_bf16_input(a_bf16, m, k, ld_a);
+    if (s) return s;
+  } else if (!a_q) {
+    return NVFP4_ERR_NULL;
+  }
+  const uint8_t *ac, *as;
+  int64_t ld_ac, ld_as;
+  hipStream_t st = (hipStream_t)stream;
+  if (a_q) {
+    ac = a_q->codes;
+    as = a_q->scales;
+    ld_ac = a_q->ld_codes;
+    ld_as = a_q->ld_scales;
+  } else {
+    if (!ws) return NVFP4_ERR_WORKSPACE;
+    if (ws_bytes < nvfp4_mxfp4_gemm_workspace_bytes(m, k) || !aligned(ws, kAlign))
+      return NVFP4_ERR_WORKSPACE;
+    const MxLayout L = mx_layout(m, k);
+    ac = (const uint8_t *)ws + L.codes_off;
+    as = (const uint8_t *)ws + L.scales_off;
+    ld_ac = L.ld_codes;
+    ld_as = L.ld_scales;
+  }
+  if (a_bf16) {
+    s = hip_status(launch_mx_quantize(a_bf16, m, k, ld_a, (uint8_t *)ac, ld_ac, (uint8_t *)as,
+                                      ld_as, st));
+    if (s) return s;
+  }
+  return hip_status(launch_mx_gemm(ac, ld_ac, as, ld_as, w->codes, w->ld_codes, w->scales,
+                                   w->ld_scales, m, n, k, (uint16_t *)y, ld_y, st));
 }
 
 }  // extern "C"

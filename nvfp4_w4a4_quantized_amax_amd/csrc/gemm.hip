@@ -15,6 +15,7 @@
 // straight into registers and feeds them to four K=16 MFMAs; A and W use the same mapping.
 
 #include "nvfp4_device.hpp"
+#include "gemm_common.hpp"
 #include "launch.hpp"
 
 namespace nvfp4 {
@@ -156,17 +157,6 @@ struct DenseArgs {
   int tiles_m, tiles_n;
 };
 
-// Workgroups are dispatched round-robin over the 8 XCDs (workgroup b runs on XCD b % 8).  Map
-// them so that each XCD gets a contiguous range of logical tiles, and order tiles in groups of
-// kGroupM tile-rows so the tiles that run together on one XCD share A and W panels in its L2.
-constexpr int kXcds = 8;
-constexpr int kGroupM = 8;
-
-__device__ __forceinline__ int xcd_logical(int b, int nwg) {
-  const int per = nwg / kXcds, rem = nwg % kXcds;
-  const int x = b % kXcds, i = b / kXcds;
-  return (x < rem ? x * (per + 1) : rem * (per + 1) + (x - rem) * per) + i;
-}
 
 template <int FM, int FN, bool W2D>
 __global__ __launch_bounds__(kGemmThreads) void k_gemm_tile(DenseArgs p) {
@@ -241,8 +231,6 @@ struct LdsStage {
 
 // One thread's share of a window: chunk c = i * 256 + tid of A and of W (row c / 2, 16-byte
 // half c % 2), and the 4 scale bytes of A row tid and of W row tid (1D) or band tid % 16 (2D).
-typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ uint32_t word(const u32x4_t &v, int i) { return v[i]; }
 struct WindowRegs {
   u32x4_t a0, a1, w0, w1;
   uint32_t as, ws;
@@ -260,10 +248,6 @@ __device__ __forceinline__ void load_window_regs(WindowRegs &r, const uint8_t *c
   r.ws = *(const uint32_t *)(gws + win * 4);
 }
 
-// Byte offset of half `h` of code row `row` in a stage.
-__device__ __forceinline__ int code_offset(int row, int h) {
-  return row * 32 + ((h ^ (row >> 2) ^ (row >> 3)) & 1) * 16;
-}
 
 __device__ __forceinline__ void store_window_regs(const WindowRegs &r, LdsStage &S, int tid) {
   // chunk c = i * 256 + tid is half c % 2 of row c / 2
@@ -276,11 +260,6 @@ __device__ __forceinline__ void store_window_regs(const WindowRegs &r, LdsStage 
   *(uint32_t *)(S.ws + tid * 4) = r.ws;
 }
 
-// Wait for this wave's LDS stores, then for every wave of the workgroup.  The asm's memory
-// clobber keeps the compiler from moving LDS accesses across it.
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
 
 template <bool W2D, class Stage>
 __device__ __forceinline__ void read_stage_frags(const Stage &S, int wave, int wm, int wn,

@@ -1,0 +1,50 @@
+// Pieces shared by the GEMM kernels (NVFP4 and MXFP4): the XCD-aware tile order, the swizzled
+// LDS code layout and the LDS barrier.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nvfp4 {
+
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint32_t word(const u32x4_t &v, int i) { return v[i]; }
+
+// Workgroups are dispatched round-robin over the 8 XCDs (workgroup b runs on XCD b % 8).  Map
+// them so that each XCD gets a contiguous range of logical tiles, and order tiles in groups of
+// kGroupM tile-rows so the tiles that run together on one XCD share A and W panels in its L2.
+constexpr int kXcds = 8;
+constexpr int kGroupM = 8;
+
+__device__ __forceinline__ int xcd_logical(int b, int nwg) {
+  const int per = nwg / kXcds, rem = nwg % kXcds;
+  const int x = b % kXcds, i = b / kXcds;
+  return (x < rem ? x * (per + 1) : rem * (per + 1) + (x - rem) * per) + i;
+}
+
+// Tile (tm, tn) of workgroup `b` in a grid of tiles_m x tiles_n tiles, in the order above.
+__device__ __forceinline__ void tile_of(int b, int nwg, int tiles_m, int tiles_n, int &tm,
+                                        int &tn) {
+  const int logical = xcd_logical(b, nwg);
+  const int in_group = kGroupM * tiles_n;
+  const int first_m = (logical / in_group) * kGroupM;
+  const int gsz = min(tiles_m - first_m, kGroupM);
+  tm = first_m + (logical % in_group) % gsz;
+  tn = (logical % in_group) / gsz;
+}
+
+// Byte offset of half `h` of a 32-byte code row `row` in an LDS stage.  The two 16-byte halves
+// are swapped on rows where bit 2 xor bit 3 of the row is set: a fragment read (one half of 8 or
+// 16 consecutive rows per LDS cycle) then covers every bank once, and a store of 16 consecutive
+// chunks still fills 256 contiguous bytes.
+__device__ __forceinline__ int code_offset(int row, int h) {
+  return row * 32 + ((h ^ (row >> 2) ^ (row >> 3)) & 1) * 16;
+}
+
+// Wait for this wave's LDS stores, then for every wave of the workgroup.  The asm's memory
+// clobber keeps the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+}  // namespace nvfp4

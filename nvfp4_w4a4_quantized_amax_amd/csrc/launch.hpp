@@ -61,4 +61,16 @@ hipError_t launch_grouped_gemm(const GemmOperand &a, const int32_t *row_index,
                                int64_t w_group_rows, int64_t n, int64_t k, int64_t total_rows,
                                uint16_t *y, int64_t ld_y, hipStream_t stream);
 
+// MXFP4 (mxfp4.hip): quantize (one pass), dequantize, and the product on the scaled FP4 MFMA.
+hipError_t launch_mx_quantize(const void *x, int64_t rows, int64_t cols, int64_t ld_x,
+                              uint8_t *codes, int64_t ld_codes, uint8_t *scales, int64_t ld_scales,
+                              hipStream_t stream);
+hipError_t launch_mx_dequantize(const uint8_t *codes, int64_t ld_codes, const uint8_t *scales,
+                                int64_t ld_scales, int64_t rows, int64_t cols, void *y,
+                                int64_t ld_y, int out_f32, hipStream_t stream);
+hipError_t launch_mx_gemm(const uint8_t *a_codes, int64_t ld_ac, const uint8_t *a_scales,
+                          int64_t ld_as, const uint8_t *w_codes, int64_t ld_wc,
+                          const uint8_t *w_scales, int64_t ld_ws, int64_t m, int64_t n, int64_t k,
+                          uint16_t *y, int64_t ld_y, hipStream_t stream);
+
 }  // namespace nvfp4

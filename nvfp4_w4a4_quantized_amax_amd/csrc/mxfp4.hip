@@ -1,0 +1,375 @@
+// MXFP4 for gfx950: the same E2M1 elements as NVFP4 with one E8M0 (power-of-two) scale per 32
+// consecutive values and no tensor scale ("What is NVFP4? 4-bit AI inference on NVIDIA
+// Blackwell explained", section "NVFP4 versus MXFP4"; "NVFP4 Explained: NVIDIA's 4-Bit Format
+// for Faster AI Inference", section "Why the Block Scale Uses FP8 E4M3").
+//
+// Scale of a block: X = 2^e, e = floor(log2(bamax)) - 2 clamped to [-127, 127] (the conversion
+// rule of the MX specification; 2 is the exponent of E2M1's largest value), stored as e + 127.
+// Element: nearest E2M1 value to x / X, ties to even, saturating at 6, sign = signbit(x).
+// x / X = x * 2^-e is exact in fp32 for every bf16 x, so the hardware FP4 conversion of that
+// product (unit scale: round to nearest even, saturating) gives the code directly.
+//
+// Unlike NVFP4's E4M3 scales, these scales are what CDNA4's scaled MFMA consumes natively:
+// v_mfma_scale_f32_32x32x64_f8f6f4 with FP4 operands takes, per lane, 16 code bytes (32
+// consecutive K values of one row, element i in nibble i) and the E8M0 byte of that block, so
+// a lane's fragment is exactly one MXFP4 block of the packed tensor.
+
+#include "nvfp4_device.hpp"
+#include "gemm_common.hpp"
+#include "launch.hpp"
+
+namespace nvfp4 {
+
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+
+// E8M0 exponent of a block from its largest |bf16| bit pattern.  For a normal maximum,
+// floor(log2) is the exponent field minus 127; zero and subnormal maxima (field 0) and the
+// smallest normals land below -127 and clamp there.  The field is at most 254, so e <= 125.
+__device__ __forceinline__ int mx_exponent(uint32_t bam) { return max((int)(bam >> 7) - 129, -127); }
+
+// 2^-e as a float (e in [-127, 125]: the biased exponent 127 - e is in [2, 254]).
+__device__ __forceinline__ float mx_inv_scale(int e) { return __uint_as_float((uint32_t)(127 - e) << 23); }
+
+// ---------------------------------------------------------------------------------------------
+// Quantize: lane l of a wave takes the 16-byte chunk (8 values) l of a 1 KiB run, so loads and
+// stores are contiguous across the wave; the four lanes of a 32-value block share their maxima
+// with two cross-lane steps.  Chunk u of the tensor is row u / (cols / 8), chunk u % (cols / 8).
+// ---------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_mx_quantize(const uint16_t *__restrict__ x, int64_t ld_x,
+                                                     uint32_t n_chunks, FastDiv cpr,
+                                                     uint8_t *__restrict__ codes, int64_t ld_codes,
+                                                     uint8_t *__restrict__ scales,
+                                                     int64_t ld_scales) {
+  const uint32_t stride = gridDim.x * blockDim.x;
+  for (uint32_t u = blockIdx.x * blockDim.x + threadIdx.x; u < n_chunks; u += stride) {
+    const uint32_t r = fdiv(u, cpr), c = u - r * cpr.d;
+    const uint4 v = *(const uint4 *)(x + (int64_t)r * ld_x + (int64_t)c * 8);
+    uint32_t m = absmax8(v);
+    // n_chunks and the row length are multiples of 4, so the four lanes of a block are all
+    // in the loop together.
+    m = max(m, (uint32_t)__shfl_xor((int)m, 1, kWave));
+    m = max(m, (uint32_t)__shfl_xor((int)m, 2, kWave));
+    const int e = mx_exponent(m);
+    const uint32_t q = encode8_fast(v, mx_inv_scale(e));
+    *(uint32_t *)(codes + (int64_t)r * ld_codes + (int64_t)c * 4) = q;
+    if ((c & 3) == 0) scales[(int64_t)r * ld_scales + (c >> 2)] = (uint8_t)(e + 127);
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Dequantize: one thread = 8 values (one code word); value = code value * 2^(byte - 127).
+// ---------------------------------------------------------------------------------------------
+template <bool OUT_F32>
+__global__ __launch_bounds__(256) void k_mx_dequantize(const uint8_t *__restrict__ codes,
+                                                       int64_t ld_codes,
+                                                       const uint8_t *__restrict__ scales,
+                                                       int64_t ld_scales, uint32_t n_chunks,
+                                                       FastDiv cpr, void *__restrict__ y,
+                                                       int64_t ld_y) {
+  const uint32_t stride = gridDim.x * blockDim.x;
+  for (uint32_t u = blockIdx.x * blockDim.x + threadIdx.x; u < n_chunks; u += stride) {
+    const uint32_t r = fdiv(u, cpr), c = u - r * cpr.d;
+    const uint32_t q = *(const uint32_t *)(codes + (int64_t)r * ld_codes + (int64_t)c * 4);
+    const uint32_t b = scales[(int64_t)r * ld_scales + (c >> 2)];
+    // 2^(b - 127) for b in [0, 254]: b = 0 is the fp32 subnormal 2^-127.
+    const float s = b ? __uint_as_float(b << 23) : 0x1p-127f;
+    const floatx2_t f[4] = {__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, 1.0f, 0),
+                            __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, 1.0f, 1),
+                            __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, 1.0f, 2),
+                            __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, 1.0f, 3)};
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[2 * j] = f[j][0] * s;
+      v[2 * j + 1] = f[j][1] * s;
+    }
+    if (OUT_F32) {
+      float *p = (float *)y + (int64_t)r * ld_y + (int64_t)c * 8;
+      ntstore16(p, make_uint4(__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
+                              __float_as_uint(v[3])));
+      ntstore16(p + 4, make_uint4(__float_as_uint(v[4]), __float_as_uint(v[5]),
+                                  __float_as_uint(v[6]), __float_as_uint(v[7])));
+    } else {
+      uint4 o;
+      o.x = f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16);
+      o.y = f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16);
+      o.z = f32_to_bf16_rne(v[4]) | (f32_to_bf16_rne(v[5]) << 16);
+      o.w = f32_to_bf16_rne(v[6]) | (f32_to_bf16_rne(v[7]) << 16);
+      ntstore16((uint16_t *)y + (int64_t)r * ld_y + (int64_t)c * 8, o);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// GEMM Y = A . W^T (both MXFP4, K-contiguous), fp32 accumulation, bf16 out.  The scaled MFMA
+// applies both E8M0 scales itself, so there is no decode: fragments go from LDS (or memory)
+// straight to the matrix core.
+// ---------------------------------------------------------------------------------------------
+struct MxArgs {
+  const uint8_t *a_codes, *a_scales, *w_codes, *w_scales;
+  int64_t ld_ac, ld_as, ld_wc, ld_ws;
+  int64_t m, n, k;
+  uint16_t *y;
+  int64_t ld_y;
+  int tiles_m, tiles_n;
+};
+
+__device__ __forceinline__ floatx16_t mx_mfma(const u32x4_t &a, const u32x4_t &w, uint32_t sa,
+                                              uint32_t sw, const floatx16_t &c) {
+  // FP4 operands occupy only the first four registers of the 8-register operand; the rest is
+  // left undefined (the instruction does not read it).
+  const i32x8_t av = __builtin_shufflevector((i32x4_t)a, (i32x4_t)a, 0, 1, 2, 3, -1, -1, -1, -1);
+  const i32x8_t wv = __builtin_shufflevector((i32x4_t)w, (i32x4_t)w, 0, 1, 2, 3, -1, -1, -1, -1);
+  // cbsz = blgp = 4: both operands FP4 (E2M1); scale byte 0 of each scale register.
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, wv, c, 4, 4, 0, (int)sa, 0, (int)sw);
+}
+
+// Pipelined 256 x 256 tiles (K a multiple of 64, scale rows 2-byte aligned).  One 64-wide K
+// window of a tile is 256 rows x 32 code bytes of A and of W plus 2 scale bytes per row; it is
+// loaded into registers two windows ahead, stored to one of two LDS stages one window ahead and
+// read back by the waves that use it.  Each wave computes 128 x 128 as 4 x 4 MFMA tiles of
+// 32 x 32; per window that is 16 MFMAs, the first 8 before and the last 8 after the barrier
+// that publishes the next window, so the LDS reads of the next window hide behind the second
+// half.  The scale bytes are read from LDS one by one: extracting them from 16-bit reads made
+// the register allocator spill the accumulators.
+struct MxStage {
+  uint8_t a[256 * 32];
+  uint8_t w[256 * 32];
+  uint16_t as[256];
+  uint16_t ws[256];
+};
+
+struct MxWindowRegs {
+  u32x4_t a0, a1, w0, w1;
+  uint16_t as, ws;
+};
+
+struct MxFrags {
+  u32x4_t a[4], w[4];
+  uint32_t sa[4], sw[4];
+};
+
+__device__ __forceinline__ void mx_load_window(MxWindowRegs &r, const uint8_t *const (&ga)[2],
+                                               const uint8_t *const (&gw)[2], const uint8_t *gas,
+                                               const uint8_t *gws, int64_t win) {
+  r.a0 = *(const u32x4_t *)(ga[0] + win * 32);
+  r.a1 = *(const u32x4_t *)(ga[1] + win * 32);
+  r.w0 = *(const u32x4_t *)(gw[0] + win * 32);
+  r.w1 = *(const u32x4_t *)(gw[1] + win * 32);
+  r.as = *(const uint16_t *)(gas + win * 2);
+  r.ws = *(const uint16_t *)(gws + win * 2);
+}
+
+__device__ __forceinline__ void mx_store_window(const MxWindowRegs &r, MxStage &S, int tid) {
+  // chunk c = i * 256 + tid is half c % 2 of row c / 2
+  const int o0 = code_offset(tid >> 1, tid & 1), o1 = code_offset(128 + (tid >> 1), tid & 1);
+  *(u32x4_t *)(S.a + o0) = r.a0;
+  *(u32x4_t *)(S.a + o1) = r.a1;
+  *(u32x4_t *)(S.w + o0) = r.w0;
+  *(u32x4_t *)(S.w + o1) = r.w1;
+  S.as[tid] = r.as;
+  S.ws[tid] = r.ws;
+}
+
+// Lane (row lr, half kh) of fragment f: row wm * 128 + f * 32 + lr of A, K half kh (one 32-value
+// block) with its scale byte; likewise for W.
+__device__ __forceinline__ void mx_read_frags(const MxStage &S, int wm, int wn, int lr, int kh,
+                                              MxFrags &fr) {
+#pragma unroll
+  for (int f = 0; f < 4; ++f) {
+    const int ra = wm * 128 + f * 32 + lr, rw = wn * 128 + f * 32 + lr;
+    fr.a[f] = *(const u32x4_t *)(S.a + code_offset(ra, kh));
+    fr.w[f] = *(const u32x4_t *)(S.w + code_offset(rw, kh));
+    fr.sa[f] = ((const uint8_t *)S.as)[ra * 2 + kh];
+    fr.sw[f] = ((const uint8_t *)S.ws)[rw * 2 + kh];
+  }
+}
+
+// Rows f0, f0 + 1 of the 4 x 4 MFMA tiles.
+template <int F0>
+__device__ __forceinline__ void mx_mfma_half(const MxFrags &fr, floatx16_t (&acc)[4][4]) {
+#pragma unroll
+  for (int f = F0; f < F0 + 2; ++f)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) acc[f][g] = mx_mfma(fr.a[f], fr.w[g], fr.sa[f], fr.sw[g], acc[f][g]);
+}
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_gemm_mx_lds(MxArgs p) {
+  __shared__ __align__(16) MxStage st[2];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int lr = lane & 31, kh = lane >> 5;
+  int tm, tn;
+  tile_of(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, tm, tn);
+  const int64_t m_tile = (int64_t)tm * 256, n_tile = (int64_t)tn * 256;
+
+  // This thread's share of every window's loads (rows clamped into the matrix; results of
+  // clamped rows are never stored).
+  const uint8_t *ga[2], *gw[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int c = i * 256 + tid, row = c >> 1, half = c & 1;
+    ga[i] = p.a_codes + min(m_tile + row, p.m - 1) * p.ld_ac + half * 16;
+    gw[i] = p.w_codes + min(n_tile + row, p.n - 1) * p.ld_wc + half * 16;
+  }
+  const uint8_t *gas = p.a_scales + min(m_tile + tid, p.m - 1) * p.ld_as;
+  const uint8_t *gws = p.w_scales + min(n_tile + tid, p.n - 1) * p.ld_ws;
+  const int64_t nwin = p.k / 64;  // >= 1
+
+  floatx16_t acc[4][4];
+#pragma unroll
+  for (int f = 0; f < 4; ++f)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) acc[f][g] = floatx16_t{};
+
+  // Window 0 goes to stage 0 and window 1 stays in registers.  In window w, window w + 1 is
+  // stored to stage (w + 1) % 2 (whose previous window every wave read before the last
+  // barrier) and window w + 2 is loaded; after the barrier, window w + 1 is read back.
+  // Windows past the end are clamped to the last one.
+  MxWindowRegs r;
+  mx_load_window(r, ga, gw, gas, gws, 0);
+  mx_store_window(r, st[0], tid);
+  mx_load_window(r, ga, gw, gas, gws, min((int64_t)1, nwin - 1));
+  lds_barrier();
+  MxFrags fa, fb;
+  mx_read_frags(st[0], wm, wn, lr, kh, fa);
+  // One window: its first 8 MFMAs overlap the store of window w + 1 and the loads of window
+  // w + 2, the last 8 the reads of window w + 1 (the scheduler is asked to alternate them).
+  auto window = [&](int64_t w, const MxFrags &cur, MxFrags &nxt) {
+    mx_store_window(r, st[(w + 1) & 1], tid);
+    mx_load_window(r, ga, gw, gas, gws, min(w + 2, nwin - 1));
+    mx_mfma_half<0>(cur, acc);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      if (i < 6) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // LDS write
+      if (i < 6) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // vector memory read
+    }
+    lds_barrier();
+    mx_read_frags(st[(w + 1) & 1], wm, wn, lr, kh, nxt);
+    mx_mfma_half<2>(cur, acc);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS reads
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // Two windows per iteration, so the fragment registers alternate without copies.  The last
+  // window also stores, loads and reads a (clamped) window past the end, which is never used.
+  int64_t w = 0;
+  for (; w + 1 < nwin; w += 2) {
+    window(w, fa, fb);
+    window(w + 1, fb, fa);
+  }
+  if (w < nwin) window(w, fa, fb);
+
+  const int64_t m0 = m_tile + wm * 128, n0 = n_tile + wn * 128;
+  const bool full = m_tile + 256 <= p.m && n_tile + 256 <= p.n;
+#pragma unroll
+  for (int f = 0; f < 4; ++f)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int64_t col = n0 + g * 32 + lr;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int64_t row = m0 + f * 32 + 8 * (i >> 2) + 4 * kh + (i & 3);
+        if (full || (row < p.m && col < p.n))
+          ntstore_u16(p.y + row * p.ld_y + col, f32_to_bf16_rne(acc[f][g][i]));
+      }
+    }
+}
+
+// Any shape (K a multiple of 32): each wave computes one 32 x 32 tile straight from memory, one
+// 64-wide K window at a time; a missing second block of the last window reads as zero codes.
+__global__ __launch_bounds__(256) void k_gemm_mx_simple(MxArgs p) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lr = lane & 31, kh = lane >> 5;
+  const int64_t tile = (int64_t)blockIdx.x * 4 + wave;
+  if (tile >= (int64_t)p.tiles_m * p.tiles_n) return;
+  const int64_t m0 = (tile / p.tiles_n) * 32, n0 = (tile % p.tiles_n) * 32;
+  const int64_t ra = min(m0 + lr, p.m - 1), rw = min(n0 + lr, p.n - 1);
+  const uint8_t *ac = p.a_codes + ra * p.ld_ac + kh * 16, *as = p.a_scales + ra * p.ld_as + kh;
+  const uint8_t *wc = p.w_codes + rw * p.ld_wc + kh * 16, *ws = p.w_scales + rw * p.ld_ws + kh;
+  const int64_t nblk = p.k / 32;
+  floatx16_t acc = floatx16_t{};
+  for (int64_t b0 = 0; b0 < nblk; b0 += 2) {
+    const bool in = b0 + kh < nblk;  // this lane's block exists
+    const u32x4_t z = {0u, 0u, 0u, 0u};
+    const u32x4_t a = in ? *(const u32x4_t *)(ac + b0 * 16) : z;
+    const u32x4_t w = in ? *(const u32x4_t *)(wc + b0 * 16) : z;
+    const uint32_t sa = in ? as[b0] : 127u, sw = in ? ws[b0] : 127u;
+    acc = mx_mfma(a, w, sa, sw, acc);
+  }
+  const int64_t col = n0 + lr;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int64_t row = m0 + 8 * (i >> 2) + 4 * kh + (i & 3);
+    if (row < p.m && col < p.n) ntstore_u16(p.y + row * p.ld_y + col, f32_to_bf16_rne(acc[i]));
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Host launchers
+// ---------------------------------------------------------------------------------------------
+static FastDiv mx_fastdiv(uint32_t d) {
+  FastDiv f;
+  f.d = d;
+  uint32_t s = 0;
+  while ((1ull << s) < d) ++s;
+  f.shift = s;
+  f.mul = (uint32_t)(((1ull << 32) * ((1ull << s) - d)) / d + 1ull);
+  return f;
+}
+
+static unsigned mx_grid(uint32_t n_chunks) {
+  uint32_t g = (n_chunks + 255) / 256;
+  if (g > 4096) g = 4096;
+  return g < 1 ? 1 : g;
+}
+
+hipError_t launch_mx_quantize(const void *x, int64_t rows, int64_t cols, int64_t ld_x,
+                              uint8_t *codes, int64_t ld_codes, uint8_t *scales, int64_t ld_scales,
+                              hipStream_t stream) {
+  const uint32_t cpr = (uint32_t)(cols / 8), n = (uint32_t)(rows * (cols / 8));
+  hipLaunchKernelGGL(k_mx_quantize, dim3(mx_grid(n)), dim3(256), 0, stream, (const uint16_t *)x,
+                     ld_x, n, mx_fastdiv(cpr), codes, ld_codes, scales, ld_scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_mx_dequantize(const uint8_t *codes, int64_t ld_codes, const uint8_t *scales,
+                                int64_t ld_scales, int64_t rows, int64_t cols, void *y,
+                                int64_t ld_y, int out_f32, hipStream_t stream) {
+  const uint32_t cpr = (uint32_t)(cols / 8), n = (uint32_t)(rows * (cols / 8));
+  if (out_f32)
+    hipLaunchKernelGGL(k_mx_dequantize<true>, dim3(mx_grid(n)), dim3(256), 0, stream, codes,
+                       ld_codes, scales, ld_scales, n, mx_fastdiv(cpr), y, ld_y);
+  else
+    hipLaunchKernelGGL(k_mx_dequantize<false>, dim3(mx_grid(n)), dim3(256), 0, stream, codes,
+                       ld_codes, scales, ld_scales, n, mx_fastdiv(cpr), y, ld_y);
+  return hipGetLastError();
+}
+
+hipError_t launch_mx_gemm(const uint8_t *a_codes, int64_t ld_ac, const uint8_t *a_scales,
+                          int64_t ld_as, const uint8_t *w_codes, int64_t ld_wc,
+                          const uint8_t *w_scales, int64_t ld_ws, int64_t m, int64_t n, int64_t k,
+                          uint16_t *y, int64_t ld_y, hipStream_t stream) {
+  MxArgs p{a_codes, a_scales, w_codes, w_scales, ld_ac, ld_as, ld_wc, ld_ws, m, n, k, y, ld_y, 0, 0};
+  const bool pipelined = m > 128 && k % 64 == 0 && (uintptr_t)a_scales % 2 == 0 &&
+                         (uintptr_t)w_scales % 2 == 0 && ld_as % 2 == 0 && ld_ws % 2 == 0;
+  if (pipelined) {
+    p.tiles_m = (int)((m + 255) / 256);
+    p.tiles_n = (int)((n + 255) / 256);
+    hipLaunchKernelGGL(k_gemm_mx_lds, dim3((unsigned)p.tiles_m * (unsigned)p.tiles_n), dim3(256),
+                       0, stream, p);
+    return hipGetLastError();
+  }
+  p.tiles_m = (int)((m + 31) / 32);
+  p.tiles_n = (int)((n + 31) / 32);
+  const int64_t tiles = (int64_t)p.tiles_m * p.tiles_n;
+  hipLaunchKernelGGL(k_gemm_mx_simple, dim3((unsigned)((tiles + 3) / 4)), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace nvfp4

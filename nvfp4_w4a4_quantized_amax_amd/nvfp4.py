@@ -26,7 +26,8 @@ EXPORTED = (
     "nvfp4_status_string", "nvfp4_version", "nvfp4_quantize_workspace_bytes",
     "nvfp4_gemm_workspace_bytes", "nvfp4_grouped_gemm_workspace_bytes", "nvfp4_quantize_1d",
     "nvfp4_quantize_2d", "nvfp4_dequantize", "nvfp4_gemm_w4a4", "nvfp4_grouped_gemm_w4a4",
-    "nvfp4_gemm_w4a16",
+    "nvfp4_gemm_w4a16", "nvfp4_mxfp4_quantize", "nvfp4_mxfp4_dequantize",
+    "nvfp4_mxfp4_gemm_workspace_bytes", "nvfp4_mxfp4_gemm",
 )
 
 
@@ -39,8 +40,16 @@ class CTensor(ctypes.Structure):
                 ("reserved", ctypes.c_int32)]
 
 
+class CMxTensor(ctypes.Structure):
+    """Mirror of `mxfp4_tensor`."""
+    _fields_ = [("codes", ctypes.c_void_p), ("ld_codes", ctypes.c_int64),
+                ("scales", ctypes.c_void_p), ("ld_scales", ctypes.c_int64),
+                ("rows", ctypes.c_int64), ("cols", ctypes.c_int64)]
+
+
 _i64, _i32, _vp, _sz = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t
 _pt = ctypes.POINTER(CTensor)
+_pmx = ctypes.POINTER(CMxTensor)
 
 _lib.nvfp4_status_string.restype = ctypes.c_char_p
 _lib.nvfp4_status_string.argtypes = [ctypes.c_int]
@@ -60,6 +69,14 @@ _lib.nvfp4_gemm_w4a4.restype = ctypes.c_int
 _lib.nvfp4_gemm_w4a4.argtypes = [_vp, _i64, _i64, _i64, _pt, _pt, _vp, _i64, _vp, _sz, _vp]
 _lib.nvfp4_gemm_w4a16.restype = ctypes.c_int
 _lib.nvfp4_gemm_w4a16.argtypes = [_vp, _i64, _i64, _i64, _pt, _vp, _i64, _vp]
+_lib.nvfp4_mxfp4_quantize.restype = ctypes.c_int
+_lib.nvfp4_mxfp4_quantize.argtypes = [_vp, _i64, _i64, _i64, _pmx, _vp]
+_lib.nvfp4_mxfp4_dequantize.restype = ctypes.c_int
+_lib.nvfp4_mxfp4_dequantize.argtypes = [_pmx, _vp, _i64, ctypes.c_int, _vp]
+_lib.nvfp4_mxfp4_gemm_workspace_bytes.restype = _sz
+_lib.nvfp4_mxfp4_gemm_workspace_bytes.argtypes = [_i64, _i64]
+_lib.nvfp4_mxfp4_gemm.restype = ctypes.c_int
+_lib.nvfp4_mxfp4_gemm.argtypes = [_vp, _i64, _i64, _i64, _pmx, _pmx, _vp, _i64, _vp, _sz, _vp]
 _lib.nvfp4_grouped_gemm_w4a4.restype = ctypes.c_int
 _lib.nvfp4_grouped_gemm_w4a4.argtypes = [_vp, _i64, _i64, _i64, _pt, _vp, _i64, _vp, _i32, _pt,
                                          _i64, _vp, _i64, _vp, _sz, _vp]
@@ -243,4 +260,81 @@ def grouped_gemm_w4a4(a, row_index, offsets, w, n, total_rows, y=None, a_q=None,
         ctypes.byref(ac) if ac is not None else None, _ptr(row_index), total_rows, _ptr(offsets),
         num_groups, ctypes.byref(wc), n, _ptr(y), y.stride(0), _ptr(ws), ws.numel(),
         _stream(dev)), "nvfp4_grouped_gemm_w4a4")
+    return y
+
+
+# ---------------------------------------------------------------------------------------------
+# MXFP4
+# ---------------------------------------------------------------------------------------------
+@dataclass
+class MxTensor:
+    """An MXFP4 matrix in device memory: packed codes (rows x ld_codes bytes) and one E8M0
+    scale byte per 32 values (rows x ld_scales bytes)."""
+    codes: torch.Tensor
+    scales: torch.Tensor
+    rows: int
+    cols: int
+
+    def c(self):
+        return CMxTensor(self.codes.data_ptr(), self.codes.stride(0), self.scales.data_ptr(),
+                         self.scales.stride(0), self.rows, self.cols)
+
+    def packed_codes(self):
+        return self.codes[:, : self.cols // 2]
+
+    def packed_scales(self):
+        return self.scales[:, : self.cols // 32]
+
+
+def empty_mxtensor(rows, cols, device="cuda"):
+    codes = torch.empty((rows, max(_round_up(cols // 2, 16), 16)), dtype=torch.uint8,
+                        device=device)
+    scales = torch.empty((rows, max(_round_up(cols // 32, 4), 4)), dtype=torch.uint8,
+                         device=device)
+    return MxTensor(codes, scales, rows, cols)
+
+
+def mxfp4_quantize(x, out=None):
+    """MXFP4 quantization of a bf16 matrix: one E8M0 scale per 32 values along rows."""
+    assert x.dtype == torch.bfloat16 and x.dim() == 2 and x.stride(1) == 1
+    rows, cols = x.shape
+    if out is None:
+        out = empty_mxtensor(rows, cols, x.device)
+    ct = out.c()
+    _check(_lib.nvfp4_mxfp4_quantize(_ptr(x), rows, cols, x.stride(0), ctypes.byref(ct),
+                                     _stream(x.device)), "nvfp4_mxfp4_quantize")
+    return out
+
+
+def mxfp4_dequantize(q, dtype=torch.float32, out=None):
+    if out is None:
+        out = torch.empty((q.rows, q.cols), dtype=dtype, device=q.codes.device)
+    ct = q.c()
+    code = OUT_F32 if out.dtype == torch.float32 else OUT_BF16
+    _check(_lib.nvfp4_mxfp4_dequantize(ctypes.byref(ct), _ptr(out), out.stride(0), code,
+                                       _stream(q.codes.device)), "nvfp4_mxfp4_dequantize")
+    return out
+
+
+def mxfp4_gemm(a, w, y=None, a_q=None, ws=None):
+    """Y = A . W^T (bf16 out) with both operands MXFP4.  `a` is a bf16 matrix (quantized inside
+    the call; `a_q`, if given, receives it) or an MxTensor."""
+    if isinstance(a, MxTensor):
+        m, k = a.rows, a.cols
+        a_bf16, a_q, dev = None, a, a.codes.device
+    else:
+        assert a.dtype == torch.bfloat16 and a.dim() == 2 and a.stride(1) == 1
+        m, k = a.shape
+        a_bf16, dev = a, a.device
+    n = w.rows
+    if y is None:
+        y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+    nbytes = _lib.nvfp4_mxfp4_gemm_workspace_bytes(m, k) if a_q is None else 0
+    ws = _ws(nbytes, dev, ws) if nbytes else ws
+    wc = w.c()
+    ac = a_q.c() if a_q is not None else None
+    _check(_lib.nvfp4_mxfp4_gemm(_ptr(a_bf16), m, k, a_bf16.stride(0) if a_bf16 is not None else 0,
+                                 ctypes.byref(ac) if ac is not None else None, ctypes.byref(wc),
+                                 _ptr(y), y.stride(0), _ptr(ws), ws.numel() if ws is not None else 0,
+                                 _stream(dev)), "nvfp4_mxfp4_gemm")
     return y

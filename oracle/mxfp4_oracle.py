@@ -52,20 +52,26 @@ def shared_exponents(bamax):
     return np.clip(e, -E8M0_BIAS, E8M0_BIAS)
 
 
-def quantize_mx(x_bf16_bits):
+def quantize_mx(x_bf16_bits, row_chunk=256):
     """MXFP4 quantization of a bf16 matrix (R x C, C % 32 == 0): one E8M0 scale per 32
-    consecutive row elements, E2M1 codes packed two per byte.
+    consecutive row elements, E2M1 codes packed two per byte.  Rows are processed in chunks
+    only to bound memory; every block is independent.
 
     Returns (codes uint8 R x C/2, scales uint8 R x C/32)."""
-    x = O._as_f64(x_bf16_bits)
-    if x.ndim != 2 or x.shape[1] % MX_BLOCK:
+    x_bf16_bits = np.asarray(x_bf16_bits, dtype=np.uint16)
+    if x_bf16_bits.ndim != 2 or x_bf16_bits.shape[1] % MX_BLOCK:
         raise ValueError("cols must be a multiple of 32")
-    r, c = x.shape
-    blocks = x.reshape(r, c // MX_BLOCK, MX_BLOCK)
-    e = shared_exponents(np.max(np.abs(blocks), axis=2))            # R x C/32
-    scale_el = np.repeat(np.ldexp(1.0, e), MX_BLOCK, axis=1)        # 2^e per element
-    codes = O.element_codes(x, scale_el, 1.0)                        # R15: |x| against mid * 2^e
-    return O.pack_codes(codes), (e + E8M0_BIAS).astype(np.uint8)
+    r, c = x_bf16_bits.shape
+    codes = np.empty((r, c // 2), dtype=np.uint8)
+    scales = np.empty((r, c // MX_BLOCK), dtype=np.uint8)
+    for r0 in range(0, r, row_chunk):
+        x = O._as_f64(x_bf16_bits[r0:r0 + row_chunk])
+        blocks = x.reshape(x.shape[0], c // MX_BLOCK, MX_BLOCK)
+        e = shared_exponents(np.max(np.abs(blocks), axis=2))         # rows x C/32
+        scale_el = np.repeat(np.ldexp(1.0, e), MX_BLOCK, axis=1)     # 2^e per element
+        codes[r0:r0 + row_chunk] = O.pack_codes(O.element_codes(x, scale_el, 1.0))  # R15
+        scales[r0:r0 + row_chunk] = (e + E8M0_BIAS).astype(np.uint8)
+    return codes, scales
 
 
 def dequantize_mx(codes, scales, out="f64"):

@@ -157,6 +157,44 @@ def test_grouped_validation():
     assert grouped(FAKE, 32, 128, None, FAKE, 64, FAKE, 8, w, 64, ws=None) == nv.ERR_WORKSPACE
 
 
+def mxt(rows, cols, ld=None, codes=FAKE, lds=None):
+    ld = ld if ld is not None else max((cols // 2 + 15) // 16 * 16, 16)
+    return nv.CMxTensor(codes, ld, FAKE, cols // 32 if lds is None else lds, rows, cols)
+
+
+def test_mxfp4_validation():
+    q = mxt(64, 256)
+    Q = L.nvfp4_mxfp4_quantize
+    assert Q(FAKE, 64, 256, 256, None, None) == nv.ERR_NULL
+    assert Q(None, 64, 256, 256, ctypes.byref(q), None) == nv.ERR_NULL
+    assert Q(FAKE, 64, 240, 240, ctypes.byref(mxt(64, 240)), None) == nv.ERR_SHAPE   # cols % 32
+    assert Q(FAKE, 64, 256, 256, ctypes.byref(mxt(64, 288)), None) == nv.ERR_SHAPE   # cols mismatch
+    assert Q(FAKE, 64, 256, 256, ctypes.byref(mxt(64, 256, ld=136)), None) == nv.ERR_ALIGN
+    assert Q(FAKE, 64, 256, 256, ctypes.byref(mxt(64, 256, lds=4)), None) == nv.ERR_SHAPE
+    assert Q(FAKE, 64, 256, 256, ctypes.byref(mxt(64, 256, codes=FAKE + 4)), None) == nv.ERR_ALIGN
+    assert Q(FAKE + 2, 64, 256, 256, ctypes.byref(q), None) == nv.ERR_ALIGN
+    D = L.nvfp4_mxfp4_dequantize
+    assert D(ctypes.byref(q), None, 256, nv.OUT_F32, None) == nv.ERR_NULL
+    assert D(ctypes.byref(q), FAKE, 256, 7, None) == nv.ERR_UNSUPPORTED
+    assert D(ctypes.byref(q), FAKE, 128, nv.OUT_F32, None) == nv.ERR_SHAPE
+    G = L.nvfp4_mxfp4_gemm
+    w = mxt(128, 256)
+    assert G(FAKE, 8, 256, 256, None, None, FAKE, 128, FAKE, 1 << 30, None) == nv.ERR_NULL
+    assert G(FAKE, 8, 240, 240, None, ctypes.byref(w), FAKE, 128, FAKE, 1 << 30, None) == \
+        nv.ERR_SHAPE                                                          # k % 32
+    assert G(FAKE, 8, 224, 224, None, ctypes.byref(w), FAKE, 128, FAKE, 1 << 30, None) == \
+        nv.ERR_SHAPE                                                          # K mismatch
+    assert G(FAKE, 8, 256, 256, None, ctypes.byref(w), FAKE, 100, FAKE, 1 << 30, None) == \
+        nv.ERR_SHAPE                                                          # ld_y < n
+    assert G(FAKE, 8, 256, 256, None, ctypes.byref(w), FAKE, 128, None, 0, None) == \
+        nv.ERR_WORKSPACE                                                      # A quantized inside
+    assert G(None, 8, 256, 0, None, ctypes.byref(w), FAKE, 128, None, 0, None) == nv.ERR_NULL
+    assert L.nvfp4_mxfp4_gemm_workspace_bytes(8, 256) >= 8 * 128 + 8 * 8
+    # empty problems
+    assert G(None, 0, 256, 0, None, ctypes.byref(w), None, 128, None, 0, None) == nv.OK
+    assert Q(None, 0, 256, 256, ctypes.byref(mxt(0, 256)), None) == nv.OK
+
+
 def test_empty_problems_need_no_buffers():
     """Zero rows: nothing is computed or written, NVFP4_OK is returned and the data pointers
     may be NULL (no GPU work is launched, so this runs without a device)."""

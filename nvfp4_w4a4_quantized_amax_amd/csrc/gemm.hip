@@ -935,8 +935,11 @@ __device__ __forceinline__ void load_decode_w(const SmallMArgs &p, const WBufs &
   if (FULL) {
     const bool valid = band < nbands;
     const int64_t row = min(band * 16 + i16, p.n - 1);
-    const uint32_t cb = (uint32_t)(row * p.w.ld_codes) + q * 16;
-    const uint32_t sb = (uint32_t)((W2D ? band : row) * p.w.ld_scales) + q * 2;
+    // 32-bit offsets; the empty asm keeps the adds plain (see gv_load_row).
+    uint32_t rc = (uint32_t)row * (uint32_t)p.w.ld_codes;
+    uint32_t rs = (uint32_t)(W2D ? band : row) * (uint32_t)p.w.ld_scales;
+    asm volatile("" : "+v"(rc), "+v"(rs));
+    const uint32_t cb = rc + q * 16, sb = rs + q * 2;
 #pragma unroll
     for (int u = 0; u < WIN; ++u) {
       const bool in = valid && u < nw;
@@ -1002,7 +1005,8 @@ __device__ __forceinline__ void decode_band_loop(const SmallMArgs &p, const WBuf
     if (wave < 4 && i16 < p.m) {
       float t = 0.0f;
 #pragma unroll
-      for (int w2 = 0; w2 < kDecWaves; ++w2) t += s_red[parity][w2][lane][wave];
+      for (int w2 = 0; w2 < kDecWaves; ++w2)  // component `wave` of each partial, 4-byte reads
+        t += ((const float *)&s_red[parity][w2][lane])[wave];
       const int64_t n = band * 16 + 4 * q + wave;
       if (n < p.n) ntstore_u16(p.y + (int64_t)i16 * p.ld_y + n, f32_to_bf16_rne(t * alpha));
     }
@@ -1244,6 +1248,133 @@ __global__ __launch_bounds__(kDecWaves * 64) void k_gemm_w4a16_decode(SmallMArgs
       });
 }
 
+// ---------------------------------------------------------------------------------------------
+// W4A16 GEMV for a single activation row (m == 1, K = 1024 * NB with NB in {2, 4, 8}): no
+// MFMA, no LDS reduction and no barrier in the loop.  Each wave owns whole rows of W (rows w,
+// w + G, ... for G waves in the grid); lane l covers K values [16 NB l, 16 NB (l + 1)), i.e. NB
+// blocks: NB * 8 code bytes and NB scale bytes of the row, and the same K range of A, which it
+// holds in registers as packed bf16 pairs (A is read from memory once per workgroup, through
+// LDS).  The unscaled W codes are converted to bf16 pairs (exact) and multiplied into fp32 with
+// the 2-term dot instruction; each 16-value block's sum takes its W scale with one FMA, and the
+// 64 lane partials of a row meet through cross-lane adds.  gv_depth(NB) rows are in flight per
+// wave, read with buffer loads: rows past the end get an offset beyond the buffer size (zeros,
+// no memory access), so the loads carry no control flow.
+// Used for N >= 8192, where it measured faster than the decode form (11.4 against 12.0 us at
+// 14336 x 4096, 15.0 against 16.6 at 28672 x 4096); for smaller N its fixed cost (A staged
+// through LDS, one row per wave) makes it slower.  A W4A4 form was slower than the decode
+// kernels at every size measured, so there is none.
+// ---------------------------------------------------------------------------------------------
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int gv_depth(int nb) { return nb == 8 ? 2 : 4; }
+
+template <int NB>
+struct GvRow {
+  u32x4_t c[NB / 2];  // NB * 8 code bytes
+  uint32_t s[(NB + 3) / 4];
+};
+
+template <bool W2D, int NB>
+__device__ __forceinline__ void gv_load_row(const SmallMArgs &p, const WBufs &buf, int64_t row,
+                                            int lane, GvRow<NB> &r) {
+  const bool valid = row < p.n;
+  const int64_t srow = W2D ? row / 16 : row;
+  // The offsets fit in 32 bits (buffers under 2 GiB).  The row products pass through an empty
+  // asm so that the lane offset is added with a plain 32-bit add: fused into a 64-bit
+  // multiply-add, the unused high half of the addend lands in a register that a pending load
+  // writes, and the read then waits for that load.
+  uint32_t rc = (uint32_t)row * (uint32_t)p.w.ld_codes, rs = (uint32_t)srow * (uint32_t)p.w.ld_scales;
+  asm volatile("" : "+v"(rc), "+v"(rs));
+  const uint32_t co = valid ? rc + lane * (NB * 8) : kBufOutOfRange;
+  const uint32_t so = valid ? rs + lane * NB : kBufOutOfRange;
+#pragma unroll
+  for (int i = 0; i < NB / 2; ++i)
+    r.c[i] = __builtin_amdgcn_raw_buffer_load_b128(buf.codes, (int)(co + (valid ? 16 * i : 0)), 0, 0);
+  if (NB == 2) r.s[0] = __builtin_amdgcn_raw_buffer_load_b16(buf.scales, (int)so, 0, 0);
+  if (NB == 4) r.s[0] = __builtin_amdgcn_raw_buffer_load_b32(buf.scales, (int)so, 0, 0);
+  if (NB == 8) {
+    const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(buf.scales, (int)so, 0, 0);
+    r.s[0] = v[0];
+    r.s[1] = v[1];
+  }
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+template <bool W2D, int NB>
+__global__ __launch_bounds__(kDecWaves * 64) void k_gemv_w4a16(SmallMArgs p) {
+  constexpr int D = gv_depth(NB);
+  constexpr int NW = NB * 2;  // code words per lane per row
+  // The wave index is uniform; saying so keeps the row logic scalar.
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t g = (int64_t)gridDim.x * kDecWaves;
+  const int64_t first = (int64_t)blockIdx.x * kDecWaves + wave;
+  const WBufs buf = make_wbufs(p);
+  const float alpha = *p.w.gs;
+
+  // A (one row) is read from memory once per workgroup into LDS (thread t copies 16-byte chunk
+  // t; its load goes out before the W loads, so waiting for it waits for nothing else); every
+  // wave then takes its copy from there.  Lane l's K range: NB blocks of 16 values.
+  __shared__ __align__(16) uint8_t s_a[NB * 2048];
+  const int tid = threadIdx.x;
+  constexpr int kChunks = NB * 128;  // <= 1024 = the workgroup size
+  uint4 achunk = make_uint4(0, 0, 0, 0);
+  if (tid < kChunks) achunk = *(const uint4 *)(p.a_bf16 + 8 * tid);
+  GvRow<NB> ring[D];
+#pragma unroll
+  for (int j = 0; j < D; ++j) {
+    gv_load_row<W2D, NB>(p, buf, first + j * g, lane, ring[j]);
+    __builtin_amdgcn_sched_barrier(0);  // keep the loads in row order: row j waits only for rows <= j
+  }
+  if (tid < kChunks) *(uint4 *)(s_a + 16 * tid) = achunk;
+  lds_barrier();
+  // A as packed bf16 pairs.
+  uint32_t a2[NW * 4];
+#pragma unroll
+  for (int i = 0; i < 2 * NB; ++i) {
+    const uint4 v = *(const uint4 *)(s_a + lane * (NB * 32) + 16 * i);
+    a2[4 * i] = v.x;
+    a2[4 * i + 1] = v.y;
+    a2[4 * i + 2] = v.z;
+    a2[4 * i + 3] = v.w;
+  }
+
+  for (int64_t base = first; base < p.n; base += D * g) {
+#pragma unroll
+    for (int j = 0; j < D; ++j) {
+      const int64_t row = base + j * g;
+      float acc = 0.0f;
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const uint32_t sbyte = (ring[j].s[b / 4] >> (8 * (b % 4))) & 0xFFu;
+        const float sb = scales_f32x2(sbyte)[0];
+        float sum = 0.0f;
+#pragma unroll
+        for (int w = 0; w < 2; ++w) {
+          const uint32_t q = ring[j].c[b / 2][2 * (b % 2) + w];
+          const bf16x2_t wv[4] = {__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, 1.0f, 0),
+                                  __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, 1.0f, 1),
+                                  __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, 1.0f, 2),
+                                  __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, 1.0f, 3)};
+#pragma unroll
+          for (int sel = 0; sel < 4; ++sel)
+            sum = __builtin_amdgcn_fdot2_f32_bf16(
+                wv[sel], __builtin_bit_cast(bf16x2_t, a2[(2 * b + w) * 4 + sel]), sum, false);
+        }
+        acc = __builtin_fmaf(sum, sb, acc);
+      }
+      gv_load_row<W2D, NB>(p, buf, row + D * g, lane, ring[j]);
+      const float t = wave_sum(acc);
+      if (lane == 0 && row < p.n) ntstore_u16(p.y + row, f32_to_bf16_rne(t * alpha));
+    }
+  }
+}
+
 // Any K: one workgroup of 16 waves per band; wave w takes windows w, w + 16, ..., loading W and
 // A for up to kW16Chunk of them at a time (A comes from L2: it is at most 16 rows).
 constexpr int kW16Chunk = 4;
@@ -1298,7 +1429,7 @@ __global__ __launch_bounds__(kDecWaves * 64) void k_gemm_w4a16_stream(SmallMArgs
   if (wave < 4 && i16 < p.m) {
     float t = 0.0f;
 #pragma unroll
-    for (int w2 = 0; w2 < kDecWaves; ++w2) t += s_red[w2][lane][wave];
+    for (int w2 = 0; w2 < kDecWaves; ++w2) t += ((const float *)&s_red[w2][lane])[wave];
     const int64_t n = band * 16 + 4 * q + wave;
     if (n < p.n) ntstore_u16(p.y + (int64_t)i16 * p.ld_y + n, f32_to_bf16_rne(t * (*p.w.gs)));
   }
@@ -1407,6 +1538,39 @@ static void launch_w4a16_t(const SmallMArgs &p, bool w2d, hipStream_t stream) {
     hipLaunchKernelGGL((k_gemm_w4a16_decode<false, FULL, WIN>), grid, block, 0, stream, p);
 }
 
+// The GEMV form: m == 1, N >= 8192, K = 1024 * NB (NB 2, 4 or 8), W's scale rows aligned to
+// NB bytes, and the buffer offsets of W under 2 GiB.
+static int gemv_nb(const SmallMArgs &p) {
+  const int64_t nb = p.k / 1024;
+  if (p.m != 1 || p.n < 8192 || p.k % 1024 || (nb != 2 && nb != 4 && nb != 8)) return 0;
+  if ((uintptr_t)p.w.scales % nb || p.w.ld_scales % nb) return 0;
+  const int64_t srows = p.w.block_rows == 16 ? (p.n + 15) / 16 : p.n;
+  const int64_t lim = (int64_t)1 << 31;
+  if ((p.n - 1) * p.w.ld_codes + p.k / 2 >= lim || (srows - 1) * p.w.ld_scales + p.k / 16 >= lim)
+    return 0;
+  return (int)nb;
+}
+
+static hipError_t launch_gemv_w4a16(const SmallMArgs &p, int nb, hipStream_t stream) {
+  static int cus = 0;
+  if (cus == 0 && hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, 0) != hipSuccess)
+    cus = 0;
+  const int64_t want = (p.n + kDecWaves - 1) / kDecWaves;
+  const int64_t slots = cus > 0 ? cus : 256;
+  const dim3 grid((unsigned)(want < slots ? want : slots)), block(kDecWaves * 64);
+  const bool w2d = p.w.block_rows == 16;
+#define NV_GEMV(NB)                                                                      \
+  if (nb == NB) {                                                                        \
+    if (w2d) hipLaunchKernelGGL((k_gemv_w4a16<true, NB>), grid, block, 0, stream, p);    \
+    else hipLaunchKernelGGL((k_gemv_w4a16<false, NB>), grid, block, 0, stream, p);       \
+  }
+  NV_GEMV(2)
+  NV_GEMV(4)
+  NV_GEMV(8)
+#undef NV_GEMV
+  return hipGetLastError();
+}
+
 hipError_t launch_gemm_decode_fused(const void *a_bf16, int64_t ld_a, const GemmOperand &aq,
                                     const GemmOperand &w, int64_t m, int64_t n, int64_t k,
                                     uint16_t *y, int64_t ld_y, hipStream_t stream) {
@@ -1445,6 +1609,7 @@ hipError_t launch_gemm_w4a16(const void *a_bf16, int64_t ld_a, const GemmOperand
   p.aq_codes = p.aq_scales = nullptr;
   p.aq_gs = nullptr;
   const bool w2d = w.block_rows == 16;
+  if (const int nb = gemv_nb(p)) return launch_gemv_w4a16(p, nb, stream);
   if ((k + 127) / 128 <= kDecWaves * kDecWin) {
     const bool full = decode_full(p);
     const bool one = (k + 127) / 128 <= kDecWaves;
@@ -1474,12 +1639,12 @@ hipError_t launch_gemm_small_m(const GemmOperand &a, const GemmOperand &w, int64
   p.ld_y = ld_y;
   p.scale_pairs = ((uintptr_t)a.scales % 2 == 0) && (a.ld_scales % 2 == 0) &&
                   ((uintptr_t)w.scales % 2 == 0) && (w.ld_scales % 2 == 0);
+  p.a_bf16 = nullptr;
+  p.ld_a = 0;
+  p.aq_codes = p.aq_scales = nullptr;
+  p.aq_gs = nullptr;
   const int64_t nbands = (n + 15) / 16;
   if ((k + 127) / 128 <= kDecWaves * kDecWin) {
-    p.a_bf16 = nullptr;
-    p.ld_a = 0;
-    p.aq_codes = p.aq_scales = nullptr;
-    p.aq_gs = nullptr;
     return launch_decode<false>(p, w.block_rows == 16, stream);
   }
   const unsigned grid = (unsigned)nbands;

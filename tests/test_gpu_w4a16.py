@@ -48,6 +48,40 @@ def test_shapes(nv, m, n, k, br):
     check_gemm(y, O.gemm64_w4a16(a, ow), what=f"w4a16 {m}x{n}x{k} b{br}")
 
 
+# A single activation row: with N >= 8192 and K = 2048, 4096 or 8192 the GEMV form runs (no
+# MFMA, no LDS reduction), otherwise the decode forms.
+@pytest.mark.parametrize("n,k,br", [(1000, 2048, 1), (4112, 4096, 16), (272, 8192, 16),
+                                    (48, 4096, 1), (18, 2048, 1), (8200, 2048, 1),
+                                    (8208, 4096, 16)])
+def test_single_row_shapes(nv, n, k, br):
+    rng = np.random.default_rng(n + k + br)
+    a = W.to_bf16_bits(W.normal_with_outliers(rng, 1, k, 0.01, 20.0))
+    w = W.to_bf16_bits(rng.standard_normal((n, k)) * 0.02)
+    wq, ow = quantized_w(nv, w, br, f"1x{n}x{k}")
+    y = nv.gemm_w4a16(dev_bf16(a), wq)
+    check_gemm(y, O.gemm64_w4a16(a, ow), what=f"w4a16 gemv 1x{n}x{k} b{br}")
+
+
+def test_single_row_long_k_sampled(nv):
+    """GEMV form with K = 8192 (8 blocks per lane) on 8192 x 8192 weights with 16x16 tiles:
+    W checked byte for byte on sampled bands, Y on their columns."""
+    rng = np.random.default_rng(77)
+    n = k = 8192
+    w = W.to_bf16_bits(rng.standard_normal((n, k)) * 0.02)
+    a = W.to_bf16_bits(W.normal_with_outliers(rng, 1, k, 0.01, 20.0))
+    wq = nv.quantize_2d(dev_bf16(w))
+    wc, ws, wg = host_q(wq)
+    gw = O.global_scale(float(np.max(np.abs(W.bf16_bits_to_float32(w)))))
+    assert np.float32(wg) == gw
+    bands = np.unique(np.concatenate([[0, 511], rng.choice(512, 20, replace=False)]))
+    rows = (bands[:, None] * 16 + np.arange(16)).ravel()
+    oc, os_ = O.encode_2d(w[rows], gw)
+    assert_codes_equal(wc[rows], oc, "W codes")
+    assert_codes_equal(ws[bands], os_, "W scales")
+    y = nv.gemm_w4a16(dev_bf16(a), wq)
+    check_gemm(y.cpu()[:, rows], O.gemm64_w4a16(a, (oc, os_, gw, 16)), what="w4a16 gemv 8192^2")
+
+
 def test_permutation_closed_form(nv):
     """A permutation weight (1D blocks) gives W_hat = 2688 gs_W P, so Y[m, i] must be
     RN_bf16(A[m, pi(i)] * 2688 gs_W): pins the operand order, nibble order and scale indexing."""

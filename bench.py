@@ -204,6 +204,21 @@ def extra_workloads(args, torch, np, nv, W, only):
                                 "note": "includes the MXFP4 quantization of A inside the call"}
         del a, wq, y
 
+    if not only or "mse" in only:
+        # Offline weight quantization with MSE-observer block scales (16x16 tiles) of the decode
+        # weight: 18 candidate scales per tile, so it is bound by vector ALU work, not HBM.
+        d = W.decode()
+        wdev = dev_bf16(torch, np, d["w"])
+        q = nv.empty_qtensor(14336, 4096, 16)
+        ws = nv.Workspace.get(nv.lib().nvfp4_quantize_workspace_bytes(14336, 4096), wdev.device)
+        ms = timed(lambda i: nv.quantize_mse(wdev, 16, out=q, ws=ws), max(5, steps // 5), warm,
+                   torch)
+        vals = 14336 * 4096
+        out["mse_quantize_2d"] = {"shape": [14336, 4096], "ms": ms, "bound": "alu",
+                                  "gvalues_per_s": vals / (ms * 1e-3) / 1e9,
+                                  "note": "offline; 18 candidate scales per 16x16 tile"}
+        del wdev, q
+
     if not only or "moe" in only:
         d = W.moe()
         experts, n = d["experts"], d["n"]

@@ -120,6 +120,22 @@ nvfp4_status nvfp4_quantize_1d(const void *x, int64_t rows, int64_t cols, int64_
 nvfp4_status nvfp4_quantize_2d(const void *w, int64_t rows, int64_t cols, int64_t ld_w,
                                const nvfp4_tensor *out, void *ws, size_t ws_bytes, void *stream);
 
+/* nvfp4_quantize_mse — offline weight quantization with MSE-observer block scales
+ * ("Accelerating large language models with NVFP4 quantization", section "NVFP4 robustness with
+ * scale-dependent variability": MSE-based observers as a calibration refinement).  Same
+ * arguments as nvfp4_quantize_1d / nvfp4_quantize_2d; out->block_rows (1 or 16) picks the block
+ * shape (rows % 16 == 0 for 16), and the result is an ordinary NVFP4 tensor.
+ * The global scale is the amax one (as above).  Each block takes, among the E4M3 codes
+ * c0 - 16 .. c0 + 1 around the amax-derived code c0 (clamped to 0 .. 126), the scale whose
+ * reconstruction has the least squared error, evaluated in fp32 in a fixed order:
+ *   d_i = RN(code value_i * sb * gs), e_i = RN(x_i - d_i), the 16 values of a row block summed
+ *   left to right as RN(e_i * e_i); a 16x16 tile combines its 16 row errors pairwise (row r
+ *   with r ^ 1, then ^ 2, ^ 4, ^ 8).
+ * Ties go to the code nearest c0, then the smaller code.  Elements are encoded as by the
+ * quantizer under the chosen scale.  Codes need 8-byte alignment here (ld_codes % 8 == 0). */
+nvfp4_status nvfp4_quantize_mse(const void *w, int64_t rows, int64_t cols, int64_t ld_w,
+                                const nvfp4_tensor *out, void *ws, size_t ws_bytes, void *stream);
+
 /* nvfp4_dequantize — reconstruction ("NVFP4 Explained", section "How NVFP4 Represents a
  * Value"): y = RN_fp32(code value x block scale x global scale); NVFP4_OUT_BF16 rounds that
  * float to bf16 (nearest, ties to even).

@@ -179,6 +179,23 @@ nvfp4_status nvfp4_quantize_2d(const void *w, int64_t rows, int64_t cols, int64_
                                     (hipStream_t)stream));
 }
 
+nvfp4_status nvfp4_quantize_mse(const void *w, int64_t rows, int64_t cols, int64_t ld_w,
+                                const nvfp4_tensor *out, void *ws, size_t ws_bytes, void *stream) {
+  if (!out) return NVFP4_ERR_NULL;
+  if (rows == 0 && cols > 0 && cols % 16 == 0) return NVFP4_OK;  // nothing to compute or write
+  nvfp4_status s = check_bf16_input(w, rows, cols, ld_w);
+  if (s) return s;
+  s = check_tensor(out, rows, cols, false);
+  if (s) return s;
+  if (!aligned(out->codes, 8) || out->ld_codes % 8) return NVFP4_ERR_ALIGN;
+  if (!ws) return NVFP4_ERR_WORKSPACE;
+  if (ws_bytes < nvfp4_quantize_workspace_bytes(rows, cols) || !aligned(ws, kAlign))
+    return NVFP4_ERR_WORKSPACE;
+  return hip_status(launch_quantize_mse(w, rows, cols, ld_w, out->block_rows == 16, out->codes,
+                                        out->ld_codes, out->scales, out->ld_scales,
+                                        out->global_scale, ws, (hipStream_t)stream));
+}
+
 nvfp4_status nvfp4_dequantize(const nvfp4_tensor *q, void *y, int64_t ld_y, int out_dtype,
                               void *stream) {
   if (!q) return NVFP4_ERR_NULL;

@@ -61,6 +61,11 @@ hipError_t launch_grouped_gemm(const GemmOperand &a, const int32_t *row_index,
                                int64_t w_group_rows, int64_t n, int64_t k, int64_t total_rows,
                                uint16_t *y, int64_t ld_y, hipStream_t stream);
 
+// MSE-observer block scales (mse.hip): amax pass, then a per-block search over 18 candidate
+// scales; two_d selects 16x16 tiles.
+hipError_t launch_quantize_mse(const void *x, int64_t rows, int64_t cols, int64_t ld_x, bool two_d,
+                               uint8_t *codes, int64_t ld_codes, uint8_t *scales,
+                               int64_t ld_scales, float *gs_out, void *ws, hipStream_t stream);
 // MXFP4 (mxfp4.hip): quantize (one pass), dequantize, and the product on the scaled FP4 MFMA.
 hipError_t launch_mx_quantize(const void *x, int64_t rows, int64_t cols, int64_t ld_x,
                               uint8_t *codes, int64_t ld_codes, uint8_t *scales, int64_t ld_scales,

@@ -27,7 +27,7 @@ EXPORTED = (
     "nvfp4_gemm_workspace_bytes", "nvfp4_grouped_gemm_workspace_bytes", "nvfp4_quantize_1d",
     "nvfp4_quantize_2d", "nvfp4_dequantize", "nvfp4_gemm_w4a4", "nvfp4_grouped_gemm_w4a4",
     "nvfp4_gemm_w4a16", "nvfp4_mxfp4_quantize", "nvfp4_mxfp4_dequantize",
-    "nvfp4_mxfp4_gemm_workspace_bytes", "nvfp4_mxfp4_gemm",
+    "nvfp4_mxfp4_gemm_workspace_bytes", "nvfp4_mxfp4_gemm", "nvfp4_quantize_mse",
 )
 
 
@@ -63,6 +63,8 @@ _lib.nvfp4_grouped_gemm_workspace_bytes.argtypes = [_i64, _i64, _i64, _i32]
 for _name in ("nvfp4_quantize_1d", "nvfp4_quantize_2d"):
     getattr(_lib, _name).restype = ctypes.c_int
     getattr(_lib, _name).argtypes = [_vp, _i64, _i64, _i64, _pt, _vp, _sz, _vp]
+_lib.nvfp4_quantize_mse.restype = ctypes.c_int
+_lib.nvfp4_quantize_mse.argtypes = [_vp, _i64, _i64, _i64, _pt, _vp, _sz, _vp]
 _lib.nvfp4_dequantize.restype = ctypes.c_int
 _lib.nvfp4_dequantize.argtypes = [_pt, _vp, _i64, ctypes.c_int, _vp]
 _lib.nvfp4_gemm_w4a4.restype = ctypes.c_int
@@ -185,6 +187,20 @@ def quantize_2d(w, out=None, ws=None):
     ct = out.c()
     _check(_lib.nvfp4_quantize_2d(_ptr(w), rows, cols, w.stride(0), ctypes.byref(ct), _ptr(ws),
                                   ws.numel(), _stream(w.device)), "nvfp4_quantize_2d")
+    return out
+
+
+def quantize_mse(w, block_rows=16, out=None, ws=None):
+    """Offline NVFP4 weight quantization with MSE-observer block scales (1D blocks or 16x16
+    tiles); the result is an ordinary QTensor."""
+    assert w.dtype == torch.bfloat16 and w.dim() == 2 and w.stride(1) == 1
+    rows, cols = w.shape
+    if out is None:
+        out = empty_qtensor(rows, cols, block_rows, w.device)
+    ws = _ws(_lib.nvfp4_quantize_workspace_bytes(rows, cols), w.device, ws)
+    ct = out.c()
+    _check(_lib.nvfp4_quantize_mse(_ptr(w), rows, cols, w.stride(0), ctypes.byref(ct), _ptr(ws),
+                                   ws.numel(), _stream(w.device)), "nvfp4_quantize_mse")
     return out
 
 

@@ -62,12 +62,14 @@ def _tile_tree(row_err):
     return s[..., 0]
 
 
-def mse_scale_codes(x_bf16_bits, block_rows=1):
+def mse_scale_codes(x_bf16_bits, block_rows=1, gs=None):
     """Block-scale codes chosen by the MSE observer, and the global scale.
-    x: R x C bf16 bits; block_rows 1 (16-value row blocks) or 16 (16x16 tiles)."""
+    x: R x C bf16 bits; block_rows 1 (16-value row blocks) or 16 (16x16 tiles).  gs defaults to
+    the tensor's own (R1); passing it lets a subset of rows (whole tiles) be checked alone."""
     x = O._as_f64(x_bf16_bits)
     R, C = x.shape
-    gs = O.global_scale(O.global_amax(x))
+    if gs is None:
+        gs = O.global_scale(O.global_amax(x))
     x32 = x.astype(np.float32)                                      # exact: x is bf16
     if block_rows == 1:
         xb = x.reshape(R, C // 16, 16)
@@ -97,10 +99,10 @@ def mse_scale_codes(x_bf16_bits, block_rows=1):
     return best_c.astype(np.uint8), gs
 
 
-def quantize_mse(x_bf16_bits, block_rows=1):
+def quantize_mse(x_bf16_bits, block_rows=1, gs=None):
     """NVFP4 quantization with MSE-observer block scales: returns (codes, scales, gs) in the
     same layout as quantize_1d (block_rows 1) or quantize_2d (block_rows 16)."""
-    sc, gs = mse_scale_codes(x_bf16_bits, block_rows)
+    sc, gs = mse_scale_codes(x_bf16_bits, block_rows, gs)
     x = O._as_f64(x_bf16_bits)
     sbv = O.E4M3_POS[sc]
     if block_rows == 1:

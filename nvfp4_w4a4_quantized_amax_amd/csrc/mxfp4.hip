@@ -281,6 +281,232 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     }
 }
 
+// Wide-window pipeline (K a multiple of 512; 16-byte aligned scale rows; operands addressable
+// with 32-bit offsets).  A window is 256 K values: 128 code bytes per row, so the 16-byte loads
+// of 8 adjacent lanes cover one whole 128-byte line and each row is fetched once per window.
+// Scale bytes travel 16 per row (two windows) per load.  The codes of a row sit in LDS as 8
+// chunks of 16 bytes, chunk c at slot c ^ wide_swizzle(row): the fragment reads (one chunk of 8
+// or 16 consecutive rows at a time) and the window stores (8 whole rows per wave) then touch
+// every bank once.  The scale bytes of a row and window, b0..b7 (block j covers K values
+// 32j .. 32j + 31 of the window), are stored as the word b0 b2 b4 b6 followed by b1 b3 b5 b7:
+// the lane that feeds K half kh of every 64-wide step reads word kh once per window, and the
+// MFMA picks byte s of it for step s through its operand select.
+//
+// Per window each wave issues 64 MFMAs in four 64-wide steps; the fragments of step s + 1 are
+// read from LDS while step s runs.  During step 0 the registers holding window w + 1 are stored
+// to the free LDS stage and refilled with window w + 2, one store and one load per MFMA; one
+// barrier per window, before step 3, publishes window w + 1.  Rows past the end of A or W are
+// read with offsets beyond the buffer, which the hardware answers with zeros and no memory
+// access.  (Compared with the 64-wide window, this quarters the cache lines fetched per flop:
+// there every window touched each row's line for 32 code bytes and 2 scale bytes.)
+constexpr int kMxWideK = 256;
+
+struct MxWideStage {
+  uint8_t a[256 * 128];
+  uint8_t w[256 * 128];
+  uint32_t as[256 * 2];
+  uint32_t ws[256 * 2];
+};
+
+__device__ __forceinline__ int wide_swizzle(int row) { return ((row >> 1) & 7) ^ ((row & 1) << 2); }
+
+struct MxWideRegs {
+  u32x4_t a[8], w[8];
+};
+
+struct MxWideFrags {
+  u32x4_t a[4], w[4];
+};
+
+template <int S>
+__device__ __forceinline__ floatx16_t mx_mfma_sel(const u32x4_t &a, const u32x4_t &w, uint32_t sa,
+                                                  uint32_t sw, const floatx16_t &c) {
+  const i32x8_t av = __builtin_shufflevector((i32x4_t)a, (i32x4_t)a, 0, 1, 2, 3, -1, -1, -1, -1);
+  const i32x8_t wv = __builtin_shufflevector((i32x4_t)w, (i32x4_t)w, 0, 1, 2, 3, -1, -1, -1, -1);
+  // both operands FP4; byte S of each scale word
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, wv, c, 4, 4, S, (int)sa, S, (int)sw);
+}
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_gemm_mx_wide(MxArgs p) {
+  __shared__ __align__(16) MxWideStage st[2];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int lr = lane & 31, kh = lane >> 5;
+  int tm, tn;
+  tile_of(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, tm, tn);
+  const uint32_t m_tile = (uint32_t)tm * 256, n_tile = (uint32_t)tn * 256;
+
+  const __amdgpu_buffer_rsrc_t bac = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)p.a_codes, 0, (int)((p.m - 1) * p.ld_ac + p.k / 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t bwc = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)p.w_codes, 0, (int)((p.n - 1) * p.ld_wc + p.k / 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t bas = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)p.a_scales, 0, (int)((p.m - 1) * p.ld_as + p.k / 32), 0x00020000);
+  const __amdgpu_buffer_rsrc_t bws = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)p.w_scales, 0, (int)((p.n - 1) * p.ld_ws + p.k / 32), 0x00020000);
+
+  // Chunk i of this thread's share of a window: row i * 32 + tid / 8, 16-byte part tid % 8.
+  const uint32_t lrow = (uint32_t)tid >> 3, part = (uint32_t)tid & 7;
+  const uint32_t ga0 = (m_tile + lrow) * (uint32_t)p.ld_ac + part * 16;
+  const uint32_t gw0 = (n_tile + lrow) * (uint32_t)p.ld_wc + part * 16;
+  const uint32_t ga_step = 32 * (uint32_t)p.ld_ac, gw_step = 32 * (uint32_t)p.ld_wc;
+  const uint32_t gas0 = (m_tile + tid) * (uint32_t)p.ld_as;
+  const uint32_t gws0 = (n_tile + tid) * (uint32_t)p.ld_ws;
+  const int st_code = lrow * 128 + ((part ^ wide_swizzle(lrow)) << 4);
+  // Fragment f of A is row wm * 128 + f * 32 + lr; its swizzle depends on lr only.
+  const int sz = wide_swizzle(lr);
+  const int fa_row = (wm * 128 + lr) * 128, fw_row = (wn * 128 + lr) * 128;
+  const int nwin = (int)(p.k / kMxWideK);  // even, >= 2
+
+  floatx16_t acc[4][4];
+#pragma unroll
+  for (int f = 0; f < 4; ++f)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) acc[f][g] = floatx16_t{};
+
+  MxWideRegs r;
+  u32x4_t sa_pair, sw_pair;  // scale bytes of two windows, this thread's A row and W row
+  auto load_codes = [&](int win) {
+    const uint32_t o = (uint32_t)win * 128;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      r.a[i] = __builtin_amdgcn_raw_buffer_load_b128(bac, (int)(ga0 + i * ga_step + o), 0, 0);
+      r.w[i] = __builtin_amdgcn_raw_buffer_load_b128(bwc, (int)(gw0 + i * gw_step + o), 0, 0);
+    }
+  };
+  auto load_scales = [&](int win) {  // win even: windows win and win + 1
+    sa_pair = __builtin_amdgcn_raw_buffer_load_b128(bas, (int)(gas0 + (uint32_t)win * 8), 0, 0);
+    sw_pair = __builtin_amdgcn_raw_buffer_load_b128(bws, (int)(gws0 + (uint32_t)win * 8), 0, 0);
+  };
+  auto store_codes = [&](MxWideStage &S) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      *(u32x4_t *)(S.a + st_code + i * 4096) = r.a[i];
+      *(u32x4_t *)(S.w + st_code + i * 4096) = r.w[i];
+    }
+  };
+  auto store_scales = [&](MxWideStage &S, int odd) {
+    const uint32_t alo = odd ? sa_pair[2] : sa_pair[0], ahi = odd ? sa_pair[3] : sa_pair[1];
+    const uint32_t wlo = odd ? sw_pair[2] : sw_pair[0], whi = odd ? sw_pair[3] : sw_pair[1];
+    typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
+    *(u32x2_t *)(S.as + tid * 2) = u32x2_t{__builtin_amdgcn_perm(ahi, alo, 0x06040200u),
+                                           __builtin_amdgcn_perm(ahi, alo, 0x07050301u)};
+    *(u32x2_t *)(S.ws + tid * 2) = u32x2_t{__builtin_amdgcn_perm(whi, wlo, 0x06040200u),
+                                           __builtin_amdgcn_perm(whi, wlo, 0x07050301u)};
+  };
+  auto read_frags = [&](const MxWideStage &S, int s, MxWideFrags &fr) {
+    const int o = ((2 * s + kh) ^ sz) << 4;
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+      fr.a[f] = *(const u32x4_t *)(S.a + fa_row + f * 4096 + o);
+      fr.w[f] = *(const u32x4_t *)(S.w + fw_row + f * 4096 + o);
+    }
+  };
+  uint32_t sa[4], sw[4];  // scale words of the current window, per fragment
+  auto read_scales = [&](const MxWideStage &S, uint32_t (&a)[4], uint32_t (&b)[4]) {
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+      a[f] = S.as[(wm * 128 + f * 32 + lr) * 2 + kh];
+      b[f] = S.ws[(wn * 128 + f * 32 + lr) * 2 + kh];
+    }
+  };
+
+  // Prologue: window 0 to stage 0, window 1 in registers.
+  load_scales(0);
+  load_codes(0);
+  store_codes(st[0]);
+  store_scales(st[0], 0);
+  load_codes(1);
+  lds_barrier();
+  MxWideFrags fx, fy;
+  read_frags(st[0], 0, fx);
+  read_scales(st[0], sa, sw);
+
+  // One window: stage `cur` holds window w, registers hold window w + 1 (and the scale pair of
+  // windows w and w + 1 if w is even, else of w + 1 and w + 2 ... loaded at the right time).
+  auto window = [&](int w, MxWideStage &cur, MxWideStage &nxt, int odd) {
+    uint32_t na[4], nb[4];
+    // step 0: store window w + 1, issue the loads of window w + 2 (and its scale pair)
+    store_codes(nxt);
+    store_scales(nxt, !odd);
+    const int w2 = min(w + 2, nwin - 1);
+    if (!odd) load_scales(w2 & ~1);
+    load_codes(w2);
+    read_frags(cur, 1, fy);
+#pragma unroll
+    for (int f = 0; f < 4; ++f)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) acc[f][g] = mx_mfma_sel<0>(fx.a[f], fx.w[g], sa[f], sw[g], acc[f][g]);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // LDS write
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // vector memory read
+      if (i < 8) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    read_frags(cur, 2, fx);
+#pragma unroll
+    for (int f = 0; f < 4; ++f)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) acc[f][g] = mx_mfma_sel<1>(fy.a[f], fy.w[g], sa[f], sw[g], acc[f][g]);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (i < 8) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    read_frags(cur, 3, fy);
+#pragma unroll
+    for (int f = 0; f < 4; ++f)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) acc[f][g] = mx_mfma_sel<2>(fx.a[f], fx.w[g], sa[f], sw[g], acc[f][g]);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (i < 8) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    lds_barrier();
+    read_frags(nxt, 0, fx);
+    read_scales(nxt, na, nb);
+#pragma unroll
+    for (int f = 0; f < 4; ++f)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) acc[f][g] = mx_mfma_sel<3>(fy.a[f], fy.w[g], sa[f], sw[g], acc[f][g]);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (i < 8) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+      sa[f] = na[f];
+      sw[f] = nb[f];
+    }
+  };
+  for (int w = 0; w < nwin; w += 2) {
+    window(w, st[0], st[1], 0);
+    window(w + 1, st[1], st[0], 1);
+  }
+
+  const int64_t m0 = m_tile + wm * 128, n0 = n_tile + wn * 128;
+  const bool full = m_tile + 256 <= p.m && n_tile + 256 <= p.n;
+#pragma unroll
+  for (int f = 0; f < 4; ++f)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int64_t col = n0 + g * 32 + lr;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int64_t row = m0 + f * 32 + 8 * (i >> 2) + 4 * kh + (i & 3);
+        if (full || (row < p.m && col < p.n))
+          ntstore_u16(p.y + row * p.ld_y + col, f32_to_bf16_rne(acc[f][g][i]));
+      }
+    }
+}
+
 // Any shape (K a multiple of 32): each wave computes one 32 x 32 tile straight from memory, one
 // 64-wide K window at a time; a missing second block of the last window reads as zero codes.
 __global__ __launch_bounds__(256) void k_gemm_mx_simple(MxArgs p) {
@@ -361,6 +587,16 @@ hipError_t launch_mx_gemm(const uint8_t *a_codes, int64_t ld_ac, const uint8_t *
   if (pipelined) {
     p.tiles_m = (int)((m + 255) / 256);
     p.tiles_n = (int)((n + 255) / 256);
+    const int64_t lim = (int64_t)1 << 31;
+    const bool wide = k % 512 == 0 && (uintptr_t)a_scales % 16 == 0 &&
+                      (uintptr_t)w_scales % 16 == 0 && ld_as % 16 == 0 && ld_ws % 16 == 0 &&
+                      (int64_t)p.tiles_m * 256 * ld_ac < lim && (int64_t)p.tiles_n * 256 * ld_wc < lim &&
+                      (int64_t)p.tiles_m * 256 * ld_as < lim && (int64_t)p.tiles_n * 256 * ld_ws < lim;
+    if (wide) {
+      hipLaunchKernelGGL(k_gemm_mx_wide, dim3((unsigned)p.tiles_m * (unsigned)p.tiles_n),
+                         dim3(256), 0, stream, p);
+      return hipGetLastError();
+    }
     hipLaunchKernelGGL(k_gemm_mx_lds, dim3((unsigned)p.tiles_m * (unsigned)p.tiles_n), dim3(256),
                        0, stream, p);
     return hipGetLastError();

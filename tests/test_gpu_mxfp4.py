@@ -109,11 +109,14 @@ def test_dequantize(nv, dtype):
         assert np.array_equal(y.cpu().view(torch.int16).numpy().view(np.uint16), want)
 
 
-# The pipelined kernel takes M > 128 with K a multiple of 64; the rest (small M, K = 32 mod 64)
-# the direct one.  Ragged M and N, one window, and K with an odd window count appear.
+# M > 128 takes a pipelined kernel: the wide-window one when K is a multiple of 512 (one and
+# three window pairs appear; 4100 x 4200 has more tiles than workgroups, so workgroups carry the
+# pipeline from one ragged tile into the next), else the 64-wide one (one window, an odd window
+# count); the rest (small M, K = 32 mod 64) the direct one.  Ragged M and N appear on every path.
 @pytest.mark.parametrize("m,n,k", [
     (1, 64, 64), (7, 96, 160), (16, 200, 2048), (129, 256, 64), (300, 512, 2048),
-    (513, 1000, 4096), (256, 256, 192), (260, 300, 96),
+    (513, 1000, 4096), (256, 256, 192), (260, 300, 96), (300, 512, 512), (257, 384, 1536),
+    (640, 272, 1024), (4100, 4200, 512),
 ])
 def test_gemm_shapes(nv, m, n, k):
     rng = np.random.default_rng(m * 7 + n * 3 + k)
@@ -130,6 +133,23 @@ def test_gemm_shapes(nv, m, n, k):
     # the prequantized form gives the same bits
     y2 = nv.mxfp4_gemm(aq, wq)
     assert torch.equal(y, y2)
+
+
+def test_gemm_unaligned_scale_rows(nv):
+    """Scale rows 20 bytes apart (not 16-byte aligned) with K = 512: the 64-wide kernel takes
+    the product, and it matches the wide kernel's on the same operands."""
+    m, n, k = 384, 256, 512
+    rng = np.random.default_rng(21)
+    a = W.to_bf16_bits(W.normal_with_outliers(rng, m, k, 0.01, 20.0))
+    w = W.to_bf16_bits(rng.standard_normal((n, k)) * 0.02)
+    wq, ow = check_quantize(nv, w, "W")
+    aq, oa = check_quantize(nv, a, "A")
+    pad = nv.MxTensor(aq.codes, torch.zeros((m, 20), dtype=torch.uint8, device="cuda"), m, k)
+    pad.scales[:, :16] = aq.packed_scales()
+    y_pad = nv.mxfp4_gemm(pad, wq)
+    y = nv.mxfp4_gemm(aq, wq)
+    check_gemm(y_pad, MX.gemm64_mx(oa, ow), what="mxfp4 unaligned scales")
+    assert torch.equal(y, y_pad)
 
 
 def test_gemm_permutation_closed_form(nv):

@@ -202,12 +202,6 @@ __device__ __forceinline__ bool multiplier_ok_at(float k, double S, int i) {
   return fast_code(below, k) <= (uint32_t)i && fast_code(above, k) >= (uint32_t)i + 1u;
 }
 
-__device__ __noinline__ bool multiplier_is_exact(float k, double S) {
-  for (int i = 0; i < 7; ++i)
-    if (!multiplier_ok_at(k, S, i)) return false;
-  return true;
-}
-
 // Block-scale threshold for code s (1..126): bamax / (6 gs) is rounded to the nearest E4M3 code,
 // ties to even, so code s is reached when bamax >= mu * 6 * gs (s even) or > it (s odd), mu being
 // the midpoint between codes s-1 and s; mu * 6 * gs has <= 5 + 2 + 24 bits: exact in double.
@@ -231,8 +225,10 @@ __device__ __forceinline__ uint32_t scale_threshold(int s, double gsd) {
 //
 // Threads 0..127 (two whole waves) each write one entry.  Both waves run the 8 x 7 multiplier
 // checks themselves (lane 7m + i checks mantissa m at E2M1 midpoint i), combine them with a
-// ballot, repair a failing mantissa in the wave (rare) and pass the base multipliers around
-// with shuffles, so nothing has to meet in LDS before the entries are written.
+// ballot and pass the base multipliers around with shuffles, so nothing has to meet in LDS
+// before the entries are written.  When a mantissa's rounded reciprocal fails somewhere (about
+// one mantissa in six), its neighbouring floats are checked the same way, one midpoint per
+// lane, so the repair costs two more checks rather than up to fourteen in a row.
 __device__ inline void build_tables(QuantTables &t, float gs) {
   const int tid = threadIdx.x;
   const double gsd = (double)gs;
@@ -245,12 +241,15 @@ __device__ inline void build_tables(QuantTables &t, float gs) {
     float kb = checker ? (float)(1.0 / S) : 0.0f;
     const bool ok = checker ? multiplier_ok_at(kb, S, i) : true;
     const unsigned long long bad = __ballot(!ok);
-    if (checker && i == 0 && ((bad >> (7 * m)) & 0x7Full)) {
-      // The rounded reciprocal fails somewhere: try the neighbouring floats, else take the exact
-      // path (negative multiplier).
+    if (bad) {  // uniform: the ballot is the same in every lane
+      // The rounded reciprocal of some mantissa fails somewhere: try the float above it, then
+      // the one below, else take the exact path (negative multiplier).
       const float ku = __uint_as_float(__float_as_uint(kb) + 1u);
       const float kd = __uint_as_float(__float_as_uint(kb) - 1u);
-      kb = multiplier_is_exact(ku, S) ? ku : (multiplier_is_exact(kd, S) ? kd : -kb);
+      const unsigned long long bad_u = __ballot(checker && !multiplier_ok_at(ku, S, i));
+      const unsigned long long bad_d = __ballot(checker && !multiplier_ok_at(kd, S, i));
+      const unsigned long long mine = 0x7Full << (7 * m);
+      if (checker && (bad & mine)) kb = !(bad_u & mine) ? ku : (!(bad_d & mine) ? kd : -kb);
     }
     // Multiplier of block-scale code c: its mantissa's base multiplier (held by lane 7m) scaled
     // by 2^-exponent; 0 outside 1..126.

@@ -14,6 +14,8 @@
 // lane loads 16 contiguous bytes (32 codes, two scale blocks) of one row per 64-wide K window
 // straight into registers and feeds them to four K=16 MFMAs; A and W use the same mapping.
 
+#include <mutex>
+
 #include "nvfp4_device.hpp"
 #include "gemm_common.hpp"
 #include "launch.hpp"
@@ -1489,13 +1491,26 @@ hipError_t launch_gemm_tile(const GemmOperand &a, const GemmOperand &w, int64_t 
   return hipGetLastError();
 }
 
+// CU count of the current device, queried once per device (256 if the query fails).
+static int device_cus() {
+  static std::mutex mu;
+  static int cache[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  std::lock_guard<std::mutex> lock(mu);
+  if (cache[dev] == 0) {
+    int c = 0;
+    if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0)
+      c = 256;
+    cache[dev] = c;
+  }
+  return cache[dev];
+}
+
 // One workgroup per CU, each taking the same number of 16-row bands.
 static unsigned decode_grid(int64_t n) {
-  static int cus = 0;
-  if (cus == 0 && hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, 0) != hipSuccess)
-    cus = 0;
   const int64_t nbands = (n + 15) / 16;
-  const int64_t slots = cus > 0 ? cus : 256;
+  const int64_t slots = device_cus();
   const int64_t per_wg = (nbands + slots - 1) / slots;
   return (unsigned)((nbands + per_wg - 1) / per_wg);
 }
@@ -1552,11 +1567,8 @@ static int gemv_nb(const SmallMArgs &p) {
 }
 
 static hipError_t launch_gemv_w4a16(const SmallMArgs &p, int nb, hipStream_t stream) {
-  static int cus = 0;
-  if (cus == 0 && hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, 0) != hipSuccess)
-    cus = 0;
   const int64_t want = (p.n + kDecWaves - 1) / kDecWaves;
-  const int64_t slots = cus > 0 ? cus : 256;
+  const int64_t slots = device_cus();
   const dim3 grid((unsigned)(want < slots ? want : slots)), block(kDecWaves * 64);
   const bool w2d = p.w.block_rows == 16;
 #define NV_GEMV(NB)                                                                      \
@@ -1679,10 +1691,7 @@ hipError_t launch_grouped_gemm(const GemmOperand &a, const int32_t *row_index,
                          aligned4(w.scales) && w.ld_scales % 4 == 0;
   if (pipelined) {
     // Two 2-wave workgroups per CU walk the tile list.
-    static int cus = 0;
-    if (cus == 0 && hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, 0) != hipSuccess)
-      cus = 0;
-    const int64_t slots = 2 * (int64_t)(cus > 0 ? cus : 256);
+    const int64_t slots = 2 * (int64_t)device_cus();
     const unsigned g = (unsigned)(max_tiles < slots ? (max_tiles < 1 ? 1 : max_tiles) : slots);
     if (w.block_rows == 16)
       hipLaunchKernelGGL((k_gemm_grouped_lds<true>), dim3(g), dim3(128), 0, stream, p);

@@ -5,7 +5,10 @@
  * HIP device pointer; every call is asynchronous on `stream` (a hipStream_t passed as void*;
  * NULL means the default stream) and never synchronizes.  The caller owns every buffer; the
  * library allocates nothing per call and keeps no state between calls other than what is
- * written into the caller's workspace.
+ * written into the caller's workspace and a host counter that tags each call of the
+ * single-read quantizer.  Calls may be captured into a HIP graph and replayed: on a capturing
+ * stream the activation quantizer takes its two-kernel form (the single-read form's tag would
+ * be frozen into the graph), and no call records memset or copy operations.
  *
  * The format (sources cited by page title and section):
  *  - element: 4-bit E2M1 code, 1 sign / 2 exponent / 1 mantissa bit, magnitudes

@@ -506,8 +506,8 @@ hipError_t launch_quantize(const void *x, int64_t rows, int64_t cols, int64_t ld
 }
 
 // Persistent single-read launch (one workgroup per CU).  Returns hipErrorNotSupported, having
-// launched nothing, when the device cannot hold one such workgroup per CU or the path is turned
-// off, so the caller can use the two-kernel path.
+// launched nothing, when the device cannot hold one such workgroup per CU, the path is turned
+// off or the stream is being captured, so the caller can use the two-kernel path.
 // 16 waves per CU; each wave keeps RT tiles in registers (8 VGPRs each) and LT tiles in LDS
 // (16 waves x 4 x 2 KiB = 128 KiB).  An 8192 x 8192 bf16 tensor is 16 tiles per wave, so 12 of
 // them are read only once.  (Holding every tile needs 8 waves per CU, which leaves the encode
@@ -586,6 +586,16 @@ hipError_t launch_quantize_persistent(const void *x, int64_t rows, int64_t cols,
   const int fits = contig ? d.fits_contig : d.fits_strided;
   if (!d.enabled || d.cus <= 0 || fits < 1 || d.cus > kMaxPersistentSlots) return hipErrorNotSupported;
   if (d.cooperative_api && !d.coop) return hipErrorNotSupported;
+  // A stream being captured into a graph would freeze this call's epoch into the graph, and
+  // every replay after the first would find all slots already carrying it and pass the barrier
+  // on stale maxima: captured calls take the two-kernel path, which has no grid barrier.  (A
+  // failed query, which can leave an error behind, is treated the same way.)
+  hipStreamCaptureStatus capture = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(stream, &capture) != hipSuccess) {
+    (void)hipGetLastError();
+    return hipErrorNotSupported;
+  }
+  if (capture != hipStreamCaptureStatusNone) return hipErrorNotSupported;
   const uint32_t bpr = (uint32_t)(cols / 16);
   uint32_t n_blocks = (uint32_t)(rows * (cols / 16));
   FastDiv f = make_fastdiv(bpr);

@@ -204,10 +204,11 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_tile(DenseArgs p) {
     for (int g = 0; g < FN; ++g) {
       const int64_t col = n0 + g * 32 + lr;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
+      for (int r = 0; r < 16; r += 2) {  // rows r and r + 1 are adjacent
         const int64_t row = m0 + f * 32 + 8 * (r >> 2) + 4 * kh + (r & 3);
-        if (row < p.m && col < p.n)
-          ntstore_u16(p.y + row * p.ld_y + col, f32_to_bf16_rne(acc[f][g][r] * alpha));
+        const uint32_t pk = bf16x2_rne(acc[f][g][r] * alpha, acc[f][g][r + 1] * alpha);
+        if (row < p.m && col < p.n) ntstore_u16(p.y + row * p.ld_y + col, pk);
+        if (row + 1 < p.m && col < p.n) ntstore_u16(p.y + (row + 1) * p.ld_y + col, pk >> 16);
       }
     }
 }
@@ -447,10 +448,12 @@ __global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(1,
     for (int g = 0; g < 4; ++g) {
       const int64_t col = n0 + g * 32 + lr;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
+      for (int r = 0; r < 16; r += 2) {  // rows r and r + 1 are adjacent
         const int64_t row = m0 + f * 32 + 8 * (r >> 2) + 4 * kh + (r & 3);
-        if (full || (row < p.m && col < p.n))
-          ntstore_u16(p.y + row * p.ld_y + col, f32_to_bf16_rne(acc[f][g][r] * alpha));
+        const uint32_t pk = bf16x2_rne(acc[f][g][r] * alpha, acc[f][g][r + 1] * alpha);
+        if (full || (row < p.m && col < p.n)) ntstore_u16(p.y + row * p.ld_y + col, pk);
+        if (full || (row + 1 < p.m && col < p.n))
+          ntstore_u16(p.y + (row + 1) * p.ld_y + col, pk >> 16);
       }
     }
 }
@@ -570,10 +573,11 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_grouped(GroupedArgs p) {
       for (int g = 0; g < FN; ++g) {
         const int64_t col = n0 + g * 32 + lr;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
+        for (int r = 0; r < 16; r += 2) {  // rows r and r + 1 are adjacent
           const int64_t row = m0 + f * 32 + 8 * (r >> 2) + 4 * kh + (r & 3);
-          if (row < r_end && col < p.n)
-            ntstore_u16(p.y + row * p.ld_y + col, f32_to_bf16_rne(acc[f][g][r] * alpha));
+          const uint32_t pk = bf16x2_rne(acc[f][g][r] * alpha, acc[f][g][r + 1] * alpha);
+          if (row < r_end && col < p.n) ntstore_u16(p.y + row * p.ld_y + col, pk);
+          if (row + 1 < r_end && col < p.n) ntstore_u16(p.y + (row + 1) * p.ld_y + col, pk >> 16);
         }
       }
   }
@@ -776,10 +780,11 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       for (int g = 0; g < 4; ++g) {
         const int64_t col = n0 + g * 32 + lr;
 #pragma unroll
-        for (int r2 = 0; r2 < 16; ++r2) {
+        for (int r2 = 0; r2 < 16; r2 += 2) {  // rows r2 and r2 + 1 are adjacent
           const int64_t row = m_tile + f * 32 + 8 * (r2 >> 2) + 4 * kh + (r2 & 3);
-          if (row < r_end && col < p.n)
-            ntstore_u16(p.y + row * p.ld_y + col, f32_to_bf16_rne(acc[f][g][r2] * alpha));
+          const uint32_t pk = bf16x2_rne(acc[f][g][r2] * alpha, acc[f][g][r2 + 1] * alpha);
+          if (row < r_end && col < p.n) ntstore_u16(p.y + row * p.ld_y + col, pk);
+          if (row + 1 < r_end && col < p.n) ntstore_u16(p.y + (row + 1) * p.ld_y + col, pk >> 16);
         }
       }
   }

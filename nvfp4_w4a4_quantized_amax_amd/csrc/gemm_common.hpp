@@ -41,6 +41,16 @@ __device__ __forceinline__ int code_offset(int row, int h) {
   return row * 32 + ((h ^ (row >> 2) ^ (row >> 3)) & 1) * 16;
 }
 
+// Two floats to bf16, round to nearest even, in one packed conversion (v_cvt_pk_bf16_f32),
+// element 0 in the low half.  The kernels keep fp32 denormals, so this equals the bit-level
+// rounding (add 0x7FFF plus the kept lsb, shift) for every value that is not a NaN.
+__device__ __forceinline__ uint32_t bf16x2_rne(float lo, float hi) {
+  typedef float f32x2_v __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
+  const f32x2_v v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_v));
+}
+
 // Wait for this wave's LDS stores, then for every wave of the workgroup.  The asm's memory
 // clobber keeps the compiler from moving LDS accesses across it.
 __device__ __forceinline__ void lds_barrier() {

@@ -273,10 +273,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     for (int g = 0; g < 4; ++g) {
       const int64_t col = n0 + g * 32 + lr;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
+      for (int i = 0; i < 16; i += 2) {  // rows i and i + 1 are adjacent
         const int64_t row = m0 + f * 32 + 8 * (i >> 2) + 4 * kh + (i & 3);
-        if (full || (row < p.m && col < p.n))
-          ntstore_u16(p.y + row * p.ld_y + col, f32_to_bf16_rne(acc[f][g][i]));
+        const uint32_t pk = bf16x2_rne(acc[f][g][i], acc[f][g][i + 1]);
+        if (full || (row < p.m && col < p.n)) ntstore_u16(p.y + row * p.ld_y + col, pk);
+        if (full || (row + 1 < p.m && col < p.n))
+          ntstore_u16(p.y + (row + 1) * p.ld_y + col, pk >> 16);
       }
     }
 }
@@ -499,10 +501,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     for (int g = 0; g < 4; ++g) {
       const int64_t col = n0 + g * 32 + lr;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
+      for (int i = 0; i < 16; i += 2) {  // rows i and i + 1 are adjacent
         const int64_t row = m0 + f * 32 + 8 * (i >> 2) + 4 * kh + (i & 3);
-        if (full || (row < p.m && col < p.n))
-          ntstore_u16(p.y + row * p.ld_y + col, f32_to_bf16_rne(acc[f][g][i]));
+        const uint32_t pk = bf16x2_rne(acc[f][g][i], acc[f][g][i + 1]);
+        if (full || (row < p.m && col < p.n)) ntstore_u16(p.y + row * p.ld_y + col, pk);
+        if (full || (row + 1 < p.m && col < p.n))
+          ntstore_u16(p.y + (row + 1) * p.ld_y + col, pk >> 16);
       }
     }
 }

@@ -39,6 +39,13 @@ PackedLayout packed_layout(int64_t rows, int64_t k) {
 
 constexpr int64_t kSmallM = 16;
 
+// Workspace bytes for the split-K partial sums of the tiled product (after the packed A).
+size_t partial_bytes(int64_t m, int64_t n, int64_t k) {
+  if (m <= kSmallM || n <= 0) return 0;
+  const int splits = gemm_k_splits(m, n, k);
+  return splits > 1 ? round_up((size_t)splits * (size_t)m * (size_t)n * 4, kAlign) : 0;
+}
+
 // MXFP4 operand checks.
 nvfp4_status check_mx_tensor(const mxfp4_tensor *t, int64_t rows, int64_t cols) {
   if (!t) return NVFP4_ERR_NULL;
@@ -132,9 +139,8 @@ size_t nvfp4_quantize_workspace_bytes(int64_t rows, int64_t cols) {
 }
 
 size_t nvfp4_gemm_workspace_bytes(int64_t m, int64_t n, int64_t k) {
-  (void)n;
   if (m < 0 || k <= 0) return kWsHeaderBytes;
-  return packed_layout(m, k).end;
+  return packed_layout(m, k).end + partial_bytes(m, n, k);
 }
 
 size_t nvfp4_grouped_gemm_workspace_bytes(int64_t tokens, int64_t k, int64_t total_rows,
@@ -283,7 +289,8 @@ nvfp4_status nvfp4_gemm_w4a4(const void *a_bf16, int64_t m, int64_t k, int64_t l
   }
   if (m <= kSmallM)
     return hip_status(launch_gemm_small_m(A, W, m, n, k, (uint16_t *)y, ld_y, st));
-  return hip_status(launch_gemm_tile(A, W, m, n, k, (uint16_t *)y, ld_y, st));
+  float *part = partial_bytes(m, n, k) ? (float *)(base + L.end) : nullptr;
+  return hip_status(launch_gemm_tile(A, W, m, n, k, (uint16_t *)y, ld_y, part, st));
 }
 
 nvfp4_status nvfp4_gemm_w4a16(const void *a_bf16, int64_t m, int64_t k, int64_t ld_a,

@@ -157,7 +157,32 @@ struct DenseArgs {
   uint16_t *y;
   int64_t ld_y;
   int tiles_m, tiles_n;
+  // Split K (shapes with too few tiles to fill the device): workgroup (tile, blockIdx.y) covers
+  // 64-wide K windows [blockIdx.y * wps, (blockIdx.y + 1) * wps) and stores its unscaled fp32
+  // sums to part + blockIdx.y * m * n (row-major, m x n); k_splitk_reduce finishes Y.  part is
+  // NULL when K is not split.
+  float *part;
+  int64_t wps;
 };
+
+// fp32 partial sums of one wave tile (before the global scales) into this split's slab.
+template <int FM, int FN, class InRange>
+__device__ __forceinline__ void store_partial(const DenseArgs &p, const floatx16_t (&acc)[FM][FN],
+                                              int64_t m0, int64_t n0, int lr, int kh,
+                                              InRange in_range) {
+  float *dst = p.part + (int64_t)blockIdx.y * p.m * p.n;
+#pragma unroll
+  for (int f = 0; f < FM; ++f)
+#pragma unroll
+    for (int g = 0; g < FN; ++g) {
+      const int64_t col = n0 + g * 32 + lr;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t row = m0 + f * 32 + 8 * (r >> 2) + 4 * kh + (r & 3);
+        if (in_range(row, col)) dst[row * p.n + col] = acc[f][g][r];
+      }
+    }
+}
 
 
 template <int FM, int FN, bool W2D>
@@ -189,14 +214,34 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_tile(DenseArgs p) {
     w_row[g] = p.w.codes + r * p.w.ld_codes + kh * 16;
     w_srow[g] = p.w.scales + (W2D ? (r >> 4) : r) * p.w.ld_scales + kh * 2;
   }
+  int64_t kk = p.k;
+  if (p.part) {  // this split's K windows: move the row pointers to its first one
+    const int64_t w0 = (int64_t)blockIdx.y * p.wps;
+#pragma unroll
+    for (int f = 0; f < FM; ++f) {
+      a_row[f] += w0 * 32;
+      a_srow[f] += w0 * 4;
+    }
+#pragma unroll
+    for (int g = 0; g < FN; ++g) {
+      w_row[g] += w0 * 32;
+      w_srow[g] += w0 * 4;
+    }
+    kk = min(p.k - w0 * 64, p.wps * 64);
+  }
   floatx16_t acc[FM][FN];
 #pragma unroll
   for (int f = 0; f < FM; ++f)
 #pragma unroll
     for (int g = 0; g < FN; ++g) acc[f][g] = floatx16_t{};
 
-  wave_tile_kloop<FM, FN>(a_row, a_srow, w_row, w_srow, p.k, kh, acc);
+  wave_tile_kloop<FM, FN>(a_row, a_srow, w_row, w_srow, kk, kh, acc);
 
+  if (p.part) {
+    store_partial<FM, FN>(p, acc, m0, n0, lr, kh,
+                          [&](int64_t row, int64_t col) { return row < p.m && col < p.n; });
+    return;
+  }
   const float alpha = (*p.a.gs) * (*p.w.gs);
 #pragma unroll
   for (int f = 0; f < FM; ++f)
@@ -366,17 +411,19 @@ __global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(1,
 
   // This thread's share of every window's loads (rows clamped into the matrix; results of
   // clamped rows are never stored).
+  // With K split, this workgroup's windows start at w0 (the row pointers move there).
+  const int64_t w0 = p.part ? (int64_t)blockIdx.y * p.wps : 0;
   const uint8_t *ga[2], *gw[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int c = i * 256 + tid, row = c >> 1, half = c & 1;
-    ga[i] = p.a.codes + min(m_tile + row, p.m - 1) * p.a.ld_codes + half * 16;
-    gw[i] = p.w.codes + min(n_tile + row, p.n - 1) * p.w.ld_codes + half * 16;
+    ga[i] = p.a.codes + min(m_tile + row, p.m - 1) * p.a.ld_codes + half * 16 + w0 * 32;
+    gw[i] = p.w.codes + min(n_tile + row, p.n - 1) * p.w.ld_codes + half * 16 + w0 * 32;
   }
-  const uint8_t *gas = p.a.scales + min(m_tile + tid, p.m - 1) * p.a.ld_scales;
-  const uint8_t *gws = W2D ? p.w.scales + min(n_tile / 16 + (lane & 15), p.n / 16 - 1) * p.w.ld_scales
-                           : p.w.scales + min(n_tile + tid, p.n - 1) * p.w.ld_scales;
-  const int64_t nwin = p.k / 64;  // >= 1
+  const uint8_t *gas = p.a.scales + min(m_tile + tid, p.m - 1) * p.a.ld_scales + w0 * 4;
+  const uint8_t *gws = (W2D ? p.w.scales + min(n_tile / 16 + (lane & 15), p.n / 16 - 1) * p.w.ld_scales
+                            : p.w.scales + min(n_tile + tid, p.n - 1) * p.w.ld_scales) + w0 * 4;
+  const int64_t nwin = p.part ? min(p.wps, p.k / 64 - w0) : p.k / 64;  // >= 1
   // Window `win` is clamped to the last one so that the loop has no branch (a clamped load is
   // never stored).
   floatx16_t acc[4][4];
@@ -439,8 +486,13 @@ __global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(1,
   end_step(ev);
   mfma_step(od, acc);
 
-  const float alpha = (*p.a.gs) * (*p.w.gs);
   const int64_t m0 = m_tile + wm * 128, n0 = n_tile + wn * 128;
+  if (p.part) {
+    store_partial<4, 4>(p, acc, m0, n0, lr, kh,
+                        [&](int64_t row, int64_t col) { return row < p.m && col < p.n; });
+    return;
+  }
+  const float alpha = (*p.a.gs) * (*p.w.gs);
   const bool full = m_tile + 256 <= p.m && n_tile + 256 <= p.n;
 #pragma unroll
   for (int f = 0; f < 4; ++f)
@@ -1445,11 +1497,47 @@ __global__ __launch_bounds__(kDecWaves * 64) void k_gemm_w4a16_stream(SmallMArgs
 // ---------------------------------------------------------------------------------------------
 // Host launchers
 // ---------------------------------------------------------------------------------------------
+// Y = RN_bf16(gsA * gsW * sum over splits of the fp32 partials); four columns per thread
+// (n % 4 == 0), the splits added in order.
+__global__ __launch_bounds__(256) void k_splitk_reduce(const float *__restrict__ part, int splits,
+                                                       int64_t m, int64_t n,
+                                                       uint16_t *__restrict__ y, int64_t ld_y,
+                                                       const float *__restrict__ gsa,
+                                                       const float *__restrict__ gsw) {
+  const float alpha = (*gsa) * (*gsw);
+  const int64_t per_row = n / 4, total = m * per_row, slab = m * n;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * 256) {
+    const int64_t r = i / per_row, c = (i - r * per_row) * 4;
+    const float *src = part + r * n + c;
+    float4 s = *(const float4 *)src;
+    for (int t = 1; t < splits; ++t) {
+      const float4 v = *(const float4 *)(src + t * slab);
+      s.x += v.x;
+      s.y += v.y;
+      s.z += v.z;
+      s.w += v.w;
+    }
+    uint32_t *dst = (uint32_t *)(y + r * ld_y + c);  // ld_y and y are 2-element aligned
+    dst[0] = bf16x2_rne(s.x * alpha, s.y * alpha);
+    dst[1] = bf16x2_rne(s.z * alpha, s.w * alpha);
+  }
+}
+
+static hipError_t launch_splitk_reduce(const DenseArgs &p, int splits, hipStream_t stream) {
+  const int64_t total = p.m * (p.n / 4);
+  int64_t g = (total + 255) / 256;
+  g = g < 1 ? 1 : (g > 2048 ? 2048 : g);
+  hipLaunchKernelGGL(k_splitk_reduce, dim3((unsigned)g), dim3(256), 0, stream, p.part, splits,
+                     p.m, p.n, p.y, p.ld_y, p.a.gs, p.w.gs);
+  return hipGetLastError();
+}
+
 template <int FM, int FN>
 static hipError_t launch_tile_fm(const GemmOperand &a, const GemmOperand &w, int64_t m,
-                                 int64_t n, int64_t k, uint16_t *y, int64_t ld_y,
+                                 int64_t n, int64_t k, uint16_t *y, int64_t ld_y, float *part,
                                  hipStream_t stream) {
-  DenseArgs p;
+  DenseArgs p{};
   p.a = a;
   p.w = w;
   p.m = m;
@@ -1459,26 +1547,33 @@ static hipError_t launch_tile_fm(const GemmOperand &a, const GemmOperand &w, int
   p.ld_y = ld_y;
   p.tiles_m = (int)((m + 64 * FM - 1) / (64 * FM));
   p.tiles_n = (int)((n + 64 * FN - 1) / (64 * FN));
-  const unsigned grid = (unsigned)p.tiles_m * (unsigned)p.tiles_n;
+  const int splits = part ? gemm_k_splits(m, n, k) : 1;
+  if (splits > 1) {
+    p.part = part;
+    p.wps = ((k + 63) / 64 + splits - 1) / splits;  // splits * wps windows cover k, none empty
+  }
+  const dim3 grid((unsigned)p.tiles_m * (unsigned)p.tiles_n, (unsigned)splits);
   if (w.block_rows == 16)
-    hipLaunchKernelGGL((k_gemm_tile<FM, FN, true>), dim3(grid), dim3(kGemmThreads), 0, stream, p);
+    hipLaunchKernelGGL((k_gemm_tile<FM, FN, true>), grid, dim3(kGemmThreads), 0, stream, p);
   else
-    hipLaunchKernelGGL((k_gemm_tile<FM, FN, false>), dim3(grid), dim3(kGemmThreads), 0, stream,
-                       p);
-  return hipGetLastError();
+    hipLaunchKernelGGL((k_gemm_tile<FM, FN, false>), grid, dim3(kGemmThreads), 0, stream, p);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess || splits == 1) return e;
+  return launch_splitk_reduce(p, splits, stream);
 }
 
 static bool aligned4(const void *q) { return ((uintptr_t)q & 3u) == 0; }
 
 hipError_t launch_gemm_tile(const GemmOperand &a, const GemmOperand &w, int64_t m, int64_t n,
-                            int64_t k, uint16_t *y, int64_t ld_y, hipStream_t stream) {
-  if (m <= 64) return launch_tile_fm<1, 4>(a, w, m, n, k, y, ld_y, stream);
-  if (m <= 128) return launch_tile_fm<2, 4>(a, w, m, n, k, y, ld_y, stream);
+                            int64_t k, uint16_t *y, int64_t ld_y, float *part,
+                            hipStream_t stream) {
+  if (m <= 64) return launch_tile_fm<1, 4>(a, w, m, n, k, y, ld_y, part, stream);
+  if (m <= 128) return launch_tile_fm<2, 4>(a, w, m, n, k, y, ld_y, part, stream);
   // The pipelined kernel needs whole 64-wide K windows and 4-byte aligned scale rows.
   const bool lds_ok = (k % 64 == 0) && aligned4(a.scales) && aligned4(w.scales) &&
                       (a.ld_scales % 4 == 0) && (w.ld_scales % 4 == 0);
-  if (!lds_ok) return launch_tile_fm<4, 4>(a, w, m, n, k, y, ld_y, stream);
-  DenseArgs p;
+  if (!lds_ok) return launch_tile_fm<4, 4>(a, w, m, n, k, y, ld_y, part, stream);
+  DenseArgs p{};
   p.a = a;
   p.w = w;
   p.m = m;
@@ -1488,12 +1583,19 @@ hipError_t launch_gemm_tile(const GemmOperand &a, const GemmOperand &w, int64_t 
   p.ld_y = ld_y;
   p.tiles_m = (int)((m + 255) / 256);
   p.tiles_n = (int)((n + 255) / 256);
-  const unsigned grid = (unsigned)p.tiles_m * (unsigned)p.tiles_n;
+  const int splits = part ? gemm_k_splits(m, n, k) : 1;
+  if (splits > 1) {
+    p.part = part;
+    p.wps = (k / 64 + splits - 1) / splits;
+  }
+  const dim3 grid((unsigned)p.tiles_m * (unsigned)p.tiles_n, (unsigned)splits);
   if (w.block_rows == 16)
-    hipLaunchKernelGGL(k_gemm_lds<true>, dim3(grid), dim3(kGemmThreads), 0, stream, p);
+    hipLaunchKernelGGL(k_gemm_lds<true>, grid, dim3(kGemmThreads), 0, stream, p);
   else
-    hipLaunchKernelGGL(k_gemm_lds<false>, dim3(grid), dim3(kGemmThreads), 0, stream, p);
-  return hipGetLastError();
+    hipLaunchKernelGGL(k_gemm_lds<false>, grid, dim3(kGemmThreads), 0, stream, p);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess || splits == 1) return e;
+  return launch_splitk_reduce(p, splits, stream);
 }
 
 // CU count of the current device, queried once per device (256 if the query fails).

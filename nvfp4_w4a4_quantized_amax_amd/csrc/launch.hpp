@@ -40,8 +40,33 @@ struct GemmOperand {
   int block_rows;
 };
 
+// K splits of the tiled product (m > 16) of m x k by n x k: a shape whose tiles (64, 128 or
+// 256 rows by 256 columns, as the launcher picks them) would fill fewer than half of a 256-CU
+// device splits its 64-wide K windows so that tiles x splits is about 256, keeping at least 4
+// windows per split and the fp32 partial sums (splits x m x n x 4 bytes) no larger than W's
+// packed codes (n x k / 2 bytes).  Depends on the shape only, so the workspace size does too.
+// 1 = no split.
+inline int gemm_k_splits(int64_t m, int64_t n, int64_t k) {
+  if (m <= 16 || n % 4 != 0 || k <= 0) return 1;
+  const int64_t bm = m <= 64 ? 64 : (m <= 128 ? 128 : 256);
+  const int64_t tiles = ((m + bm - 1) / bm) * ((n + 255) / 256);
+  constexpr int64_t kTarget = 256;
+  if (2 * tiles > kTarget) return 1;
+  const int64_t nwin = (k + 63) / 64;
+  int64_t s = (kTarget + tiles - 1) / tiles;
+  if (s > nwin / 4) s = nwin / 4;
+  if (s > k / (8 * m)) s = k / (8 * m);
+  if (s > 16) s = 16;
+  if (s < 2) return 1;
+  const int64_t wps = (nwin + s - 1) / s;
+  return (int)((nwin + wps - 1) / wps);  // every split keeps at least one window
+}
+
+// Tiled product for m > 16.  `part` (workspace, gemm_k_splits(m, n, k) x m x n floats, 16-byte
+// aligned) receives the partial sums when K is split; it may be NULL when it is not.
 hipError_t launch_gemm_tile(const GemmOperand &a, const GemmOperand &w, int64_t m, int64_t n,
-                            int64_t k, uint16_t *y, int64_t ld_y, hipStream_t stream);
+                            int64_t k, uint16_t *y, int64_t ld_y, float *part,
+                            hipStream_t stream);
 // Decode-shaped product with the activation quantization fused in (1 <= m <= 16, k <= 4096):
 // bf16 A is quantized inside the kernel; aq's codes / scales / gs, where not NULL, receive the
 // quantized A (row strides aq.ld_codes / aq.ld_scales).  hipErrorNotSupported (nothing

@@ -53,6 +53,11 @@ def test_tiny_config(nv):
     (8, 256, 4096, 16), (3, 48, 16, 1),
     (17, 256, 512, 16), (37, 80, 176, 1), (64, 512, 256, 16), (100, 272, 528, 16),
     (128, 256, 1024, 1), (300, 512, 2048, 16), (513, 1024, 4096, 16),
+    # K split over workgroups (too few tiles for the device): 16 splits of 4 windows; 1D W;
+    # K with a partial last window (5 splits, the tail in the last); the pipelined kernel with
+    # 2 splits; N not a multiple of 4 (no split).
+    (17, 1024, 4096, 16), (32, 4096, 4096, 16), (64, 1000, 2048, 1), (72, 768, 3088, 16),
+    (200, 512, 4096, 16), (40, 514, 2048, 1),
 ])
 def test_shapes(nv, m, n, k, br):
     rng = np.random.default_rng(m * 7 + n * 3 + k)
@@ -121,6 +126,29 @@ def test_decode_config_full_size(nv):
         y = nv.gemm_w4a4(dev_bf16(a), wq)
         y64 = O.gemm64(O.quantize_1d(a) + (1,), ow)
         check_gemm(y.cpu()[:, rows], y64, what=f"decode M={m}")
+
+
+@pytest.mark.parametrize("m", [17, 64, 200])
+def test_batched_decode_full_width(nv, m):
+    """The 14336 x 4096 decode weight with M = 17, 64 and 200 activation rows (quantized inside
+    the call): too few tiles to fill the device, so K is split over workgroups and the partial
+    sums are added by a second kernel.  Outputs are checked on sampled 16-row bands of W."""
+    d = W.decode()
+    w = d["w"]
+    wq = nv.quantize_2d(dev_bf16(w))
+    wc, ws, wg = host_q(wq)
+    gw = O.global_scale(float(np.max(np.abs(W.bf16_bits_to_float32(w)))))
+    assert np.float32(wg) == gw
+    rng = np.random.default_rng(100 + m)
+    bands = np.unique(np.concatenate([[0, 895], rng.choice(896, 14, replace=False)]))
+    rows = (bands[:, None] * 16 + np.arange(16)).ravel()
+    oc, os_ = O.encode_2d(w[rows], gw)
+    assert_codes_equal(wc[rows], oc, "W codes")
+    assert_codes_equal(ws[bands], os_, "W scales")
+    a = W.to_bf16_bits(W.normal_with_outliers(rng, m, 4096, 0.01, 20.0))
+    y = nv.gemm_w4a4(dev_bf16(a), wq)
+    y64 = O.gemm64(O.quantize_1d(a) + (1,), (oc, os_, gw, 16))
+    check_gemm(y.cpu()[:, rows], y64, what=f"batched decode M={m}")
 
 
 def test_prefill_config_full_size(nv):

@@ -42,16 +42,16 @@ struct GemmOperand {
 
 // K splits of the tiled product (m > 16) of m x k by n x k: a shape whose tiles (64, 128 or
 // 256 rows by 256 columns, as the launcher picks them) would fill fewer than half of a 256-CU
-// device splits its 64-wide K windows so that tiles x splits is about 256, keeping at least 4
-// windows per split and the fp32 partial sums (splits x m x n x 4 bytes) no larger than W's
-// packed codes (n x k / 2 bytes).  Depends on the shape only, so the workspace size does too.
-// 1 = no split.
+// device splits its 64-wide K windows so that tiles x splits is about 512 (two workgroups per
+// CU, which hide each other's load latency), keeping at least 4 windows per split and the fp32
+// partial sums (splits x m x n x 4 bytes) no larger than W's packed codes (n x k / 2 bytes).
+// Depends on the shape only, so the workspace size does too.  1 = no split.
 inline int gemm_k_splits(int64_t m, int64_t n, int64_t k) {
   if (m <= 16 || n % 4 != 0 || k <= 0) return 1;
   const int64_t bm = m <= 64 ? 64 : (m <= 128 ? 128 : 256);
   const int64_t tiles = ((m + bm - 1) / bm) * ((n + 255) / 256);
-  constexpr int64_t kTarget = 256;
-  if (2 * tiles > kTarget) return 1;
+  constexpr int64_t kTarget = 512;
+  if (4 * tiles > kTarget) return 1;
   const int64_t nwin = (k + 63) / 64;
   int64_t s = (kTarget + tiles - 1) / tiles;
   if (s > nwin / 4) s = nwin / 4;

@@ -132,7 +132,8 @@ def extra_workloads(args, torch, np, nv, W, only):
     warm = max(2, args.warmup)
 
     if not only or "decode" in only:
-        d = W.decode()
+        # M = 1, 8, 16 (the decode configuration) and a batched M = 64 (split-K tiled product)
+        d = W.decode(ms=(1, 8, 16, 64))
         wq0 = nv.quantize_2d(dev_bf16(torch, np, d["w"]))
         nw = 10  # 10 x 29.6 MB of weights > the 256 MB Infinity Cache
         wqs = [wq0] + [nv.QTensor(wq0.codes.clone(), wq0.scales.clone(), wq0.global_scale.clone(),
@@ -149,6 +150,8 @@ def extra_workloads(args, torch, np, nv, W, only):
                 "shape": [m, n, k], "ms": ms, "bound": "hbm", "achieved": gbs,
                 "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
                 "tflops": 2 * m * n * k / (ms * 1e-3) / 1e12}
+            if m > 16:  # the weight-only form serves m <= 16
+                continue
             # Weight-only form of the same product: the bf16 A is used as is.
             ms = timed(lambda i: nv.gemm_w4a16(a, wqs[i % nw], y=y), steps, warm, torch)
             gbs = nbytes / (ms * 1e-3) / 1e9

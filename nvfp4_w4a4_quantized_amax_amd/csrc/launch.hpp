@@ -19,7 +19,9 @@ hipError_t launch_quantize_persistent(const void *x, int64_t rows, int64_t cols,
                                       int64_t ld_scales, float *gs_out, void *ws,
                                       hipStream_t stream);
 // One-workgroup quantization (1D blocks) of a small tensor (rows * cols <= kSmallMaxElems).
-constexpr int64_t kSmallMaxElems = 1 << 17;
+// One CU reads the whole tensor, so past 64K values the single-read kernel is faster (32 x 4096:
+// 14.6 us on one workgroup, 9.5 us on all CUs).
+constexpr int64_t kSmallMaxElems = 1 << 16;
 hipError_t launch_quantize_small(const void *x, int64_t rows, int64_t cols, int64_t ld_x,
                                  uint8_t *codes, int64_t ld_codes, uint8_t *scales,
                                  int64_t ld_scales, float *gs_out, hipStream_t stream);
@@ -40,22 +42,25 @@ struct GemmOperand {
   int block_rows;
 };
 
-// K splits of the tiled product (m > 16) of m x k by n x k: a shape whose tiles (64, 128 or
-// 256 rows by 256 columns, as the launcher picks them) would fill fewer than half of a 256-CU
-// device splits its 64-wide K windows so that tiles x splits is about 512 (two workgroups per
-// CU, which hide each other's load latency), keeping at least 4 windows per split and the fp32
-// partial sums (splits x m x n x 4 bytes) no larger than W's packed codes (n x k / 2 bytes).
-// Depends on the shape only, so the workspace size does too.  1 = no split.
+// K splits of the tiled product (m > 16) of m x k by n x k.  The launcher picks 64-row tiles
+// (two resident workgroups per CU), 128-row or 256-row tiles (one per CU), all 256 columns
+// wide.  A shape whose tiles fill fewer than half of the resident slots of a 256-CU device
+// splits its 64-wide K windows so that tiles x splits fills the slots without a partial second
+// round, keeping at least 4 windows per split and the fp32 partial sums (splits x m x n x 4
+// bytes) no larger than W's packed codes (n x k / 2 bytes), or twice that for 256-row tiles,
+// whose compute gains more from the split.  Depends on the shape only, so the workspace size
+// does too.  1 = no split.
 inline int gemm_k_splits(int64_t m, int64_t n, int64_t k) {
   if (m <= 16 || n % 4 != 0 || k <= 0) return 1;
   const int64_t bm = m <= 64 ? 64 : (m <= 128 ? 128 : 256);
+  const int64_t slots = 256 * (m <= 64 ? 2 : 1);
   const int64_t tiles = ((m + bm - 1) / bm) * ((n + 255) / 256);
-  constexpr int64_t kTarget = 512;
-  if (4 * tiles > kTarget) return 1;
+  if (2 * tiles > slots) return 1;
   const int64_t nwin = (k + 63) / 64;
-  int64_t s = (kTarget + tiles - 1) / tiles;
+  int64_t s = slots / tiles;
   if (s > nwin / 4) s = nwin / 4;
-  if (s > k / (8 * m)) s = k / (8 * m);
+  const int64_t cap = k / ((m > 128 ? 4 : 8) * m);  // partial sums vs W's packed codes
+  if (s > cap) s = cap;
   if (s > 16) s = 16;
   if (s < 2) return 1;
   const int64_t wps = (nwin + s - 1) / s;

@@ -50,8 +50,15 @@ struct GemmOperand {
 // bytes) no larger than W's packed codes (n x k / 2 bytes), or twice that for 256-row tiles,
 // whose compute gains more from the split.  Depends on the shape only, so the workspace size
 // does too.  1 = no split.
+// Mid-size M takes 64 x 64 tiles with K split inside the workgroup (k_gemm_mid) when K is a
+// multiple of 1024 (four quarters of whole 4-window rounds), the scale rows are 2-byte aligned
+// (checked by the launcher) and the tiles give at least 128 workgroups.
+inline bool gemm_uses_mid(int64_t m, int64_t n, int64_t k) {
+  return m > 16 && m <= 128 && k > 0 && k % 1024 == 0 && ((m + 63) / 64) * ((n + 63) / 64) >= 128;
+}
+
 inline int gemm_k_splits(int64_t m, int64_t n, int64_t k) {
-  if (m <= 16 || n % 4 != 0 || k <= 0) return 1;
+  if (m <= 16 || n % 4 != 0 || k <= 0 || gemm_uses_mid(m, n, k)) return 1;
   const int64_t bm = m <= 64 ? 64 : (m <= 128 ? 128 : 256);
   const int64_t slots = 256 * (m <= 64 ? 2 : 1);
   const int64_t tiles = ((m + bm - 1) / bm) * ((n + 255) / 256);

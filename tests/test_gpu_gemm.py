@@ -58,6 +58,9 @@ def test_tiny_config(nv):
     # 2 splits; N not a multiple of 4 (no split).
     (17, 1024, 4096, 16), (32, 4096, 4096, 16), (64, 1000, 2048, 1), (72, 768, 3088, 16),
     (200, 512, 4096, 16), (40, 514, 2048, 1),
+    # 16 < M <= 128 with many 64-column tiles: K split over the 4 waves of each workgroup
+    # (ragged M and N; K = 1024 is a single round of the window ring).
+    (40, 8200, 2048, 1), (100, 4160, 1024, 16), (128, 4096, 4096, 16),
 ])
 def test_shapes(nv, m, n, k, br):
     rng = np.random.default_rng(m * 7 + n * 3 + k)

@@ -1495,33 +1495,31 @@ __global__ __launch_bounds__(kDecWaves * 64) void k_gemm_w4a16_stream(SmallMArgs
 }
 
 // ---------------------------------------------------------------------------------------------
-// Host launchers
-// ---------------------------------------------------------------------------------------------
-// ---------------------------------------------------------------------------------------------
-// Mid-size M (16 < M <= 128, K a multiple of 1024): 64 x 64 output tiles, one per workgroup, so a
-// 14336-row W gives 224 or more workgroups.  The 4 waves split K in four contiguous quarters;
-// each wave computes the whole 64 x 64 tile over its quarter (2 x 2 MFMA tiles of 32 x 32) with
-// four 64-wide windows of loads in flight, and the four partial tiles are added through LDS.
-// W is read once (per 64-row tile of A), nothing goes back to memory but Y.
+// Mid-size M (16 < M <= 128, K a multiple of 1024): output tiles of 32 FM rows by 64 columns
+// (the launcher uses FM = 2), one per workgroup, so a 14336-row W gives 224 workgroups per row
+// slice.  The 4 waves split K in four contiguous quarters; each wave computes the whole tile
+// over its quarter (FM x 2 MFMA tiles of 32 x 32) with four 64-wide windows of loads in flight,
+// and the four partial tiles are added through LDS.  W is read once per row slice of A;
+// nothing but Y goes to memory.  FM = 2 leaves room for two workgroups per CU.
 // ---------------------------------------------------------------------------------------------
 constexpr int kMidDepth = 4;
 
-template <bool W2D>
+template <int FM, bool W2D>
 __global__ __launch_bounds__(kGemmThreads) void k_gemm_mid(DenseArgs p) {
-  __shared__ float s_red[4][2][2][16][kWave];  // [wave][f][g][register][lane]
+  __shared__ float s_red[4][FM][2][16][kWave];  // [wave][f][g][register][lane]
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lr = lane & 31, kh = lane >> 5;
   int tm, tn;
   tile_of(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, tm, tn);
-  const int64_t m0 = (int64_t)tm * 64, n0 = (int64_t)tn * 64;
+  const int64_t m0 = (int64_t)tm * (32 * FM), n0 = (int64_t)tn * 64;
 
   // Rows clamped into the matrices; results of clamped rows are never stored.
-  const int64_t wpw = p.k / 256;  // windows per wave
+  const int64_t wpw = p.k / 256;  // windows per wave, a multiple of kMidDepth
   const int64_t w_first = wave * wpw;
-  const uint8_t *a_row[2], *a_srow[2], *w_row[2], *w_srow[2];
+  const uint8_t *a_row[FM], *a_srow[FM], *w_row[2], *w_srow[2];
 #pragma unroll
-  for (int f = 0; f < 2; ++f) {
+  for (int f = 0; f < FM; ++f) {
     const int64_t r = min(m0 + f * 32 + lr, p.m - 1);
     a_row[f] = p.a.codes + r * p.a.ld_codes + kh * 16 + w_first * 32;
     a_srow[f] = p.a.scales + r * p.a.ld_scales + kh * 2 + w_first * 4;
@@ -1532,18 +1530,19 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_mid(DenseArgs p) {
     w_row[g] = p.w.codes + r * p.w.ld_codes + kh * 16 + w_first * 32;
     w_srow[g] = p.w.scales + (W2D ? (r >> 4) : r) * p.w.ld_scales + kh * 2 + w_first * 4;
   }
-  floatx16_t acc[2][2];
+  floatx16_t acc[FM][2];
 #pragma unroll
-  for (int f = 0; f < 2; ++f)
+  for (int f = 0; f < FM; ++f)
 #pragma unroll
     for (int g = 0; g < 2; ++g) acc[f][g] = floatx16_t{};
 
-  // Ring of kMidDepth windows (wpw is a multiple of kMidDepth): full rounds refill every slot
-  // after using it, the last round only drains, so no load sits under a branch.  Two scale
-  // bytes per fragment come in one 16-bit load.
-  auto load = [&](Frags<2, 2> &fr, int64_t win) {
+  // Ring of kMidDepth windows: full rounds refill every slot after using it, the last round
+  // only drains, so no load sits under a branch.  Two scale bytes per fragment come in one
+  // 16-bit load.  The scheduling barriers keep the loads in window order, so that waiting for
+  // window j waits for nothing issued after it.
+  auto load = [&](Frags<FM, 2> &fr, int64_t win) {
 #pragma unroll
-    for (int f = 0; f < 2; ++f) {
+    for (int f = 0; f < FM; ++f) {
       fr.a[f] = load16(a_row[f] + win * 32);
       fr.sa[f] = *(const uint16_t *)(a_srow[f] + win * 4);
     }
@@ -1553,9 +1552,7 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_mid(DenseArgs p) {
       fr.sw[g] = *(const uint16_t *)(w_srow[g] + win * 4);
     }
   };
-  // The scheduling barriers keep the loads in window order, so that waiting for window j
-  // waits for nothing issued after it.
-  Frags<2, 2> ring[kMidDepth];
+  Frags<FM, 2> ring[kMidDepth];
 #pragma unroll
   for (int j = 0; j < kMidDepth; ++j) {
     load(ring[j], j);
@@ -1573,30 +1570,33 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_mid(DenseArgs p) {
 #pragma unroll
   for (int j = 0; j < kMidDepth; ++j) compute_window(ring[j], acc);
 
-  // Add the four quarters: every wave stores its tile, then wave q finishes MFMA tile
-  // (q / 2, q % 2) from all four copies.
+  // Add the four quarters: every wave stores its tile, then wave q finishes MFMA tiles
+  // t = q * FM / 2 .. (q + 1) * FM / 2 - 1 (tile t is (t / 2, t % 2)) from all four copies.
 #pragma unroll
-  for (int f = 0; f < 2; ++f)
+  for (int f = 0; f < FM; ++f)
 #pragma unroll
     for (int g = 0; g < 2; ++g)
 #pragma unroll
       for (int r = 0; r < 16; ++r) s_red[wave][f][g][r][lane] = acc[f][g][r];
   __syncthreads();
-  const int f = wave >> 1, g = wave & 1;
   const float alpha = (*p.a.gs) * (*p.w.gs);
-  const int64_t col = n0 + g * 32 + lr;
 #pragma unroll
-  for (int r = 0; r < 16; r += 2) {  // rows r and r + 1 are adjacent
-    float v0 = s_red[0][f][g][r][lane], v1 = s_red[0][f][g][r + 1][lane];
+  for (int t = 0; t < FM / 2; ++t) {
+    const int tile = wave * (FM / 2) + t, f = tile >> 1, g = tile & 1;
+    const int64_t col = n0 + g * 32 + lr;
 #pragma unroll
-    for (int w = 1; w < 4; ++w) {
-      v0 += s_red[w][f][g][r][lane];
-      v1 += s_red[w][f][g][r + 1][lane];
+    for (int r = 0; r < 16; r += 2) {  // rows r and r + 1 are adjacent
+      float v0 = s_red[0][f][g][r][lane], v1 = s_red[0][f][g][r + 1][lane];
+#pragma unroll
+      for (int w = 1; w < 4; ++w) {
+        v0 += s_red[w][f][g][r][lane];
+        v1 += s_red[w][f][g][r + 1][lane];
+      }
+      const int64_t row = m0 + f * 32 + 8 * (r >> 2) + 4 * kh + (r & 3);
+      const uint32_t pk = bf16x2_rne(v0 * alpha, v1 * alpha);
+      if (row < p.m && col < p.n) ntstore_u16(p.y + row * p.ld_y + col, pk);
+      if (row + 1 < p.m && col < p.n) ntstore_u16(p.y + (row + 1) * p.ld_y + col, pk >> 16);
     }
-    const int64_t row = m0 + f * 32 + 8 * (r >> 2) + 4 * kh + (r & 3);
-    const uint32_t pk = bf16x2_rne(v0 * alpha, v1 * alpha);
-    if (row < p.m && col < p.n) ntstore_u16(p.y + row * p.ld_y + col, pk);
-    if (row + 1 < p.m && col < p.n) ntstore_u16(p.y + (row + 1) * p.ld_y + col, pk >> 16);
   }
 }
 
@@ -1627,6 +1627,9 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(const float *__restrict__
   }
 }
 
+// ---------------------------------------------------------------------------------------------
+// Host launchers
+// ---------------------------------------------------------------------------------------------
 static hipError_t launch_splitk_reduce(const DenseArgs &p, int splits, hipStream_t stream) {
   const int64_t total = p.m * (p.n / 4);
   int64_t g = (total + 255) / 256;
@@ -1685,9 +1688,9 @@ hipError_t launch_gemm_tile(const GemmOperand &a, const GemmOperand &w, int64_t 
     p.tiles_n = (int)((n + 63) / 64);
     const unsigned grid = (unsigned)p.tiles_m * (unsigned)p.tiles_n;
     if (w.block_rows == 16)
-      hipLaunchKernelGGL(k_gemm_mid<true>, dim3(grid), dim3(kGemmThreads), 0, stream, p);
+      hipLaunchKernelGGL((k_gemm_mid<2, true>), dim3(grid), dim3(kGemmThreads), 0, stream, p);
     else
-      hipLaunchKernelGGL(k_gemm_mid<false>, dim3(grid), dim3(kGemmThreads), 0, stream, p);
+      hipLaunchKernelGGL((k_gemm_mid<2, false>), dim3(grid), dim3(kGemmThreads), 0, stream, p);
     return hipGetLastError();
   }
   if (m <= 64) return launch_tile_fm<1, 4>(a, w, m, n, k, y, ld_y, part, stream);

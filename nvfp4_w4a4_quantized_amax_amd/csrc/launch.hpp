@@ -50,9 +50,11 @@ struct GemmOperand {
 // bytes) no larger than W's packed codes (n x k / 2 bytes), or twice that for 256-row tiles,
 // whose compute gains more from the split.  Depends on the shape only, so the workspace size
 // does too.  1 = no split.
-// Mid-size M takes 64 x 64 tiles with K split inside the workgroup (k_gemm_mid) when K is a
-// multiple of 1024 (four quarters of whole 4-window rounds), the scale rows are 2-byte aligned
-// (checked by the launcher) and the tiles give at least 128 workgroups.
+// Mid-size M (16 < M <= 128) takes 64 x 64 tiles with K split inside the workgroup
+// (k_gemm_mid) when K is a multiple of 1024 (four quarters of whole 4-window rounds), the scale
+// rows are 2-byte aligned (checked by the launcher) and the tiles give at least 128 workgroups.
+// (128-row tiles, one workgroup per CU, measured no faster up to M = 128 and slower beyond,
+// where the 256 x 256 tiles with their interleaved decode win.)
 inline bool gemm_uses_mid(int64_t m, int64_t n, int64_t k) {
   return m > 16 && m <= 128 && k > 0 && k % 1024 == 0 && ((m + 63) / 64) * ((n + 63) / 64) >= 128;
 }

@@ -58,9 +58,10 @@ def test_tiny_config(nv):
     # 2 splits; N not a multiple of 4 (no split).
     (17, 1024, 4096, 16), (32, 4096, 4096, 16), (64, 1000, 2048, 1), (72, 768, 3088, 16),
     (200, 512, 4096, 16), (40, 514, 2048, 1),
-    # 16 < M <= 128 with many 64-column tiles: K split over the 4 waves of each workgroup
-    # (ragged M and N; K = 1024 is a single round of the window ring).
-    (40, 8200, 2048, 1), (100, 4160, 1024, 16), (128, 4096, 4096, 16),
+    # 16 < M <= 512 with many 64-column tiles: K split over the 4 waves of each workgroup,
+    # 64-row tiles up to M = 64, 128-row tiles above (ragged M and N; K = 1024 is a single
+    # round of the window ring); 128-row tiles with too few of them take the split path.
+    (40, 8200, 2048, 1), (100, 8256, 1024, 16), (300, 4160, 2048, 16), (128, 4096, 4096, 16),
 ])
 def test_shapes(nv, m, n, k, br):
     rng = np.random.default_rng(m * 7 + n * 3 + k)
@@ -131,11 +132,11 @@ def test_decode_config_full_size(nv):
         check_gemm(y.cpu()[:, rows], y64, what=f"decode M={m}")
 
 
-@pytest.mark.parametrize("m", [17, 64, 200])
+@pytest.mark.parametrize("m", [17, 64, 200, 513])
 def test_batched_decode_full_width(nv, m):
-    """The 14336 x 4096 decode weight with M = 17, 64 and 200 activation rows (quantized inside
-    the call): too few tiles to fill the device, so K is split over workgroups and the partial
-    sums are added by a second kernel.  Outputs are checked on sampled 16-row bands of W."""
+    """The 14336 x 4096 decode weight with M = 17, 64, 200 and 513 activation rows (quantized
+    inside the call): 64- and 128-row tiles of 64 columns with K split over each workgroup's
+    waves, then 256 x 256 tiles.  Outputs are checked on sampled 16-row bands of W."""
     d = W.decode()
     w = d["w"]
     wq = nv.quantize_2d(dev_bf16(w))

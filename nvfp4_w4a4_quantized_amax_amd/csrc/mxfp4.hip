@@ -511,6 +511,139 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     }
 }
 
+// Small and mid-size M (M <= 128): output tiles of 32FM x 32FN, one per workgroup.  The 4 waves
+// take the four quarters of K; each computes the whole tile over its quarter (FM x FN MFMA tiles
+// of 32 x 32, straight from memory: a lane's operand is one MXFP4 block) with DEPTH 64-wide
+// windows of loads in flight, and the four partial tiles are added through LDS.  Scales come
+// 8 bytes (4 windows) per row and load: lane half kh shifts the word by 8 kh, and the MFMA's
+// scale select picks byte 0 or 2 of each 32-bit half.  K must be a multiple of 256 * DEPTH and
+// scale rows 8-byte aligned; W is read once per 32FM-row slice of A.
+template <int FM, int FN>
+struct MxMidWin {
+  u32x4_t a[FM], w[FN];
+};
+
+template <int FM, int FN, int DEPTH>
+struct MxMidScales {
+  uint2 a[FM][DEPTH / 4], w[FN][DEPTH / 4];
+};
+
+template <int FM, int FN, int DEPTH>
+__global__ __launch_bounds__(256) void k_gemm_mx_mid(MxArgs p) {
+  static_assert(DEPTH % 4 == 0, "a scale load covers 4 windows");
+  __shared__ float s_red[4][FM][FN][16][kWave];  // [wave][f][g][register][lane]
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lr = lane & 31, kh = lane >> 5;
+  const uint32_t sh = 8u * kh;
+  int tm, tn;
+  tile_of(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, tm, tn);
+  const int64_t m0 = (int64_t)tm * (32 * FM), n0 = (int64_t)tn * (32 * FN);
+  // Rows clamped into the matrices; results of clamped rows are never stored.
+  const int64_t wpw = p.k / 256;  // 64-wide windows per wave, a multiple of DEPTH
+  const int64_t w_first = wave * wpw;
+  const uint8_t *ac[FM], *as[FM], *wc[FN], *ws[FN];
+#pragma unroll
+  for (int f = 0; f < FM; ++f) {
+    const int64_t ra = min(m0 + f * 32 + lr, p.m - 1);
+    ac[f] = p.a_codes + ra * p.ld_ac + kh * 16 + w_first * 32;
+    as[f] = p.a_scales + ra * p.ld_as + w_first * 2;
+  }
+#pragma unroll
+  for (int g = 0; g < FN; ++g) {
+    const int64_t rw = min(n0 + g * 32 + lr, p.n - 1);
+    wc[g] = p.w_codes + rw * p.ld_wc + kh * 16 + w_first * 32;
+    ws[g] = p.w_scales + rw * p.ld_ws + w_first * 2;
+  }
+  floatx16_t acc[FM][FN];
+#pragma unroll
+  for (int f = 0; f < FM; ++f)
+#pragma unroll
+    for (int g = 0; g < FN; ++g) acc[f][g] = floatx16_t{};
+  auto load = [&](MxMidWin<FM, FN> &r, int64_t win) {
+#pragma unroll
+    for (int f = 0; f < FM; ++f) r.a[f] = *(const u32x4_t *)(ac[f] + win * 32);
+#pragma unroll
+    for (int g = 0; g < FN; ++g) r.w[g] = *(const u32x4_t *)(wc[g] + win * 32);
+  };
+  // scales of windows win .. win + DEPTH - 1
+  auto load_scales = [&](MxMidScales<FM, FN, DEPTH> &q, int64_t win) {
+#pragma unroll
+    for (int f = 0; f < FM; ++f)
+#pragma unroll
+      for (int u = 0; u < DEPTH / 4; ++u) q.a[f][u] = *(const uint2 *)(as[f] + (win + 4 * u) * 2);
+#pragma unroll
+    for (int g = 0; g < FN; ++g)
+#pragma unroll
+      for (int u = 0; u < DEPTH / 4; ++u) q.w[g][u] = *(const uint2 *)(ws[g] + (win + 4 * u) * 2);
+  };
+  // window j of the round whose scales are q
+  auto compute = [&](const MxMidWin<FM, FN> &r, const MxMidScales<FM, FN, DEPTH> &q, int j) {
+#pragma unroll
+    for (int f = 0; f < FM; ++f) {
+      const uint32_t sa = ((j >> 1) & 1 ? q.a[f][j >> 2].y : q.a[f][j >> 2].x) >> sh;
+#pragma unroll
+      for (int g = 0; g < FN; ++g) {
+        const uint32_t sw = ((j >> 1) & 1 ? q.w[g][j >> 2].y : q.w[g][j >> 2].x) >> sh;
+        if (j & 1)
+          acc[f][g] = mx_mfma_sel<2>(r.a[f], r.w[g], sa, sw, acc[f][g]);
+        else
+          acc[f][g] = mx_mfma_sel<0>(r.a[f], r.w[g], sa, sw, acc[f][g]);
+      }
+    }
+  };
+  // Full rounds refill every slot after using it (the next round's scales first), the last
+  // round only drains; the scheduling barriers keep the loads in window order.
+  MxMidWin<FM, FN> ring[DEPTH];
+  MxMidScales<FM, FN, DEPTH> cur, nxt;
+  load_scales(cur, 0);
+#pragma unroll
+  for (int j = 0; j < DEPTH; ++j) {
+    load(ring[j], j);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  for (int64_t i = 0; i + DEPTH < wpw; i += DEPTH) {
+#pragma unroll
+    for (int j = 0; j < DEPTH; ++j) {
+      compute(ring[j], cur, j);
+      __builtin_amdgcn_sched_barrier(0);
+      if (j == 0) load_scales(nxt, i + DEPTH);
+      load(ring[j], i + j + DEPTH);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    cur = nxt;
+  }
+#pragma unroll
+  for (int j = 0; j < DEPTH; ++j) compute(ring[j], cur, j);
+
+  // Add the four quarters.  The tile's FM * FN * 16 accumulator registers (in (f, g, register)
+  // order) are shared out 4 * FM * FN to a wave; registers r and r + 1 hold adjacent rows.
+#pragma unroll
+  for (int f = 0; f < FM; ++f)
+#pragma unroll
+    for (int g = 0; g < FN; ++g)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s_red[wave][f][g][r][lane] = acc[f][g][r];
+  __syncthreads();
+  constexpr int kPer = 4 * FM * FN;
+#pragma unroll
+  for (int j = 0; j < kPer; j += 2) {
+    const int t = wave * kPer + j;
+    const int f = t / (16 * FN), g = (t / 16) % FN, r = t % 16;
+    float v0 = s_red[0][f][g][r][lane], v1 = s_red[0][f][g][r + 1][lane];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) {
+      v0 += s_red[w][f][g][r][lane];
+      v1 += s_red[w][f][g][r + 1][lane];
+    }
+    const int64_t row = m0 + f * 32 + 8 * (r >> 2) + 4 * kh + (r & 3);
+    const int64_t col = n0 + g * 32 + lr;
+    const uint32_t pk = bf16x2_rne(v0, v1);
+    if (row < p.m && col < p.n) ntstore_u16(p.y + row * p.ld_y + col, pk);
+    if (row + 1 < p.m && col < p.n) ntstore_u16(p.y + (row + 1) * p.ld_y + col, pk >> 16);
+  }
+}
+
 // Any shape (K a multiple of 32): each wave computes one 32 x 32 tile straight from memory, one
 // 64-wide K window at a time; a missing second block of the last window reads as zero codes.
 __global__ __launch_bounds__(256) void k_gemm_mx_simple(MxArgs p) {
@@ -581,11 +714,42 @@ hipError_t launch_mx_dequantize(const uint8_t *codes, int64_t ld_codes, const ui
   return hipGetLastError();
 }
 
+// Launches k_gemm_mx_mid when K suits its ring, the scale rows are 8-byte aligned and the
+// shape makes at least 128 tiles; returns whether it did.
+template <int FM, int FN, int DEPTH>
+static bool launch_mx_mid(MxArgs &p, hipStream_t stream) {
+  const int64_t tiles_m = (p.m + 32 * FM - 1) / (32 * FM), tiles_n = (p.n + 32 * FN - 1) / (32 * FN);
+  if (p.k % (256 * DEPTH) != 0 || tiles_m * tiles_n < 128 || (uintptr_t)p.a_scales % 8 ||
+      (uintptr_t)p.w_scales % 8 || p.ld_as % 8 || p.ld_ws % 8)
+    return false;
+  p.tiles_m = (int)tiles_m;
+  p.tiles_n = (int)tiles_n;
+  hipLaunchKernelGGL((k_gemm_mx_mid<FM, FN, DEPTH>), dim3((unsigned)(tiles_m * tiles_n)), dim3(256),
+                     0, stream, p);
+  return true;
+}
+
 hipError_t launch_mx_gemm(const uint8_t *a_codes, int64_t ld_ac, const uint8_t *a_scales,
                           int64_t ld_as, const uint8_t *w_codes, int64_t ld_wc,
                           const uint8_t *w_scales, int64_t ld_ws, int64_t m, int64_t n, int64_t k,
                           uint16_t *y, int64_t ld_y, hipStream_t stream) {
   MxArgs p{a_codes, a_scales, w_codes, w_scales, ld_ac, ld_as, ld_wc, ld_ws, m, n, k, y, ld_y, 0, 0};
+  // M <= 128: the mid-size kernel.  Deeper rings keep more of W in flight (16 windows, all of a
+  // quarter of K = 4096 at once); each M range takes the deepest ring K allows, and 128-row
+  // tiles fall back to 64-row ones where they would be too few.
+  bool mid = false;
+  if (m <= 4)
+    mid = launch_mx_mid<1, 1, 16>(p, stream) || launch_mx_mid<1, 1, 8>(p, stream) ||
+          launch_mx_mid<1, 1, 4>(p, stream);
+  else if (m <= 32)
+    mid = launch_mx_mid<1, 2, 16>(p, stream) || launch_mx_mid<1, 2, 8>(p, stream) ||
+          launch_mx_mid<1, 2, 4>(p, stream);
+  else if (m <= 64)
+    mid = launch_mx_mid<2, 2, 8>(p, stream) || launch_mx_mid<2, 2, 4>(p, stream);
+  else if (m <= 128)
+    mid = launch_mx_mid<4, 2, 8>(p, stream) || launch_mx_mid<4, 2, 4>(p, stream) ||
+          launch_mx_mid<2, 2, 4>(p, stream);
+  if (mid) return hipGetLastError();
   const bool pipelined = m > 128 && k % 64 == 0 && (uintptr_t)a_scales % 2 == 0 &&
                          (uintptr_t)w_scales % 2 == 0 && ld_as % 2 == 0 && ld_ws % 2 == 0;
   if (pipelined) {

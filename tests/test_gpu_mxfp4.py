@@ -112,7 +112,8 @@ def test_dequantize(nv, dtype):
 # M > 128 takes a pipelined kernel: the wide-window one when K is a multiple of 512 (one and
 # three window pairs appear; 4100 x 4200 has more tiles than workgroups, so workgroups carry the
 # pipeline from one ragged tile into the next), else the 64-wide one (one window, an odd window
-# count); the rest (small M, K = 32 mod 64) the direct one.  Ragged M and N appear on every path.
+# count).  M <= 128 with enough columns takes the mid-size kernel (covered below); the rest
+# (small M and N, K = 32 mod 64) the direct one.  Ragged M and N appear on every path.
 @pytest.mark.parametrize("m,n,k", [
     (1, 64, 64), (7, 96, 160), (16, 200, 2048), (129, 256, 64), (300, 512, 2048),
     (513, 1000, 4096), (256, 256, 192), (260, 300, 96), (300, 512, 512), (257, 384, 1536),
@@ -133,6 +134,36 @@ def test_gemm_shapes(nv, m, n, k):
     # the prequantized form gives the same bits
     y2 = nv.mxfp4_gemm(aq, wq)
     assert torch.equal(y, y2)
+
+
+# The mid-size kernel for M <= 128: each case names the (row tiles, column tiles, ring depth)
+# form the shape selects, by M range and by the K multiple (4096, 2048 or 1024) that fits the
+# ring; with too few 128-row tiles the 64-row form takes over.  W is checked on sampled rows
+# and Y on the sampled columns (the ragged last columns always among them).
+@pytest.mark.parametrize("m,n,k,form", [
+    (1, 8200, 1024, "1x1 depth 4"), (3, 4100, 2048, "1x1 depth 8"), (4, 4096, 4096, "1x1 depth 16"),
+    (17, 8192, 1024, "1x2 depth 4"), (32, 8256, 2048, "1x2 depth 8"), (9, 8200, 4096, "1x2 depth 16"),
+    (40, 8192, 1024, "2x2 depth 4"), (64, 8200, 2048, "2x2 depth 8"), (97, 8200, 1024, "4x2 depth 4"),
+    (128, 8192, 2048, "4x2 depth 8"), (100, 4100, 2048, "2x2 depth 4 (too few 128-row tiles)"),
+])
+def test_gemm_mid_sizes(nv, m, n, k, form):
+    rng = np.random.default_rng(m * 11 + n + k)
+    a = W.to_bf16_bits(W.normal_with_outliers(rng, m, k, 0.01, 20.0))
+    w = W.to_bf16_bits(rng.standard_normal((n, k)) * 0.02)
+    wq = nv.mxfp4_quantize(dev_bf16(w))
+    aq = nv.empty_mxtensor(m, k)
+    y = nv.mxfp4_gemm(dev_bf16(a), wq, a_q=aq)
+    cols = np.unique(np.concatenate([np.arange(n - 40, n), rng.choice(n - 40, 88, replace=False)]))
+    wc, ws = host_mx(wq)
+    ac, as_ = host_mx(aq)
+    ow = MX.quantize_mx(w[cols])
+    oa = MX.quantize_mx(a)
+    assert_codes_equal(wc[cols], ow[0], f"{form}: W codes")
+    assert_codes_equal(ws[cols], ow[1], f"{form}: W scales")
+    assert_codes_equal(ac, oa[0], f"{form}: A codes")
+    assert_codes_equal(as_, oa[1], f"{form}: A scales")
+    check_gemm(y.cpu()[:, cols], MX.gemm64_mx(oa, ow), what=f"mxfp4 mid {form} {m}x{n}x{k}")
+    assert torch.equal(y, nv.mxfp4_gemm(aq, wq))
 
 
 def test_gemm_unaligned_scale_rows(nv):

@@ -193,6 +193,7 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_tile(DenseArgs p) {
   const int lr = lane & 31, kh = lane >> 5;
 
   const int logical = xcd_logical(blockIdx.x, gridDim.x);
+  const float alpha = load_global_scale(p.a.gs) * load_global_scale(p.w.gs);
   const int in_group = kGroupM * p.tiles_n;
   const int first_m = (logical / in_group) * kGroupM;
   const int gsz = min(p.tiles_m - first_m, kGroupM);
@@ -242,7 +243,6 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_tile(DenseArgs p) {
                           [&](int64_t row, int64_t col) { return row < p.m && col < p.n; });
     return;
   }
-  const float alpha = (*p.a.gs) * (*p.w.gs);
 #pragma unroll
   for (int f = 0; f < FM; ++f)
 #pragma unroll
@@ -871,6 +871,7 @@ constexpr int kSmallMWin = 8;
 template <bool W2D>
 __global__ __launch_bounds__(kGemmThreads) void k_gemm_small_m(SmallMArgs p) {
   __shared__ floatx4_t s_red[4][kWave];
+  const float alpha = load_global_scale(p.a.gs) * load_global_scale(p.w.gs);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int i16 = lane & 15, q = lane >> 4;
   const int64_t n0 = (int64_t)blockIdx.x * 16;
@@ -932,7 +933,6 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_small_m(SmallMArgs p) {
   __syncthreads();
   if (wave == 0) {
     const floatx4_t s = s_red[0][lane] + s_red[1][lane] + s_red[2][lane] + s_red[3][lane];
-    const float alpha = (*p.a.gs) * (*p.w.gs);
     if (i16 < p.m) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -947,9 +947,10 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_small_m(SmallMArgs p) {
 // Decode-shaped kernels (m <= 16, K <= 4096): one workgroup of 16 waves per CU walks the 16-row
 // bands of W (bands b, b + G, b + 2G, ... for a grid of G).  Wave w owns the w-th sixteenth of K
 // for every band and keeps its slice of A, ready for the MFMA, in registers for the whole call,
-// so the loop only streams W.  dec_depth(WIN) bands of W are in flight per workgroup: a band's
-// registers are refilled with the band dec_depth(WIN) steps ahead as soon as they have been
-// multiplied.  The sixteen partial sums of a band meet in LDS.
+// so the loop only streams W.  dec_depth bands of W are in flight per workgroup (4: with the
+// launch grid, all of a workgroup's bands for N up to 16384): a band's registers are refilled
+// with the band dec_depth steps ahead as soon as they have been multiplied.  The sixteen partial
+// sums of each band of a round meet in LDS, one barrier per round.
 //
 // FULL (K a multiple of 128, scale rows 2-byte aligned with even strides, W's codes and scales
 // each under 2 GiB): W is read with buffer loads whose offsets are unsigned 32-bit; windows past
@@ -960,8 +961,10 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_small_m(SmallMArgs p) {
 // ---------------------------------------------------------------------------------------------
 constexpr int kDecWaves = 16;
 constexpr int kDecWin = 2;  // 128-wide K windows per wave at most (K <= 16 * 2 * 128)
-// Bands of W in flight per workgroup: as many as the 128 registers of a 16-wave workgroup hold.
-constexpr int dec_depth(int win) { return win == 1 ? 4 : 3; }
+// Bands of W in flight per workgroup: as many as the 128 registers of a 16-wave workgroup hold
+// next to the rest of the kernel (deep: the FULL forms, except the W4A4 one that quantizes A
+// itself, which measured faster with 3 bands of two windows).
+constexpr int dec_depth(int win, bool deep) { return win == 1 || deep ? 4 : 3; }
 constexpr uint32_t kBufOutOfRange = 0x80000000u;  // above every buffer size used here
 
 template <int WIN>
@@ -1032,59 +1035,67 @@ __device__ __forceinline__ void load_decode_w(const SmallMArgs &p, const WBufs &
   }
 }
 
-// Issues the loads of the workgroup's first dec_depth(WIN) bands.
-template <bool W2D, bool FULL, int WIN>
+// Issues the loads of the workgroup's first dec_depth bands.
+template <bool W2D, bool FULL, int WIN, int D>
 __device__ __forceinline__ void decode_ring_start(const SmallMArgs &p, const WBufs &buf,
                                                   int64_t nbands, int i16, int q, int64_t win0,
-                                                  int nw, DecodeW<WIN> (&ring)[dec_depth(WIN)]) {
+                                                  int nw, DecodeW<WIN> (&ring)[D]) {
 #pragma unroll
-  for (int j = 0; j < dec_depth(WIN); ++j)
+  for (int j = 0; j < D; ++j)
     load_decode_w<W2D, FULL, WIN>(p, buf, blockIdx.x + (int64_t)j * gridDim.x, nbands, i16, q,
                                   win0, nw, ring[j]);
+  // Work on A that follows must not move above these loads (it would wait for A first).
+  __builtin_amdgcn_sched_barrier(0);
 }
 
-// The band loop: mul(ring slot) returns the wave's 16x16 partial product of that band; the slot
-// is refilled with the band dec_depth(WIN) steps ahead, the partials are summed through LDS (two
-// buffers alternate, so one barrier per band suffices) and waves 0..3 each finish one of the four
-// output rows a lane holds.  The main loop runs while all dec_depth(WIN) steps of a round are
-// real bands, so its refills need no condition; the last, partial round only drains the ring.
-template <bool W2D, bool FULL, int WIN, class Mul>
+// The band loop, in rounds of D bands (bands base + j G, j < D, for a grid of G).
+// mul(ring slot) returns the wave's 16x16 partial product of a band and the slot is refilled with
+// the band D G further on.  After a round the D partials of the 16 waves meet in LDS: after one
+// barrier, thread t adds the 16 waves' values of output (band t / 256, lane (t / 4) % 64,
+// component t % 4) in wave order, and a second barrier frees the buffer for the next round.  The
+// main loop runs while all D bands of a round are real, so its refills need no condition (past
+// the last band they load nothing in the FULL form); the last, partial round only drains.  The
+// scheduler may interleave the W decode of one band with the MFMAs of another; that overlap
+// measured faster than keeping each band's waits precise with scheduling barriers.
+template <bool W2D, bool FULL, int WIN, int D, class Mul>
 __device__ __forceinline__ void decode_band_loop(const SmallMArgs &p, const WBufs &buf,
                                                  int64_t nbands, int lane, int wave,
                                                  int64_t win0, int nw, float alpha,
-                                                 DecodeW<WIN> (&ring)[dec_depth(WIN)],
+                                                 DecodeW<WIN> (&ring)[D],
                                                  floatx4_t (*s_red)[kDecWaves][kWave], Mul mul) {
-  constexpr int D = dec_depth(WIN);
+  static_assert(D * 256 <= kDecWaves * 64, "at most one output per thread and round");
   const int i16 = lane & 15, q = lane >> 4;
   const int64_t g = gridDim.x;
-  int parity = 0;
-  auto finish = [&](const floatx4_t &acc, int64_t band) {
-    s_red[parity][wave][lane] = acc;
+  const int fj = threadIdx.x >> 8, fl = (threadIdx.x >> 2) & 63, fc = threadIdx.x & 3;
+  const int frow = fl & 15;
+  auto finish = [&](const floatx4_t (&acc)[D], int64_t base) {
+#pragma unroll
+    for (int j = 0; j < D; ++j) s_red[j][wave][lane] = acc[j];
     __syncthreads();
-    if (wave < 4 && i16 < p.m) {
+    const int64_t band = base + fj * g;
+    if (fj < D && band < nbands && frow < p.m) {
       float t = 0.0f;
 #pragma unroll
-      for (int w2 = 0; w2 < kDecWaves; ++w2)  // component `wave` of each partial, 4-byte reads
-        t += ((const float *)&s_red[parity][w2][lane])[wave];
-      const int64_t n = band * 16 + 4 * q + wave;
-      if (n < p.n) ntstore_u16(p.y + (int64_t)i16 * p.ld_y + n, f32_to_bf16_rne(t * alpha));
+      for (int w2 = 0; w2 < kDecWaves; ++w2) t += ((const float *)&s_red[fj][w2][fl])[fc];
+      const int64_t n = band * 16 + 4 * (fl >> 4) + fc;
+      if (n < p.n) ntstore_u16(p.y + (int64_t)frow * p.ld_y + n, f32_to_bf16_rne(t * alpha));
     }
-    parity ^= 1;
+    __syncthreads();
   };
+  floatx4_t acc[D];
   int64_t base = blockIdx.x;
   for (; base + (D - 1) * g < nbands; base += D * g) {
 #pragma unroll
     for (int j = 0; j < D; ++j) {
-      const int64_t band = base + j * g;
-      const floatx4_t acc = mul(ring[j]);
-      load_decode_w<W2D, FULL, WIN>(p, buf, band + D * g, nbands, i16, q, win0, nw, ring[j]);
-      finish(acc, band);
+      acc[j] = mul(ring[j]);
+      load_decode_w<W2D, FULL, WIN>(p, buf, base + (j + D) * g, nbands, i16, q, win0, nw, ring[j]);
     }
+    finish(acc, base);
   }
+  if (base < nbands) {
 #pragma unroll
-  for (int j = 0; j < D - 1; ++j) {
-    const int64_t band = base + j * g;
-    if (band < nbands) finish(mul(ring[j]), band);
+    for (int j = 0; j < D; ++j) acc[j] = base + j * g < nbands ? mul(ring[j]) : floatx4_t{};
+    finish(acc, base);
   }
 }
 
@@ -1094,7 +1105,8 @@ __device__ __forceinline__ void decode_band_loop(const SmallMArgs &p, const WBuf
 // most 16 rows, so the redundant work is small and no workgroup waits for another.
 template <bool W2D, bool FUSED, bool FULL, int WIN>
 __global__ __launch_bounds__(kDecWaves * 64) void k_gemm_decode(SmallMArgs p) {
-  __shared__ floatx4_t s_red[2][kDecWaves][kWave];
+  constexpr int D = dec_depth(WIN, FULL && !FUSED);
+  __shared__ floatx4_t s_red[D][kDecWaves][kWave];
   __shared__ QuantTables tab;
   __shared__ uint32_t red[kDecWaves];
   // Quantized A slice of each wave (fused form): up to 16 rows x 16 blocks.
@@ -1110,38 +1122,46 @@ __global__ __launch_bounds__(kDecWaves * 64) void k_gemm_decode(SmallMArgs p) {
   const int64_t nbands = (p.n + 15) / 16;
   const WBufs buf = make_wbufs(p);
   // Read before any load of A or W is issued, so that waiting for it waits for nothing else.
-  const float gs_w = *p.w.gs, gs_a_in = FUSED ? 0.0f : *p.a.gs;
+  const float gs_w = load_global_scale(p.w.gs);
+  const float gs_a_in = FUSED ? 0.0f : load_global_scale(p.a.gs);
 
   // This wave's K slice of A, decoded once: window u, K step kk -> 8 fp16 values of A row i16.
   half8_t aop[WIN][4];
   float gs_a = 0.0f;
-  DecodeW<WIN> ring[dec_depth(WIN)];
+  DecodeW<WIN> ring[D];
   if (FUSED) {
     // Each wave loads its own K slice of all m rows of A, coalesced: step j gives lane l the
     // 16-value block j * 64 + l of the slice (row = block / bps, bps blocks per row); lanes past
     // the slice reload its last block (or A's first block when the slice is empty), which leaves
-    // the maximum unchanged.  These loads go out before W's, so waiting for them does not wait
-    // for W.  The registers give this workgroup's share of the global amax and are then encoded
-    // in place; the codes reach the MFMA layout through the wave's own corner of LDS.
+    // the maximum unchanged; steps wholly past the slice load nothing.  The registers give this
+    // workgroup's share of the global amax and are then encoded in place; the codes reach the
+    // MFMA layout through the wave's own corner of LDS.  W's ring is issued once every wave
+    // holds its A: issued earlier, the A loads of the later waves wait behind the W stream of
+    // the whole chip (measured: A of the last wave slot about 2 us after the first), and the
+    // amax that every wave needs waits for the last of them.
     const int64_t kb0 = win0 * 8;                                       // first block of the slice
     const int bps = (int)max((int64_t)0, min(per * 8, kblocks - kb0));  // blocks per row
     const int nblk = (int)p.m * bps;                                    // <= 16 * 16
     uint4 xa[4][2];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int blk = min(j * 64 + lane, max(nblk - 1, 0));
-      const int r = bps > 0 ? blk / bps : 0, c = bps > 0 ? blk - r * bps : 0;
-      const uint16_t *src = p.a_bf16 + r * p.ld_a + (bps > 0 ? kb0 + c : 0) * 16;
-      xa[j][0] = *(const uint4 *)src;
-      xa[j][1] = *(const uint4 *)(src + 8);
+      if (j == 0 || j * 64 < nblk) {  // steps past the slice (small M) load nothing
+        const int blk = min(j * 64 + lane, max(nblk - 1, 0));
+        const int r = bps > 0 ? blk / bps : 0, c = bps > 0 ? blk - r * bps : 0;
+        const uint16_t *src = p.a_bf16 + r * p.ld_a + (bps > 0 ? kb0 + c : 0) * 16;
+        xa[j][0] = *(const uint4 *)src;
+        xa[j][1] = *(const uint4 *)(src + 8);
+      } else {
+        xa[j][0] = xa[j][1] = make_uint4(0u, 0u, 0u, 0u);
+      }
     }
-    decode_ring_start<W2D, FULL, WIN>(p, buf, nbands, i16, q, win0, nw, ring);
     uint32_t mx = 0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) mx = max(mx, absmax16(xa[j][0], xa[j][1]));
     mx = wave_max_u32(mx);
     if (lane == 0) red[wave] = mx;
     __syncthreads();
+    decode_ring_start<W2D, FULL, WIN>(p, buf, nbands, i16, q, win0, nw, ring);
     mx = red[0];
 #pragma unroll
     for (int w2 = 1; w2 < kDecWaves; ++w2) mx = max(mx, red[w2]);
@@ -1257,7 +1277,8 @@ __device__ __forceinline__ bf16x8_t load_a_bf16x8(const uint16_t *row, int64_t k
 // K <= 4096: the decode form above with bf16 A held in registers.
 template <bool W2D, bool FULL, int WIN>
 __global__ __launch_bounds__(kDecWaves * 64) void k_gemm_w4a16_decode(SmallMArgs p) {
-  __shared__ floatx4_t s_red[2][kDecWaves][kWave];
+  constexpr int D = dec_depth(WIN, FULL);
+  __shared__ floatx4_t s_red[D][kDecWaves][kWave];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int i16 = lane & 15, q = lane >> 4;
   const int64_t nwin = (p.k + 127) / 128;
@@ -1266,7 +1287,7 @@ __global__ __launch_bounds__(kDecWaves * 64) void k_gemm_w4a16_decode(SmallMArgs
   const int nw = (int)max((int64_t)0, min(per, nwin - win0));
   const int64_t nbands = (p.n + 15) / 16;
   const WBufs buf = make_wbufs(p);
-  const float gs_w = *p.w.gs;  // read before the loads of A and W are issued
+  const float gs_w = load_global_scale(p.w.gs);  // read before the loads of A and W are issued
 
   bf16x8_t aop[WIN][4];
   if (FULL) {
@@ -1286,7 +1307,7 @@ __global__ __launch_bounds__(kDecWaves * 64) void k_gemm_w4a16_decode(SmallMArgs
       for (int kk = 0; kk < 4; ++kk)
         aop[u][kk] = load_a_bf16x8(arow, (win0 + u) * 128 + q * 32 + kk * 8, p.k, a_ok && u < nw);
   }
-  DecodeW<WIN> ring[dec_depth(WIN)];
+  DecodeW<WIN> ring[D];
   decode_ring_start<W2D, FULL, WIN>(p, buf, nbands, i16, q, win0, nw, ring);
 
   decode_band_loop<W2D, FULL, WIN>(
@@ -1374,7 +1395,7 @@ __global__ __launch_bounds__(kDecWaves * 64) void k_gemv_w4a16(SmallMArgs p) {
   const int64_t g = (int64_t)gridDim.x * kDecWaves;
   const int64_t first = (int64_t)blockIdx.x * kDecWaves + wave;
   const WBufs buf = make_wbufs(p);
-  const float alpha = *p.w.gs;
+  const float alpha = load_global_scale(p.w.gs);
 
   // A (one row) is read from memory once per workgroup into LDS (thread t copies 16-byte chunk
   // t; its load goes out before the W loads, so waiting for it waits for nothing else); every
@@ -1441,6 +1462,7 @@ constexpr int kW16Chunk = 4;
 template <bool W2D>
 __global__ __launch_bounds__(kDecWaves * 64) void k_gemm_w4a16_stream(SmallMArgs p) {
   __shared__ floatx4_t s_red[kDecWaves][kWave];
+  const float gs_w = load_global_scale(p.w.gs);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int i16 = lane & 15, q = lane >> 4;
   const int64_t band = blockIdx.x;
@@ -1490,7 +1512,7 @@ __global__ __launch_bounds__(kDecWaves * 64) void k_gemm_w4a16_stream(SmallMArgs
 #pragma unroll
     for (int w2 = 0; w2 < kDecWaves; ++w2) t += ((const float *)&s_red[w2][lane])[wave];
     const int64_t n = band * 16 + 4 * q + wave;
-    if (n < p.n) ntstore_u16(p.y + (int64_t)i16 * p.ld_y + n, f32_to_bf16_rne(t * (*p.w.gs)));
+    if (n < p.n) ntstore_u16(p.y + (int64_t)i16 * p.ld_y + n, f32_to_bf16_rne(t * gs_w));
   }
 }
 
@@ -1507,6 +1529,7 @@ constexpr int kMidDepth = 4;
 template <int FM, bool W2D>
 __global__ __launch_bounds__(kGemmThreads) void k_gemm_mid(DenseArgs p) {
   __shared__ float s_red[4][FM][2][16][kWave];  // [wave][f][g][register][lane]
+  const float alpha = load_global_scale(p.a.gs) * load_global_scale(p.w.gs);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lr = lane & 31, kh = lane >> 5;
@@ -1579,7 +1602,6 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_mid(DenseArgs p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) s_red[wave][f][g][r][lane] = acc[f][g][r];
   __syncthreads();
-  const float alpha = (*p.a.gs) * (*p.w.gs);
 #pragma unroll
   for (int t = 0; t < FM / 2; ++t) {
     const int tile = wave * (FM / 2) + t, f = tile >> 1, g = tile & 1;

@@ -41,6 +41,16 @@ __device__ __forceinline__ int code_offset(int row, int h) {
   return row * 32 + ((h ^ (row >> 2) ^ (row >> 3)) & 1) * 16;
 }
 
+// A global scale read with a vector load.  A uniform read would be a scalar load, which the
+// compiler may issue after the operand loads, and scalar loads share their wait counter with
+// LDS: the first LDS barrier would then wait for it behind the whole stream of W (the rotated
+// weights of a decode loop are not in cache).  Issued before the operand loads, a vector load is
+// also waited for before them, since loads complete in order.
+__device__ __forceinline__ float load_global_scale(const float *p) {
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void *)p, 0, 4, 0x00020000);
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, 0, 0, 0));
+}
+
 // Two floats to bf16, round to nearest even, in one packed conversion (v_cvt_pk_bf16_f32),
 // element 0 in the low half.  The kernels keep fp32 denormals, so this equals the bit-level
 // rounding (add 0x7FFF plus the kept lsb, shift) for every value that is not a NaN.

@@ -1522,11 +1522,14 @@ __global__ __launch_bounds__(kDecWaves * 64) void k_gemm_w4a16_stream(SmallMArgs
 // slice.  The 4 waves split K in four contiguous quarters; each wave computes the whole tile
 // over its quarter (FM x 2 MFMA tiles of 32 x 32) with four 64-wide windows of loads in flight,
 // and the four partial tiles are added through LDS.  W is read once per row slice of A;
-// nothing but Y goes to memory.  FM = 2 leaves room for two workgroups per CU.
+// nothing but Y goes to memory.  FM = 2 leaves room for two workgroups per CU.  SCV (scale rows
+// 16-byte aligned): the scales of a round of four windows come in one 16-byte load per
+// fragment row (a 32-bit word per window; lane half kh takes its two bytes by a shift), in
+// place of a 16-bit load per window.
 // ---------------------------------------------------------------------------------------------
 constexpr int kMidDepth = 4;
 
-template <int FM, bool W2D>
+template <int FM, bool W2D, bool SCV>
 __global__ __launch_bounds__(kGemmThreads) void k_gemm_mid(DenseArgs p) {
   __shared__ float s_red[4][FM][2][16][kWave];  // [wave][f][g][register][lane]
   const float alpha = load_global_scale(p.a.gs) * load_global_scale(p.w.gs);
@@ -1545,13 +1548,14 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_mid(DenseArgs p) {
   for (int f = 0; f < FM; ++f) {
     const int64_t r = min(m0 + f * 32 + lr, p.m - 1);
     a_row[f] = p.a.codes + r * p.a.ld_codes + kh * 16 + w_first * 32;
-    a_srow[f] = p.a.scales + r * p.a.ld_scales + kh * 2 + w_first * 4;
+    a_srow[f] = p.a.scales + r * p.a.ld_scales + (SCV ? 0 : kh * 2) + w_first * 4;
   }
 #pragma unroll
   for (int g = 0; g < 2; ++g) {
     const int64_t r = min(n0 + g * 32 + lr, p.n - 1);
     w_row[g] = p.w.codes + r * p.w.ld_codes + kh * 16 + w_first * 32;
-    w_srow[g] = p.w.scales + (W2D ? (r >> 4) : r) * p.w.ld_scales + kh * 2 + w_first * 4;
+    w_srow[g] = p.w.scales + (W2D ? (r >> 4) : r) * p.w.ld_scales + (SCV ? 0 : kh * 2) +
+                w_first * 4;
   }
   floatx16_t acc[FM][2];
 #pragma unroll
@@ -1567,15 +1571,34 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_mid(DenseArgs p) {
 #pragma unroll
     for (int f = 0; f < FM; ++f) {
       fr.a[f] = load16(a_row[f] + win * 32);
-      fr.sa[f] = *(const uint16_t *)(a_srow[f] + win * 4);
+      if (!SCV) fr.sa[f] = *(const uint16_t *)(a_srow[f] + win * 4);
     }
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
       fr.w[g] = load16(w_row[g] + win * 32);
-      fr.sw[g] = *(const uint16_t *)(w_srow[g] + win * 4);
+      if (!SCV) fr.sw[g] = *(const uint16_t *)(w_srow[g] + win * 4);
     }
   };
+  struct RoundScales {
+    uint4 a[FM], w[2];
+  };
+  static_assert(kMidDepth == 4, "a 16-byte scale load covers four windows");
+  auto load_scales = [&](RoundScales &q, int64_t win) {
+#pragma unroll
+    for (int f = 0; f < FM; ++f) q.a[f] = *(const uint4 *)(a_srow[f] + win * 4);
+#pragma unroll
+    for (int g = 0; g < 2; ++g) q.w[g] = *(const uint4 *)(w_srow[g] + win * 4);
+  };
+  const uint32_t ssh = 16u * kh;
+  auto set_scales = [&](Frags<FM, 2> &fr, const RoundScales &q, int j) {
+#pragma unroll
+    for (int f = 0; f < FM; ++f) fr.sa[f] = word(q.a[f], j) >> ssh;
+#pragma unroll
+    for (int g = 0; g < 2; ++g) fr.sw[g] = word(q.w[g], j) >> ssh;
+  };
   Frags<FM, 2> ring[kMidDepth];
+  RoundScales cur, nxt;
+  if (SCV) load_scales(cur, 0);
 #pragma unroll
   for (int j = 0; j < kMidDepth; ++j) {
     load(ring[j], j);
@@ -1584,14 +1607,20 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_mid(DenseArgs p) {
   for (int64_t i = 0; i + kMidDepth < wpw; i += kMidDepth) {
 #pragma unroll
     for (int j = 0; j < kMidDepth; ++j) {
+      if (SCV) set_scales(ring[j], cur, j);
       compute_window(ring[j], acc);
       __builtin_amdgcn_sched_barrier(0);
+      if (SCV && j == 0) load_scales(nxt, i + kMidDepth);
       load(ring[j], i + j + kMidDepth);
       __builtin_amdgcn_sched_barrier(0);
     }
+    if (SCV) cur = nxt;
   }
 #pragma unroll
-  for (int j = 0; j < kMidDepth; ++j) compute_window(ring[j], acc);
+  for (int j = 0; j < kMidDepth; ++j) {
+    if (SCV) set_scales(ring[j], cur, j);
+    compute_window(ring[j], acc);
+  }
 
   // Add the four quarters: every wave stores its tile, then wave q finishes MFMA tiles
   // t = q * FM / 2 .. (q + 1) * FM / 2 - 1 (tile t is (t / 2, t % 2)) from all four copies.
@@ -1709,10 +1738,16 @@ hipError_t launch_gemm_tile(const GemmOperand &a, const GemmOperand &w, int64_t 
     p.tiles_m = (int)((m + 63) / 64);
     p.tiles_n = (int)((n + 63) / 64);
     const unsigned grid = (unsigned)p.tiles_m * (unsigned)p.tiles_n;
-    if (w.block_rows == 16)
-      hipLaunchKernelGGL((k_gemm_mid<2, true>), dim3(grid), dim3(kGemmThreads), 0, stream, p);
+    const bool scv = (uintptr_t)a.scales % 16 == 0 && (uintptr_t)w.scales % 16 == 0 &&
+                     a.ld_scales % 16 == 0 && w.ld_scales % 16 == 0;
+    if (w.block_rows == 16 && scv)
+      hipLaunchKernelGGL((k_gemm_mid<2, true, true>), dim3(grid), dim3(kGemmThreads), 0, stream, p);
+    else if (w.block_rows == 16)
+      hipLaunchKernelGGL((k_gemm_mid<2, true, false>), dim3(grid), dim3(kGemmThreads), 0, stream, p);
+    else if (scv)
+      hipLaunchKernelGGL((k_gemm_mid<2, false, true>), dim3(grid), dim3(kGemmThreads), 0, stream, p);
     else
-      hipLaunchKernelGGL((k_gemm_mid<2, false>), dim3(grid), dim3(kGemmThreads), 0, stream, p);
+      hipLaunchKernelGGL((k_gemm_mid<2, false, false>), dim3(grid), dim3(kGemmThreads), 0, stream, p);
     return hipGetLastError();
   }
   if (m <= 64) return launch_tile_fm<1, 4>(a, w, m, n, k, y, ld_y, part, stream);

@@ -1911,8 +1911,12 @@ hipError_t launch_gemm_w4a16(const void *a_bf16, int64_t ld_a, const GemmOperand
   p.aq_codes = p.aq_scales = nullptr;
   p.aq_gs = nullptr;
   const bool w2d = w.block_rows == 16;
-  if (const int nb = gemv_nb(p)) return launch_gemv_w4a16(p, nb, stream);
-  if ((k + 127) / 128 <= kDecWaves * kDecWin) {
+  // One activation row takes the band kernel where its full-window form applies (0.6-0.9 us
+  // faster than the GEMV at 14336 x 4096); the GEMV serves the longer K it also covers.
+  const bool dec_fits = (k + 127) / 128 <= kDecWaves * kDecWin;
+  if (!(dec_fits && decode_full(p)))
+    if (const int nb = gemv_nb(p)) return launch_gemv_w4a16(p, nb, stream);
+  if (dec_fits) {
     const bool full = decode_full(p);
     const bool one = (k + 127) / 128 <= kDecWaves;
     if (full && one) launch_w4a16_t<true, 1>(p, w2d, stream);

@@ -84,15 +84,16 @@ def test_prequantized_a(nv, m):
     check_gemm(y, y64, what=f"prequantized m={m}")
 
 
-# A single activation row with K = 2048, 4096 or 8192 takes the GEMV form; with bf16 A the
-# activation is quantized inside it (K <= 4096), and the quantized A it writes is checked.
+# A single activation row: K <= 4096 takes the decode kernel, which quantizes the bf16
+# activation inside it (the quantized A it writes is checked); K = 8192 a quantize launch and
+# the small-M kernel.
 @pytest.mark.parametrize("n,k,br", [(1000, 2048, 1), (4112, 4096, 16), (272, 8192, 16),
                                     (48, 4096, 1)])
 def test_single_row_shapes(nv, n, k, br):
     rng = np.random.default_rng(n * 3 + k + br)
     a = W.to_bf16_bits(W.normal_with_outliers(rng, 1, k, 0.01, 20.0))
     w = W.to_bf16_bits(rng.standard_normal((n, k)) * 0.02)
-    _, y, y64, aq, wq = run_dense(nv, a, w, br, f"gemv 1x{n}x{k} b{br}")
+    _, y, y64, aq, wq = run_dense(nv, a, w, br, f"single row 1x{n}x{k} b{br}")
     y_pre = nv.gemm_w4a4(aq, wq)          # the prequantized form of the same product
     assert torch.equal(y, y_pre)
 

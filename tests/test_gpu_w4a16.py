@@ -48,18 +48,18 @@ def test_shapes(nv, m, n, k, br):
     check_gemm(y, O.gemm64_w4a16(a, ow), what=f"w4a16 {m}x{n}x{k} b{br}")
 
 
-# A single activation row: with N >= 8192 and K = 2048, 4096 or 8192 the GEMV form runs (no
-# MFMA, no LDS reduction), otherwise the decode forms.
+# A single activation row: K <= 4096 (K a multiple of 128) runs the band kernel; with N >= 8192
+# and K = 8192 the GEMV form (no MFMA, no LDS reduction); other shapes the streaming form.
 @pytest.mark.parametrize("n,k,br", [(1000, 2048, 1), (4112, 4096, 16), (272, 8192, 16),
                                     (48, 4096, 1), (18, 2048, 1), (8200, 2048, 1),
-                                    (8208, 4096, 16)])
+                                    (8208, 4096, 16), (8192, 8192, 1)])
 def test_single_row_shapes(nv, n, k, br):
     rng = np.random.default_rng(n + k + br)
     a = W.to_bf16_bits(W.normal_with_outliers(rng, 1, k, 0.01, 20.0))
     w = W.to_bf16_bits(rng.standard_normal((n, k)) * 0.02)
     wq, ow = quantized_w(nv, w, br, f"1x{n}x{k}")
     y = nv.gemm_w4a16(dev_bf16(a), wq)
-    check_gemm(y, O.gemm64_w4a16(a, ow), what=f"w4a16 gemv 1x{n}x{k} b{br}")
+    check_gemm(y, O.gemm64_w4a16(a, ow), what=f"w4a16 single row 1x{n}x{k} b{br}")
 
 
 def test_single_row_long_k_sampled(nv):

@@ -206,6 +206,26 @@ def extra_workloads(args, torch, np, nv, W, only):
                                 "frac": tf / FP4_MFMA_PEAK_TFLOPS,
                                 "note": "includes the MXFP4 quantization of A inside the call"}
         del a, wq, y
+        # Decode-shaped MXFP4 products against the decode weight (14336 x 4096) rotating over 10
+        # copies so that W comes from HBM; the activation is quantized inside each call.
+        d = W.decode(ms=(1, 16, 64))
+        wq0 = nv.mxfp4_quantize(dev_bf16(torch, np, d["w"]))
+        nw = 10
+        wqs = [wq0] + [nv.MxTensor(wq0.codes.clone(), wq0.scales.clone(), wq0.rows, wq0.cols)
+                       for _ in range(nw - 1)]
+        n, k = 14336, 4096
+        for m, a_host in d["a"].items():
+            a = dev_bf16(torch, np, a_host)
+            y = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+            ws = nv.Workspace.get(nv.lib().nvfp4_mxfp4_gemm_workspace_bytes(m, k), a.device)
+            ms = timed(lambda i: nv.mxfp4_gemm(a, wqs[i % nw], y=y, ws=ws), steps, warm, torch)
+            nbytes = n * k // 2 + n * k // 32 + m * k * 2 + m * n * 2
+            gbs = nbytes / (ms * 1e-3) / 1e9
+            out[f"mxfp4_decode_m{m}"] = {
+                "shape": [m, n, k], "ms": ms, "bound": "hbm", "achieved": gbs, "unit": "GB/s",
+                "frac": gbs / HBM_PEAK_GBS, "tflops": 2 * m * n * k / (ms * 1e-3) / 1e12,
+                "note": "includes the MXFP4 quantization of A inside the call"}
+        del wqs, wq0
 
     if not only or "mse" in only:
         # Offline weight quantization with MSE-observer block scales (16x16 tiles) of the decode

@@ -257,8 +257,9 @@ nvfp4_status nvfp4_mxfp4_dequantize(const mxfp4_tensor *q, void *y, int64_t ld_y
  *   Y[m, n] = RN_bf16( sum_k (cA * XA)[m, k] * (cW * XW)[n, k] ).
  * The products run on CDNA4's scaled FP4 MFMA, which applies the E8M0 scales itself.
  *   a_bf16 : if not NULL, device bf16 activations (m x k, ld_a as for the quantize) quantized
- *            to MXFP4 inside the call (into a_q's buffers when a_q is not NULL, else into the
- *            workspace); if NULL, a_q is the already quantized A.
+ *            to MXFP4 inside the call (written to a_q's buffers when a_q is not NULL; otherwise
+ *            an intermediate, held in the workspace or, for m <= 4, inside the product kernel);
+ *            if NULL, a_q is the already quantized A.
  *   w      : n = w->rows, w->cols == k.   y : device bf16 m x n, row stride ld_y, 4-byte
  *            aligned, ld_y % 2 == 0.   k % 32 == 0.
  *   ws     : nvfp4_mxfp4_gemm_workspace_bytes(m, k) bytes, 256-byte aligned (may be NULL with

@@ -454,6 +454,13 @@ nvfp4_status nvfp4_mxfp4_gemm(const void *a_bf16, int64_t m, int64_t k, int64_t 
     ld_as = L.ld_scales;
   }
   if (a_bf16) {
+    // Small M: one launch that quantizes A itself (writing it only to a_q, if given).
+    bool launched = false;
+    const hipError_t e = launch_mx_gemm_fused(
+        a_bf16, ld_a, a_q ? (uint8_t *)ac : nullptr, ld_ac, a_q ? (uint8_t *)as : nullptr, ld_as,
+        w->codes, w->ld_codes, w->scales, w->ld_scales, m, n, k, (uint16_t *)y, ld_y, st,
+        &launched);
+    if (launched) return hip_status(e);
     s = hip_status(launch_mx_quantize(a_bf16, m, k, ld_a, (uint8_t *)ac, ld_ac, (uint8_t *)as,
                                       ld_as, st));
     if (s) return s;

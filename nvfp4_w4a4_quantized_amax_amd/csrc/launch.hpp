@@ -116,5 +116,12 @@ hipError_t launch_mx_gemm(const uint8_t *a_codes, int64_t ld_ac, const uint8_t *
                           int64_t ld_as, const uint8_t *w_codes, int64_t ld_wc,
                           const uint8_t *w_scales, int64_t ld_ws, int64_t m, int64_t n, int64_t k,
                           uint16_t *y, int64_t ld_y, hipStream_t stream);
+// Small M with bf16 activations in one launch; *launched is false when the shape does not fit
+// (nothing launched).
+hipError_t launch_mx_gemm_fused(const void *a_bf16, int64_t ld_a, uint8_t *aq_codes,
+                                int64_t ld_aqc, uint8_t *aq_scales, int64_t ld_aqs,
+                                const uint8_t *w_codes, int64_t ld_wc, const uint8_t *w_scales,
+                                int64_t ld_ws, int64_t m, int64_t n, int64_t k, uint16_t *y,
+                                int64_t ld_y, hipStream_t stream, bool *launched);
 
 }  // namespace nvfp4

@@ -113,6 +113,12 @@ struct MxArgs {
   uint16_t *y;
   int64_t ld_y;
   int tiles_m, tiles_n;
+  // Activation quantized inside the product (k_gemm_mx_mid, small M): bf16 A, and where
+  // workgroup 0 writes its MXFP4 form (null: nowhere).
+  const uint16_t *a_bf16;
+  int64_t ld_a;
+  uint8_t *aq_codes, *aq_scales;
+  int64_t ld_aqc, ld_aqs;
 };
 
 __device__ __forceinline__ floatx16_t mx_mfma(const u32x4_t &a, const u32x4_t &w, uint32_t sa,
@@ -518,6 +524,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 // 8 bytes (4 windows) per row and load: lane half kh shifts the word by 8 kh, and the MFMA's
 // scale select picks byte 0 or 2 of each 32-bit half.  K must be a multiple of 256 * DEPTH and
 // scale rows 8-byte aligned; W is read once per 32FM-row slice of A.
+// FA (one row tile, M * K <= kMxFaMaxValues): A arrives as bf16 and every workgroup quantizes
+// all of it into LDS exactly as k_mx_quantize does (8-value chunks, the four lanes of a block
+// sharing its maximum); its loads go out before W's, so waiting for them waits for nothing
+// else, and workgroup 0 also writes the quantized A when asked to.
 template <int FM, int FN>
 struct MxMidWin {
   u32x4_t a[FM], w[FN];
@@ -528,10 +538,16 @@ struct MxMidScales {
   uint2 a[FM][DEPTH / 4], w[FN][DEPTH / 4];
 };
 
-template <int FM, int FN, int DEPTH>
+constexpr int kMxFaChunks = 8;                        // 8-value chunks of A per thread
+constexpr int64_t kMxFaMaxValues = kMxFaChunks * 8 * 256;  // 16384
+
+template <int FM, int FN, int DEPTH, bool FA>
 __global__ __launch_bounds__(256) void k_gemm_mx_mid(MxArgs p) {
   static_assert(DEPTH % 4 == 0, "a scale load covers 4 windows");
+  static_assert(!FA || FM == 1, "the fused activation is one row tile");
   __shared__ float s_red[4][FM][FN][16][kWave];  // [wave][f][g][register][lane]
+  // FA: A's codes (m rows of k / 2 bytes), then its scales (m rows of k / 32 bytes).
+  extern __shared__ __align__(16) uint8_t s_fa[];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lr = lane & 31, kh = lane >> 5;
@@ -555,14 +571,34 @@ __global__ __launch_bounds__(256) void k_gemm_mx_mid(MxArgs p) {
     wc[g] = p.w_codes + rw * p.ld_wc + kh * 16 + w_first * 32;
     ws[g] = p.w_scales + rw * p.ld_ws + w_first * 2;
   }
+  // FA: this lane's rows of A in LDS (one row tile: m0 = 0).
+  const int64_t fa_row = min((int64_t)lr, p.m - 1);
+  const uint8_t *lac = s_fa + fa_row * (p.k / 2) + kh * 16 + w_first * 32;
+  const uint8_t *las = s_fa + p.m * (p.k / 2) + fa_row * (p.k / 32) + kh + w_first * 2;
   floatx16_t acc[FM][FN];
 #pragma unroll
   for (int f = 0; f < FM; ++f)
 #pragma unroll
     for (int g = 0; g < FN; ++g) acc[f][g] = floatx16_t{};
-  auto load = [&](MxMidWin<FM, FN> &r, int64_t win) {
+  // FA: A's 8-value chunks u = threadIdx.x + 256 t, loaded before any load of W (past the
+  // end: the last chunk again, never stored).
+  // (fa_n <= 2048: 32-bit arithmetic.)
+  const uint32_t fa_cpr = (uint32_t)(p.k / 8), fa_n = (uint32_t)p.m * fa_cpr;
+  uint4 xa[FA ? kMxFaChunks : 1];
+  if (FA) {
 #pragma unroll
-    for (int f = 0; f < FM; ++f) r.a[f] = *(const u32x4_t *)(ac[f] + win * 32);
+    for (int t = 0; t < kMxFaChunks; ++t) {
+      const uint32_t u = min(threadIdx.x + 256u * t, fa_n - 1u);
+      const uint32_t r = u / fa_cpr, c = u - r * fa_cpr;
+      xa[t] = *(const uint4 *)(p.a_bf16 + (int64_t)r * p.ld_a + c * 8);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  auto load = [&](MxMidWin<FM, FN> &r, int64_t win) {
+    if (!FA) {
+#pragma unroll
+      for (int f = 0; f < FM; ++f) r.a[f] = *(const u32x4_t *)(ac[f] + win * 32);
+    }
 #pragma unroll
     for (int g = 0; g < FN; ++g) r.w[g] = *(const u32x4_t *)(wc[g] + win * 32);
   };
@@ -571,24 +607,29 @@ __global__ __launch_bounds__(256) void k_gemm_mx_mid(MxArgs p) {
 #pragma unroll
     for (int f = 0; f < FM; ++f)
 #pragma unroll
-      for (int u = 0; u < DEPTH / 4; ++u) q.a[f][u] = *(const uint2 *)(as[f] + (win + 4 * u) * 2);
+      for (int u = 0; u < DEPTH / 4; ++u)
+        if (!FA) q.a[f][u] = *(const uint2 *)(as[f] + (win + 4 * u) * 2);
 #pragma unroll
     for (int g = 0; g < FN; ++g)
 #pragma unroll
       for (int u = 0; u < DEPTH / 4; ++u) q.w[g][u] = *(const uint2 *)(ws[g] + (win + 4 * u) * 2);
   };
-  // window j of the round whose scales are q
-  auto compute = [&](const MxMidWin<FM, FN> &r, const MxMidScales<FM, FN, DEPTH> &q, int j) {
+  // window j of the round whose scales are q (window win of the wave's share; FA reads A's
+  // operand and scale byte from LDS, the byte moved to where the scale select looks)
+  auto compute = [&](const MxMidWin<FM, FN> &r, const MxMidScales<FM, FN, DEPTH> &q, int j,
+                     int64_t win) {
 #pragma unroll
     for (int f = 0; f < FM; ++f) {
-      const uint32_t sa = ((j >> 1) & 1 ? q.a[f][j >> 2].y : q.a[f][j >> 2].x) >> sh;
+      const u32x4_t av = FA ? *(const u32x4_t *)(lac + win * 32) : r.a[f];
+      const uint32_t sa = FA ? (uint32_t)las[win * 2] << ((j & 1) ? 16 : 0)
+                             : ((j >> 1) & 1 ? q.a[f][j >> 2].y : q.a[f][j >> 2].x) >> sh;
 #pragma unroll
       for (int g = 0; g < FN; ++g) {
         const uint32_t sw = ((j >> 1) & 1 ? q.w[g][j >> 2].y : q.w[g][j >> 2].x) >> sh;
         if (j & 1)
-          acc[f][g] = mx_mfma_sel<2>(r.a[f], r.w[g], sa, sw, acc[f][g]);
+          acc[f][g] = mx_mfma_sel<2>(av, r.w[g], sa, sw, acc[f][g]);
         else
-          acc[f][g] = mx_mfma_sel<0>(r.a[f], r.w[g], sa, sw, acc[f][g]);
+          acc[f][g] = mx_mfma_sel<0>(av, r.w[g], sa, sw, acc[f][g]);
       }
     }
   };
@@ -602,10 +643,35 @@ __global__ __launch_bounds__(256) void k_gemm_mx_mid(MxArgs p) {
     load(ring[j], j);
     __builtin_amdgcn_sched_barrier(0);
   }
-  for (int64_t i = 0; i + DEPTH < wpw; i += DEPTH) {
+  if (FA) {
+    // Quantize A into LDS (and, from workgroup 0, into the caller's buffers).  fa_n and 256 are
+    // multiples of 4, so the four lanes of a block are in or out together.
+    uint8_t *sac = s_fa, *sas = s_fa + p.m * (p.k / 2);
+#pragma unroll
+    for (int t = 0; t < kMxFaChunks; ++t) {
+      const uint32_t u = threadIdx.x + 256u * t;
+      uint32_t mm = absmax8(xa[t]);
+      mm = max(mm, (uint32_t)__shfl_xor((int)mm, 1, kWave));
+      mm = max(mm, (uint32_t)__shfl_xor((int)mm, 2, kWave));
+      if (u < fa_n) {
+        const uint32_t r = u / fa_cpr, c = u - r * fa_cpr;
+        const int e = mx_exponent(mm);
+        const uint32_t qv = encode8_fast(xa[t], mx_inv_scale(e));
+        *(uint32_t *)(sac + r * (fa_cpr * 4) + c * 4) = qv;
+        if ((c & 3) == 0) sas[r * (fa_cpr / 4) + (c >> 2)] = (uint8_t)(e + 127);
+        if (blockIdx.x == 0 && p.aq_codes) {
+          *(uint32_t *)(p.aq_codes + (int64_t)r * p.ld_aqc + c * 4) = qv;
+          if ((c & 3) == 0) p.aq_scales[(int64_t)r * p.ld_aqs + (c >> 2)] = (uint8_t)(e + 127);
+        }
+      }
+    }
+    __syncthreads();
+  }
+  int64_t i = 0;
+  for (; i + DEPTH < wpw; i += DEPTH) {
 #pragma unroll
     for (int j = 0; j < DEPTH; ++j) {
-      compute(ring[j], cur, j);
+      compute(ring[j], cur, j, i + j);
       __builtin_amdgcn_sched_barrier(0);
       if (j == 0) load_scales(nxt, i + DEPTH);
       load(ring[j], i + j + DEPTH);
@@ -614,7 +680,7 @@ __global__ __launch_bounds__(256) void k_gemm_mx_mid(MxArgs p) {
     cur = nxt;
   }
 #pragma unroll
-  for (int j = 0; j < DEPTH; ++j) compute(ring[j], cur, j);
+  for (int j = 0; j < DEPTH; ++j) compute(ring[j], cur, j, i + j);
 
   // Add the four quarters.  The tile's FM * FN * 16 accumulator registers (in (f, g, register)
   // order) are shared out 4 * FM * FN to a wave; registers r and r + 1 hold adjacent rows.
@@ -715,17 +781,22 @@ hipError_t launch_mx_dequantize(const uint8_t *codes, int64_t ld_codes, const ui
 }
 
 // Launches k_gemm_mx_mid when K suits its ring, the scale rows are 8-byte aligned and the
-// shape makes at least 128 tiles; returns whether it did.
-template <int FM, int FN, int DEPTH>
+// shape makes at least 128 tiles (FA: and A fits the fused form); returns whether it did.
+template <int FM, int FN, int DEPTH, bool FA = false>
 static bool launch_mx_mid(MxArgs &p, hipStream_t stream) {
   const int64_t tiles_m = (p.m + 32 * FM - 1) / (32 * FM), tiles_n = (p.n + 32 * FN - 1) / (32 * FN);
-  if (p.k % (256 * DEPTH) != 0 || tiles_m * tiles_n < 128 || (uintptr_t)p.a_scales % 8 ||
-      (uintptr_t)p.w_scales % 8 || p.ld_as % 8 || p.ld_ws % 8)
+  if (p.k % (256 * DEPTH) != 0 || tiles_m * tiles_n < 128 || (uintptr_t)p.w_scales % 8 ||
+      p.ld_ws % 8)
+    return false;
+  if (!FA && ((uintptr_t)p.a_scales % 8 || p.ld_as % 8)) return false;
+  if (FA && (tiles_m != 1 || p.m * p.k > kMxFaMaxValues || (uintptr_t)p.a_bf16 % 16 ||
+             p.ld_a % 8 || (p.aq_codes && ((uintptr_t)p.aq_codes % 4 || p.ld_aqc % 4))))
     return false;
   p.tiles_m = (int)tiles_m;
   p.tiles_n = (int)tiles_n;
-  hipLaunchKernelGGL((k_gemm_mx_mid<FM, FN, DEPTH>), dim3((unsigned)(tiles_m * tiles_n)), dim3(256),
-                     0, stream, p);
+  const size_t lds = FA ? (size_t)(p.m * (p.k / 2 + p.k / 32)) : 0;
+  hipLaunchKernelGGL((k_gemm_mx_mid<FM, FN, DEPTH, FA>), dim3((unsigned)(tiles_m * tiles_n)),
+                     dim3(256), lds, stream, p);
   return true;
 }
 
@@ -774,6 +845,22 @@ hipError_t launch_mx_gemm(const uint8_t *a_codes, int64_t ld_ac, const uint8_t *
   const int64_t tiles = (int64_t)p.tiles_m * p.tiles_n;
   hipLaunchKernelGGL(k_gemm_mx_simple, dim3((unsigned)((tiles + 3) / 4)), dim3(256), 0, stream, p);
   return hipGetLastError();
+}
+
+// One launch for small M with bf16 activations: the activation is quantized inside the
+// mid-size kernel.  Sets *launched (and returns the launch status) only when the shape fits.
+hipError_t launch_mx_gemm_fused(const void *a_bf16, int64_t ld_a, uint8_t *aq_codes,
+                                int64_t ld_aqc, uint8_t *aq_scales, int64_t ld_aqs,
+                                const uint8_t *w_codes, int64_t ld_wc, const uint8_t *w_scales,
+                                int64_t ld_ws, int64_t m, int64_t n, int64_t k, uint16_t *y,
+                                int64_t ld_y, hipStream_t stream, bool *launched) {
+  *launched = false;
+  if (m > 4) return hipSuccess;
+  MxArgs p{nullptr, nullptr, w_codes, w_scales, 0, 0, ld_wc, ld_ws, m, n, k, y, ld_y, 0, 0,
+           (const uint16_t *)a_bf16, ld_a, aq_codes, aq_scales, ld_aqc, ld_aqs};
+  *launched = launch_mx_mid<1, 1, 16, true>(p, stream) || launch_mx_mid<1, 1, 8, true>(p, stream) ||
+              launch_mx_mid<1, 1, 4, true>(p, stream);
+  return *launched ? hipGetLastError() : hipSuccess;
 }
 
 }  // namespace nvfp4

@@ -138,8 +138,9 @@ def test_gemm_shapes(nv, m, n, k):
 
 # The mid-size kernel for M <= 128: each case names the (row tiles, column tiles, ring depth)
 # form the shape selects, by M range and by the K multiple (4096, 2048 or 1024) that fits the
-# ring; with too few 128-row tiles the 64-row form takes over.  W is checked on sampled rows
-# and Y on the sampled columns (the ragged last columns always among them).
+# ring; with too few 128-row tiles the 64-row form takes over.  With bf16 A and M <= 4 the
+# kernel quantizes A itself (the 1x1 cases), checked through the a_q it writes.  W is checked on
+# sampled rows and Y on the sampled columns (the ragged last columns always among them).
 @pytest.mark.parametrize("m,n,k,form", [
     (1, 8200, 1024, "1x1 depth 4"), (3, 4100, 2048, "1x1 depth 8"), (4, 4096, 4096, "1x1 depth 16"),
     (17, 8192, 1024, "1x2 depth 4"), (32, 8256, 2048, "1x2 depth 8"), (9, 8200, 4096, "1x2 depth 16"),
@@ -164,6 +165,8 @@ def test_gemm_mid_sizes(nv, m, n, k, form):
     assert_codes_equal(as_, oa[1], f"{form}: A scales")
     check_gemm(y.cpu()[:, cols], MX.gemm64_mx(oa, ow), what=f"mxfp4 mid {form} {m}x{n}x{k}")
     assert torch.equal(y, nv.mxfp4_gemm(aq, wq))
+    # without a_q (M <= 4: the activation quantized inside the product kernel, written nowhere)
+    assert torch.equal(y, nv.mxfp4_gemm(dev_bf16(a), wq))
 
 
 def test_gemm_unaligned_scale_rows(nv):

@@ -99,16 +99,20 @@ nvfp4_status check_bf16_input(const void *x, int64_t rows, int64_t cols, int64_t
 
 inline nvfp4_status hip_status(hipError_t e) { return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP; }
 
-// 1D quantization into explicit buffers, choosing the one-workgroup path for small tensors.
+// 1D quantization into explicit buffers, choosing the one-workgroup path for small tensors
+// and, ahead of a product in the same call (before_product), the two-kernel path for
+// mid-size ones.
 nvfp4_status run_quantize_1d(const void *x, int64_t rows, int64_t cols, int64_t ld_x,
                              uint8_t *codes, int64_t ld_codes, uint8_t *scales, int64_t ld_scales,
-                             float *gs, void *ws, hipStream_t stream) {
+                             float *gs, void *ws, hipStream_t stream, bool before_product) {
   if (rows * cols <= kSmallMaxElems)
     return hip_status(launch_quantize_small(x, rows, cols, ld_x, codes, ld_codes, scales,
                                             ld_scales, gs, stream));
-  const hipError_t e = launch_quantize_persistent(x, rows, cols, ld_x, codes, ld_codes, scales,
-                                                  ld_scales, gs, ws, stream);
-  if (e != hipErrorNotSupported) return hip_status(e);
+  if (!(before_product && rows * cols <= kTwoPassBeforeProductMaxElems)) {
+    const hipError_t e = launch_quantize_persistent(x, rows, cols, ld_x, codes, ld_codes, scales,
+                                                    ld_scales, gs, ws, stream);
+    if (e != hipErrorNotSupported) return hip_status(e);
+  }
   return hip_status(launch_quantize(x, rows, cols, ld_x, false, codes, ld_codes, scales,
                                     ld_scales, gs, ws, stream));
 }
@@ -164,7 +168,7 @@ nvfp4_status nvfp4_quantize_1d(const void *x, int64_t rows, int64_t cols, int64_
   if (ws_bytes < nvfp4_quantize_workspace_bytes(rows, cols) || !aligned(ws, kAlign))
     return NVFP4_ERR_WORKSPACE;
   return run_quantize_1d(x, rows, cols, ld_x, out->codes, out->ld_codes, out->scales,
-                         out->ld_scales, out->global_scale, ws, (hipStream_t)stream);
+                         out->ld_scales, out->global_scale, ws, (hipStream_t)stream, false);
 }
 
 nvfp4_status nvfp4_quantize_2d(const void *w, int64_t rows, int64_t cols, int64_t ld_w,
@@ -284,7 +288,7 @@ nvfp4_status nvfp4_gemm_w4a4(const void *a_bf16, int64_t m, int64_t k, int64_t l
   }
   if (a_bf16) {
     s = run_quantize_1d(a_bf16, m, k, ld_a, (uint8_t *)A.codes, A.ld_codes, (uint8_t *)A.scales,
-                        A.ld_scales, (float *)A.gs, ws, st);
+                        A.ld_scales, (float *)A.gs, ws, st, true);
     if (s) return s;
   }
   if (m <= kSmallM)
@@ -371,7 +375,7 @@ nvfp4_status nvfp4_grouped_gemm_w4a4(const void *a_bf16, int64_t tokens, int64_t
   }
   if (a_bf16) {
     s = run_quantize_1d(a_bf16, tokens, k, ld_a, (uint8_t *)A.codes, A.ld_codes,
-                        (uint8_t *)A.scales, A.ld_scales, (float *)A.gs, ws, st);
+                        (uint8_t *)A.scales, A.ld_scales, (float *)A.gs, ws, st, true);
     if (s) return s;
   }
   GemmOperand W{w->codes, w->ld_codes, w->scales, w->ld_scales, w->global_scale, w->block_rows};

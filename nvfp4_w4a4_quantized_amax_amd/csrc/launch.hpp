@@ -24,9 +24,10 @@ hipError_t launch_quantize_persistent(const void *x, int64_t rows, int64_t cols,
 constexpr int64_t kSmallMaxElems = 1 << 16;
 // An activation quantized inside a product call with at most this many values takes the
 // two-kernel path (amax, then encode) instead of the single-read kernel: measured 3-4 us faster
-// per call for 17-256 rows x 4096 ahead of the mid-size and split-K products, though on its own
-// the single-read kernel is the faster quantize.
-constexpr int64_t kTwoPassBeforeProductMaxElems = (int64_t)1 << 20;
+// per call for 17-256 rows x 4096 ahead of the mid-size and split-K products, and 8-9 us for
+// the 4096 x 2048 MoE activation, though on its own the single-read kernel is the faster
+// quantize.  At 8192 x 8192 (prefill) the single-read kernel stays ahead.
+constexpr int64_t kTwoPassBeforeProductMaxElems = (int64_t)1 << 23;
 hipError_t launch_quantize_small(const void *x, int64_t rows, int64_t cols, int64_t ld_x,
                                  uint8_t *codes, int64_t ld_codes, uint8_t *scales,
                                  int64_t ld_scales, float *gs_out, hipStream_t stream);

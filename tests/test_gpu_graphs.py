@@ -85,11 +85,13 @@ def test_gemm_w4a4_replays(nv, m):
         assert torch.equal(got, want)
 
 
-def test_mxfp4_gemm_replays(nv):
-    m, n, k = 300, 256, 512
-    rng = np.random.default_rng(34)
+@pytest.mark.parametrize("m,n,k", [(300, 256, 512), (2, 4096, 1024)])
+def test_mxfp4_gemm_replays(nv, m, n, k):
+    """M = 300: the quantize launch then the product; M = 2: one launch that quantizes A
+    itself and writes it to a_q."""
+    rng = np.random.default_rng(34 + m)
     wq = nv.mxfp4_quantize(dev_bf16(W.to_bf16_bits(rng.standard_normal((n, k)) * 0.02)))
-    xs = inputs(35, m, k)
+    xs = inputs(35 + m, m, k)
     a = dev_bf16(xs[0])
     aq = nv.empty_mxtensor(m, k)
     y = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")

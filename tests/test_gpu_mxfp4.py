@@ -146,6 +146,7 @@ def test_gemm_shapes(nv, m, n, k):
     (17, 8192, 1024, "1x2 depth 4"), (32, 8256, 2048, "1x2 depth 8"), (9, 8200, 4096, "1x2 depth 16"),
     (40, 8192, 1024, "2x2 depth 4"), (64, 8200, 2048, "2x2 depth 8"), (97, 8200, 1024, "4x2 depth 4"),
     (128, 8192, 2048, "4x2 depth 8"), (100, 4100, 2048, "2x2 depth 4 (too few 128-row tiles)"),
+    (4, 4100, 8192, "1x1 depth 16, A quantized by its own launch (M * K > 16384)"),
 ])
 def test_gemm_mid_sizes(nv, m, n, k, form):
     rng = np.random.default_rng(m * 11 + n + k)

@@ -92,7 +92,8 @@ int nvfp4_version(void);
  * Workspace.  Every call that takes `ws` needs at least the matching number of bytes, 256-byte
  * aligned; its contents need no initialization and carry nothing from one call to the next.  Its
  * first 8 KiB hold the per-workgroup partial maxima of the amax pass (and the grid-barrier slots
- * of the single-read quantizer); the rest holds the quantized activations of the GEMM calls.
+ * of the single-read quantizer); the rest holds the quantized activations of the GEMM calls
+ * and, for product shapes that split K across workgroups, their fp32 partial sums.
  * Calls that may overlap in time (different streams) need different workspaces.
  * ------------------------------------------------------------------------------------------- */
 size_t nvfp4_quantize_workspace_bytes(int64_t rows, int64_t cols);

@@ -3,7 +3,8 @@
  *
  * Plain C ABI: no C++ types, no exceptions, no torch types.  Every pointer named "device" is a
  * HIP device pointer; every call is asynchronous on `stream` (a hipStream_t passed as void*;
- * NULL means the default stream) and never synchronizes.  The caller owns every buffer; the
+ * NULL means the default stream) and never synchronizes (except for the opt-in NVFP4_DEBUG
+ * check of nvfp4_grouped_gemm_w4a4's routing arrays).  The caller owns every buffer; the
  * library allocates nothing per call and keeps no state between calls other than what is
  * written into the caller's workspace and a host counter that tags each call of the
  * single-read quantizer.  Calls may be captured into a HIP graph and replayed: on a capturing
@@ -111,9 +112,11 @@ size_t nvfp4_grouped_gemm_workspace_bytes(int64_t tokens, int64_t k, int64_t tot
  *   out    : out->codes / scales / global_scale receive the result; out->rows == rows,
  *            out->cols == cols, out->block_rows == 1; codes 16-byte aligned, ld_codes % 16 == 0.
  * Computes amax (pass 1) then block scales and codes (pass 2).  cols % 16 == 0.
- * Large tensors run as one workgroup per compute unit that read the tensor once and wait for
- * each other between the passes; should other work on the device keep some of them from
- * starting for about a second, the call writes NaN as the global scale instead of hanging.
+ * Large tensors run as one workgroup per compute unit, started with HIP's cooperative launch
+ * (all of them resident at once), that read the tensor once and wait for each other between the
+ * passes.  Where the cooperative launch is unavailable or refused, the call takes a two-kernel
+ * form (amax, then encode) with the same result.  The wait is bounded: a workgroup that gives up
+ * waiting reads the whole tensor for the maximum itself, so the result never depends on it.
  * ------------------------------------------------------------------------------------------- */
 nvfp4_status nvfp4_quantize_1d(const void *x, int64_t rows, int64_t cols, int64_t ld_x,
                                const nvfp4_tensor *out, void *ws, size_t ws_bytes, void *stream);
@@ -131,12 +134,16 @@ nvfp4_status nvfp4_quantize_2d(const void *w, int64_t rows, int64_t cols, int64_
  * shape (rows % 16 == 0 for 16), and the result is an ordinary NVFP4 tensor.
  * The global scale is the amax one (as above).  Each block takes, among the E4M3 codes
  * c0 - 16 .. c0 + 1 around the amax-derived code c0 (clamped to 0 .. 126), the scale whose
- * reconstruction has the least squared error, evaluated in fp32 in a fixed order:
+ * reconstruction has the least squared error sum_i (x_i - code value_i * sb * gs)^2.  The
+ * library evaluates that error in fp32:
  *   d_i = RN(code value_i * sb * gs), e_i = RN(x_i - d_i), the 16 values of a row block summed
  *   left to right as RN(e_i * e_i); a 16x16 tile combines its 16 row errors pairwise (row r
- *   with r ^ 1, then ^ 2, ^ 4, ^ 8).
- * Ties go to the code nearest c0, then the smaller code.  Elements are encoded as by the
- * quantizer under the chosen scale.  Codes need 8-byte alignment here (ld_codes % 8 == 0). */
+ *   with r ^ 1, then ^ 2, ^ 4, ^ 8);
+ * so between candidates whose exact errors differ by less than this evaluation resolves it may
+ * keep either: the chosen scale's exact error exceeds the exact minimum by at most the two
+ * candidates' fp32 evaluation error bounds.  Equal fp32 errors go to the code nearest c0, then
+ * the smaller code.  Elements are encoded as by the quantizer under the chosen scale (bit-exact).
+ * Codes need 8-byte alignment here (ld_codes % 8 == 0). */
 nvfp4_status nvfp4_quantize_mse(const void *w, int64_t rows, int64_t cols, int64_t ld_w,
                                 const nvfp4_tensor *out, void *ws, size_t ws_bytes, void *stream);
 
@@ -205,8 +212,13 @@ nvfp4_status nvfp4_gemm_w4a16(const void *a_bf16, int64_t m, int64_t k, int64_t 
  *               g*n .. g*n+n-1; w->global_scale points to num_groups floats (one per expert);
  *               n % 16 == 0 when block_rows == 16.
  *   y         : device bf16 total_rows x n, row stride ld_y.
- * Alignment rules as for nvfp4_gemm_w4a4.  Offsets and row indices are trusted (checked only
- * for being non-NULL).
+ * Alignment rules as for nvfp4_gemm_w4a4.  Offsets and row indices live in device memory and
+ * are trusted on the hot path (checked only for being non-NULL): values outside the rules above
+ * make the kernels read and write out of bounds.  With the environment variable NVFP4_DEBUG=1 the
+ * call first copies them to the host (on `stream`, then waits for it) and returns
+ * NVFP4_ERR_SHAPE, launching nothing, when offsets[0] != 0, the offsets decrease, the last one
+ * exceeds total_rows, or a row index lies outside [0, tokens).  The check is skipped on a stream
+ * that is being captured into a graph (it would have to wait).
  * ------------------------------------------------------------------------------------------- */
 nvfp4_status nvfp4_grouped_gemm_w4a4(const void *a_bf16, int64_t tokens, int64_t k,
                                      int64_t ld_a, const nvfp4_tensor *a_q,

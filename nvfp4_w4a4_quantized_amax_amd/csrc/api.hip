@@ -3,6 +3,9 @@
 #include "../../include/nvfp4.h"
 
 #include <hip/hip_runtime.h>
+#include <stdlib.h>
+
+#include <vector>
 
 #include "launch.hpp"
 #include "nvfp4_device.hpp"
@@ -98,6 +101,41 @@ nvfp4_status check_bf16_input(const void *x, int64_t rows, int64_t cols, int64_t
 }
 
 inline nvfp4_status hip_status(hipError_t e) { return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP; }
+
+// NVFP4_DEBUG=1: host-side check of the grouped product's device-resident routing arrays (read
+// on every grouped call, so a process may switch it on and off).
+bool debug_checks() {
+  const char *v = getenv("NVFP4_DEBUG");
+  return v && v[0] == '1' && v[1] == '\0';
+}
+
+// Copies offsets[0..num_groups] and row_index[0..total_rows) to the host (ordered on `stream`)
+// and checks them; NVFP4_ERR_HIP if a copy fails.
+nvfp4_status check_routing(const int32_t *offsets, int32_t num_groups, const int32_t *row_index,
+                           int64_t total_rows, int64_t tokens, hipStream_t stream) {
+  hipStreamCaptureStatus capture = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(stream, &capture) != hipSuccess) {
+    (void)hipGetLastError();
+    return NVFP4_OK;
+  }
+  if (capture != hipStreamCaptureStatusNone) return NVFP4_OK;
+  std::vector<int32_t> off((size_t)num_groups + 1);
+  std::vector<int32_t> ri(row_index ? (size_t)total_rows : 0);
+  if (hipMemcpyAsync(off.data(), offsets, off.size() * sizeof(int32_t), hipMemcpyDeviceToHost,
+                     stream) != hipSuccess)
+    return NVFP4_ERR_HIP;
+  if (row_index && hipMemcpyAsync(ri.data(), row_index, ri.size() * sizeof(int32_t),
+                                  hipMemcpyDeviceToHost, stream) != hipSuccess)
+    return NVFP4_ERR_HIP;
+  if (hipStreamSynchronize(stream) != hipSuccess) return NVFP4_ERR_HIP;
+  if (off[0] != 0) return NVFP4_ERR_SHAPE;
+  for (int32_t g = 0; g < num_groups; ++g)
+    if (off[(size_t)g + 1] < off[(size_t)g]) return NVFP4_ERR_SHAPE;
+  if ((int64_t)off[(size_t)num_groups] > total_rows) return NVFP4_ERR_SHAPE;
+  for (const int32_t r : ri)
+    if (r < 0 || (int64_t)r >= tokens) return NVFP4_ERR_SHAPE;
+  return NVFP4_OK;
+}
 
 // 1D quantization into explicit buffers, choosing the one-workgroup path for small tensors
 // and, ahead of a product in the same call (before_product), the two-kernel path for
@@ -356,6 +394,10 @@ nvfp4_status nvfp4_grouped_gemm_w4a4(const void *a_bf16, int64_t tokens, int64_t
     return NVFP4_ERR_WORKSPACE;
 
   hipStream_t st = (hipStream_t)stream;
+  if (debug_checks()) {
+    s = check_routing(offsets, num_groups, row_index, total_rows, tokens, st);
+    if (s) return s;
+  }
   uint8_t *base = (uint8_t *)ws;
   const PackedLayout L = packed_layout(tokens, k);
   GemmOperand A;

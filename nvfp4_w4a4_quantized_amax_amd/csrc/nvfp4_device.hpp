@@ -40,8 +40,9 @@ struct QuantTables {
 
 // Workspace header (8 KiB).  The two-pass path leaves one partial maximum (|bf16| bit pattern)
 // per amax workgroup in the first 4 KiB; the single-read path keeps one 64-bit (epoch, max) slot
-// per workgroup in the next 4 KiB, with a status word at its end.  Nothing in it needs to be zero
-// between calls.
+// per workgroup in the next 4 KiB, with a status word at its end that counts (across calls) the
+// workgroups whose grid barrier gave up waiting and read the whole tensor for the maximum.
+// Nothing in it needs to be zero between calls.
 constexpr int kMaxAmaxSlots = 1024;
 constexpr size_t kWsHeaderBytes = 8192;
 constexpr size_t kPersistentSlotOffset = 4096;

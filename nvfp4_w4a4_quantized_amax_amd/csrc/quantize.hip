@@ -178,28 +178,29 @@ __global__ __launch_bounds__(kQThreads) void k_encode_1d(const uint4 *__restrict
 }
 
 // ---------------------------------------------------------------------------------------------
-// Single-read path: one persistent workgroup per CU.  It is launched only when the occupancy
-// query shows that one such workgroup fits on every CU, so all of them become resident (at the
-// latest when other work on the device drains).  Phase 1 reads each wave's tiles once, keeping
-// the first RT of them in registers and the next LT in LDS, and publishes the workgroup's
-// partial max.  A grid barrier without read-modify-write atomics follows: every workgroup
-// stores (epoch << 16 | max) into its own 64-bit slot, and one wave per workgroup polls all
-// slots until every slot carries this call's epoch (a per-call 48-bit number, so stale slots
-// never match).  The poll is bounded; if it ever ran out, the global scale is written as NaN
-// and a status word is set, but the kernel still ends.  Phase 2 builds the tables and encodes
-// the resident tiles without touching memory again; tiles beyond RT + LT per wave are read a
-// second time.
+// Single-read path: one persistent workgroup per CU, started with the cooperative launch, which
+// guarantees that all of them are resident at once.  Phase 1 reads each wave's tiles once,
+// keeping the first RT of them in registers and the next LT in LDS, and publishes the
+// workgroup's partial max.  A grid barrier without read-modify-write atomics follows: every
+// workgroup stores (epoch << 16 | max) into its own 64-bit slot, and one wave per workgroup polls
+// all slots until every slot carries this call's epoch (a per-call 48-bit number, so stale slots
+// never match).  The poll is bounded (spin_limit rounds); a workgroup whose poll runs out
+// (possible only if the workgroups were not all resident, e.g. after a plain launch next to
+// other work) computes the global maximum itself by reading the whole tensor, so the result is
+// the same either way, and counts itself in the status word.  Phase 2 builds the tables and
+// encodes the resident tiles without touching memory again; tiles beyond RT + LT per wave are
+// read a second time.
 // ---------------------------------------------------------------------------------------------
 constexpr uint32_t kSpinLimit = 1u << 20;
 
 template <int WAVES, int RT, int LT, bool CONTIG>
 __global__ __launch_bounds__(WAVES * 64, 1) void k_quantize_persistent(
     const uint4 *__restrict__ x, uint32_t n_blocks, FastDiv bpr, int64_t ld_x8, EncOut o,
-    unsigned long long *__restrict__ slots, unsigned long long epoch,
+    unsigned long long *__restrict__ slots, unsigned long long epoch, uint32_t spin_limit,
     float *__restrict__ gs_out, uint32_t *__restrict__ status) {
   __shared__ QuantTables tab;
   __shared__ uint32_t red[WAVES];
-  __shared__ uint32_t s_amax;
+  __shared__ uint32_t s_amax, s_done;
   // LDS-resident tiles: [tile][half][wave][lane], one 16-byte half-block per lane, and each
   // block's |max| pattern (found in phase 1, used again in phase 2).
   __shared__ uint4 s_tiles[LT * 2 * WAVES][kWave];
@@ -291,7 +292,7 @@ __global__ __launch_bounds__(WAVES * 64, 1) void k_quantize_persistent(
 #pragma unroll
     for (int r = 0; r < kPoll; ++r)
       if (lane + kWave * r < (int)gridDim.x) pending |= 1u << r;
-    for (uint32_t it = 0; it < kSpinLimit && !done; ++it) {
+    for (uint32_t it = 0; it < spin_limit && !done; ++it) {
       unsigned long long v[kPoll];
 #pragma unroll
       for (int r = 0; r < kPoll; ++r)
@@ -314,12 +315,26 @@ __global__ __launch_bounds__(WAVES * 64, 1) void k_quantize_persistent(
       }
     }
     if (lane == 0) {
-      // A barrier that never completed (workgroups not co-resident) poisons the global scale.
-      s_amax = done ? mx : 0x7FC0u;
-      if (!done) *status = 1u;
+      s_amax = mx;
+      s_done = done ? 1u : 0u;
     }
   }
   __syncthreads();
+  if (s_done == 0u) {
+    // The barrier did not complete: read the whole tensor for the global maximum (uniform
+    // branch: every thread of the workgroup takes it).
+    uint32_t mm = 0;
+    for (uint32_t b = threadIdx.x; b < n_blocks; b += WAVES * 64) {
+      const size_t idx = block_index<CONTIG>(b, bpr, ld_x8);
+      mm = max(mm, absmax16(x[idx], x[idx + 1]));
+    }
+    mm = block_max_u32(mm, red);
+    if (threadIdx.x == 0) {
+      s_amax = mm;
+      atomicAdd(status, 1u);
+    }
+    __syncthreads();
+  }
   const float gs = global_scale_from_amax_bits(s_amax);
   if (blockIdx.x == 0 && threadIdx.x == 0) *gs_out = gs;
   build_tables(tab, gs);
@@ -518,11 +533,19 @@ constexpr int kPResidentS = 8, kPLdsS = 4;
 #define K_PERSISTENT_C k_quantize_persistent<kPWaves, kPResidentC, kPLdsC, true>
 #define K_PERSISTENT_S k_quantize_persistent<kPWaves, kPResidentS, kPLdsS, false>
 
+// How the single-read kernel is started, chosen once per process by NVFP4_QUANT_PATH (a switch
+// for measurement and tests): by default the cooperative launch; "plain" launches it as an
+// ordinary kernel (all workgroups are then resident only when nothing else occupies the
+// device; the bounded barrier covers the rest); "two_pass" turns the single-read path off.
+// NVFP4_QUANT_SPIN_LIMIT overrides the barrier's poll bound (a test switch: 0 makes every
+// workgroup take the whole-tensor maximum of a barrier that did not complete).
+enum class QuantLaunch { kCooperative, kPlain, kOff };
+
 struct DeviceInfo {
   int cus = 0;
   bool coop = false;
-  bool enabled = true;          // NVFP4_QUANT_PATH=two_pass turns the single-read path off
-  bool cooperative_api = false; // NVFP4_QUANT_PATH=cooperative launches through the cooperative API
+  QuantLaunch mode = QuantLaunch::kCooperative;
+  uint32_t spin_limit = kSpinLimit;
   int fits_contig = 0, fits_strided = 0;
 };
 
@@ -550,8 +573,11 @@ static DeviceInfo device_info() {
     }
     (void)hipGetLastError();
     const char *path = getenv("NVFP4_QUANT_PATH");
-    if (path && strcmp(path, "two_pass") == 0) d.enabled = false;
-    if (path && strcmp(path, "cooperative") == 0) d.cooperative_api = true;
+    if (path && strcmp(path, "two_pass") == 0) d.mode = QuantLaunch::kOff;
+    if (path && strcmp(path, "plain") == 0) d.mode = QuantLaunch::kPlain;
+    if (d.mode == QuantLaunch::kCooperative && !d.coop) d.mode = QuantLaunch::kOff;
+    const char *spin = getenv("NVFP4_QUANT_SPIN_LIMIT");
+    if (spin && *spin) d.spin_limit = (uint32_t)strtoul(spin, nullptr, 10);
     cache[dev] = d;
     known[dev] = true;
   }
@@ -584,8 +610,8 @@ hipError_t launch_quantize_persistent(const void *x, int64_t rows, int64_t cols,
   const DeviceInfo d = device_info();
   const bool contig = (ld_x == cols) && (ld_codes == cols / 2) && (ld_scales == cols / 16);
   const int fits = contig ? d.fits_contig : d.fits_strided;
-  if (!d.enabled || d.cus <= 0 || fits < 1 || d.cus > kMaxPersistentSlots) return hipErrorNotSupported;
-  if (d.cooperative_api && !d.coop) return hipErrorNotSupported;
+  if (d.mode == QuantLaunch::kOff || d.cus <= 0 || fits < 1 || d.cus > kMaxPersistentSlots)
+    return hipErrorNotSupported;
   // A stream being captured into a graph would freeze this call's epoch into the graph, and
   // every replay after the first would find all slots already carrying it and pass the barrier
   // on stale maxima: captured calls take the two-kernel path, which has no grid barrier.  (A
@@ -604,21 +630,30 @@ hipError_t launch_quantize_persistent(const void *x, int64_t rows, int64_t cols,
   unsigned long long *slots = (unsigned long long *)((uint8_t *)ws + kPersistentSlotOffset);
   unsigned long long epoch = next_epoch();
   uint32_t *status = (uint32_t *)((uint8_t *)ws + kPersistentStatusOffset);
+  uint32_t spin = d.spin_limit;
   const uint4 *xp = (const uint4 *)x;
   void *args[] = {(void *)&xp, (void *)&n_blocks, (void *)&f, (void *)&ld_x8, (void *)&o,
-                  (void *)&slots, (void *)&epoch, (void *)&gs_out, (void *)&status};
+                  (void *)&slots, (void *)&epoch, (void *)&spin, (void *)&gs_out,
+                  (void *)&status};
   const void *fn = contig ? (const void *)K_PERSISTENT_C : (const void *)K_PERSISTENT_S;
-  if (d.cooperative_api)
-    return hipLaunchCooperativeKernel(fn, dim3(d.cus), dim3(kPWaves * 64), args, 0, stream);
+  if (d.mode == QuantLaunch::kCooperative) {
+    if (hipLaunchCooperativeKernel(fn, dim3(d.cus), dim3(kPWaves * 64), args, 0, stream) ==
+        hipSuccess)
+      return hipSuccess;
+    // The cooperative launch was refused (nothing ran): clear the error and let the caller take
+    // the two-kernel path.
+    (void)hipGetLastError();
+    return hipErrorNotSupported;
+  }
   // Plain launch: the occupancy check above guarantees one workgroup per CU fits, so on a device
   // that is not running other work all of them are resident at once; if they ever are not, the
-  // bounded barrier ends the kernel with a NaN global scale instead of hanging.
+  // workgroups whose bounded barrier runs out read the whole tensor for the maximum.
   if (contig)
     hipLaunchKernelGGL((K_PERSISTENT_C), dim3(d.cus), dim3(kPWaves * 64), 0, stream, xp, n_blocks,
-                       f, ld_x8, o, slots, epoch, gs_out, status);
+                       f, ld_x8, o, slots, epoch, spin, gs_out, status);
   else
     hipLaunchKernelGGL((K_PERSISTENT_S), dim3(d.cus), dim3(kPWaves * 64), 0, stream, xp, n_blocks,
-                       f, ld_x8, o, slots, epoch, gs_out, status);
+                       f, ld_x8, o, slots, epoch, spin, gs_out, status);
   return hipGetLastError();
 }
 

@@ -1,6 +1,9 @@
 """Run as a separate process by test_gpu_quantize.py: quantizes a few tensors on whatever 1D path
-NVFP4_QUANT_PATH selects (the library reads it once per process) and compares every byte with
-the oracle.  Prints one line per case; exit status 0 when all match."""
+NVFP4_QUANT_PATH selects, with the grid barrier's poll bound NVFP4_QUANT_SPIN_LIMIT (the library
+reads both once per process), and compares every byte with the oracle.  With a poll bound of 0
+every workgroup of the single-read kernel gives up on the barrier and reads the whole tensor for
+the maximum; the status word of the workspace (its count of such workgroups) must then grow by
+one per compute unit per call.  Prints one line per case; exit status 0 when all match."""
 
 import os
 import sys
@@ -17,7 +20,13 @@ from gpu_helpers import assert_codes_equal, dev_bf16, host_q  # noqa: E402
 
 
 def main():
-    path = os.environ.get("NVFP4_QUANT_PATH", "")
+    import torch
+    path = os.environ.get("NVFP4_QUANT_PATH", "") + " spin=" + os.environ.get(
+        "NVFP4_QUANT_SPIN_LIMIT", "default")
+    spin0 = os.environ.get("NVFP4_QUANT_SPIN_LIMIT") == "0"
+    ws = nv.Workspace.get(nv.lib().nvfp4_quantize_workspace_bytes(1, 16), "cuda")
+    status_off = 8192 - 64
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
     rng = np.random.default_rng(11)
     cases = {
         "activation band 512x8192": W.activation(seed=1, rows=512, cols=8192)["x"],
@@ -32,7 +41,11 @@ def main():
         else:
             xt = dev_bf16(x)
             want = O.quantize_1d(x)
-        c, s, g = host_q(nv.quantize_1d(xt))
+        before = int(ws[status_off:status_off + 4].view(torch.int32).item())
+        c, s, g = host_q(nv.quantize_1d(xt, ws=ws))
+        after = int(ws[status_off:status_off + 4].view(torch.int32).item())
+        if spin0:
+            assert after - before == cus, (path, name, before, after, cus)
         assert np.float32(g) == want[2], (path, name, g, want[2])
         assert_codes_equal(s, want[1], f"{path} {name} scales")
         assert_codes_equal(c, want[0], f"{path} {name} codes")

@@ -62,12 +62,41 @@ def test_tiny_config(nv):
     # 64-row tiles up to M = 64, 128-row tiles above (ragged M and N; K = 1024 is a single
     # round of the window ring); 128-row tiles with too few of them take the split path.
     (40, 8200, 2048, 1), (100, 8256, 1024, 16), (300, 4160, 2048, 16), (128, 4096, 4096, 16),
+    # 128-row tiles of the mid-size kernel on a wide 2D-scaled weight with several rounds of
+    # the window ring (K = 4096); 1D-scaled weights with M > 128 on the pipelined 256 x 256
+    # kernel (with and without a K split); M > 128 with K not a multiple of 64 (the
+    # register-prefetch kernel with 256-row tiles), 2D and 1D.
+    (65, 8192, 4096, 16), (200, 512, 4096, 1), (513, 1024, 1024, 1), (1024, 2048, 512, 1),
+    (200, 256, 1040, 16), (150, 272, 528, 1),
 ])
 def test_shapes(nv, m, n, k, br):
     rng = np.random.default_rng(m * 7 + n * 3 + k)
     a = W.normal_with_outliers(rng, m, k, 0.01, 20.0)
     w = rng.standard_normal((n, k)) * 0.02
     run_dense(nv, W.to_bf16_bits(a), W.to_bf16_bits(w), br, f"{m}x{n}x{k} b{br}")
+
+
+@pytest.mark.parametrize("br", [16, 1])
+@pytest.mark.parametrize("m", [40, 100])
+def test_mid_kernel_strided_scales(nv, m, br):
+    """Mid-size M on a wide weight whose scale rows are not 16-byte aligned (a strided view of
+    a wider scale buffer): the mid-size kernel's form that loads scales 2 bytes at a time."""
+    rng = np.random.default_rng(m + br)
+    n, k = 8192, 2048
+    a = W.to_bf16_bits(W.normal_with_outliers(rng, m, k, 0.01, 20.0))
+    w = W.to_bf16_bits(rng.standard_normal((n, k)) * 0.02)
+    wq = (nv.quantize_2d if br == 16 else nv.quantize_1d)(dev_bf16(w))
+    srows = n // br
+    wide = torch.zeros((srows, k // 16 + 2), dtype=torch.uint8, device="cuda")
+    wide[:, :k // 16] = wq.scales
+    wq2 = nv.QTensor(wq.codes, wide[:, :k // 16], wq.global_scale, n, k, br)
+    assert wq2.scales.stride(0) % 16 != 0
+    aq = nv.quantize_1d(dev_bf16(a))
+    y = nv.gemm_w4a4(aq, wq2)
+    y_ref = nv.gemm_w4a4(aq, wq)
+    ow = (O.quantize_2d(w) if br == 16 else O.quantize_1d(w)) + (br,)
+    check_gemm(y, O.gemm64(O.quantize_1d(a) + (1,), ow), what=f"strided scales m={m} b{br}")
+    check_gemm(y_ref, O.gemm64(O.quantize_1d(a) + (1,), ow), what=f"aligned scales m={m} b{br}")
 
 
 @pytest.mark.parametrize("m", [1, 16, 200])
@@ -111,74 +140,87 @@ def test_identity_weight_closed_form(nv):
     check_gemm(y, y64, what="identity")
 
 
-def test_decode_config_full_size(nv):
-    """14336 x 4096 weights (16x16 blocks), activations M = 1, 8, 16 quantized inside the call.
-    W's bytes are checked on sampled 16-row bands; outputs on the columns of those bands."""
-    d = W.decode()
+@pytest.fixture(scope="module")
+def decode_w(nv):
+    """The 14336 x 4096 decode weight (16x16 tiles) quantized on the GPU, checked byte for byte
+    in full against the oracle; returns (workload, GPU tensor, oracle tensor, its float64
+    reconstruction)."""
+    d = W.decode(ms=(1, 8, 16))
     w = d["w"]
     wq = nv.quantize_2d(dev_bf16(w))
     wc, ws, wg = host_q(wq)
-    gw = O.global_scale(float(np.max(np.abs(W.bf16_bits_to_float32(w)))))
-    assert np.float32(wg) == gw
-    rng = np.random.default_rng(1)
-    bands = np.unique(np.concatenate([[0, 895], rng.choice(896, 30, replace=False)]))
-    rows = (bands[:, None] * 16 + np.arange(16)).ravel()
-    oc, os_ = O.encode_2d(w[rows], gw)
-    assert_codes_equal(wc[rows], oc, "decode W codes")
-    assert_codes_equal(ws[bands], os_, "decode W scales")
-    ow = (oc, os_, gw, 16)
+    oc, os_, og = O.quantize_2d(w)
+    assert np.float32(wg) == og
+    assert_codes_equal(ws, os_, "decode W scales")
+    assert_codes_equal(wc, oc, "decode W codes")
+    ow = (oc, os_, og, 16)
+    return d, wq, ow, O.dequantize(*ow, out="f64")
+
+
+def test_decode_config_full_size(nv, decode_w):
+    """14336 x 4096 weights (16x16 blocks), activations M = 1, 8, 16 quantized inside the call:
+    the quantized A the kernel writes and every output element against the oracle."""
+    d, wq, ow, w64 = decode_w
     for m, a in d["a"].items():
-        y = nv.gemm_w4a4(dev_bf16(a), wq)
-        y64 = O.gemm64(O.quantize_1d(a) + (1,), ow)
-        check_gemm(y.cpu()[:, rows], y64, what=f"decode M={m}")
+        aq = nv.empty_qtensor(m, 4096, 1)
+        y = nv.gemm_w4a4(dev_bf16(a), wq, a_q=aq)
+        oa = O.quantize_1d(a) + (1,)
+        ac, as_, ag = host_q(aq)
+        assert np.float32(ag) == oa[2]
+        assert_codes_equal(ac, oa[0], f"decode M={m} A codes")
+        assert_codes_equal(as_, oa[1], f"decode M={m} A scales")
+        y64 = O.dequantize(*oa, out="f64") @ w64.T
+        check_gemm(y, y64, what=f"decode M={m}", min_agree=0.99)
 
 
-@pytest.mark.parametrize("m", [17, 64, 200, 513])
-def test_batched_decode_full_width(nv, m):
-    """The 14336 x 4096 decode weight with M = 17, 64, 200 and 513 activation rows (quantized
-    inside the call): 64- and 128-row tiles of 64 columns with K split over each workgroup's
-    waves, then 256 x 256 tiles.  Outputs are checked on sampled 16-row bands of W."""
-    d = W.decode()
-    w = d["w"]
-    wq = nv.quantize_2d(dev_bf16(w))
-    wc, ws, wg = host_q(wq)
-    gw = O.global_scale(float(np.max(np.abs(W.bf16_bits_to_float32(w)))))
-    assert np.float32(wg) == gw
+@pytest.mark.parametrize("m", [17, 64, 65, 128, 200, 513])
+def test_batched_decode_full_width(nv, decode_w, m):
+    """The 14336 x 4096 decode weight with 17 to 513 activation rows (quantized inside the
+    call): 64-row tiles of the mid-size kernel (M = 17, 64), its 128-row tiles on this wide
+    weight (M = 65, 128; K = 4096 runs four rounds of the window ring), then 256 x 256 tiles
+    with a K split (M = 200, 513).  Every output element against the oracle."""
+    _, wq, ow, w64 = decode_w
     rng = np.random.default_rng(100 + m)
-    bands = np.unique(np.concatenate([[0, 895], rng.choice(896, 14, replace=False)]))
-    rows = (bands[:, None] * 16 + np.arange(16)).ravel()
-    oc, os_ = O.encode_2d(w[rows], gw)
-    assert_codes_equal(wc[rows], oc, "W codes")
-    assert_codes_equal(ws[bands], os_, "W scales")
     a = W.to_bf16_bits(W.normal_with_outliers(rng, m, 4096, 0.01, 20.0))
     y = nv.gemm_w4a4(dev_bf16(a), wq)
-    y64 = O.gemm64(O.quantize_1d(a) + (1,), (oc, os_, gw, 16))
-    check_gemm(y.cpu()[:, rows], y64, what=f"batched decode M={m}")
+    y64 = O.dequantize(*(O.quantize_1d(a) + (1,)), out="f64") @ w64.T
+    check_gemm(y, y64, what=f"batched decode M={m}", min_agree=0.99)
+
+
+def tile_cover(rng, n, tile, per_tile):
+    """`per_tile` random indices in every `tile`-wide slice of range(n) (plus 0 and n - 1)."""
+    idx = [t0 + rng.choice(min(tile, n - t0), min(per_tile, n - t0), replace=False)
+           for t0 in range(0, n, tile)]
+    return np.unique(np.concatenate(idx + [[0, n - 1]]))
 
 
 def test_prefill_config_full_size(nv):
     """8192^3 with the activation quantized inside the call: the quantized A (captured) and W
-    are checked byte for byte on sampled rows / bands, Y on their cross product."""
+    are checked byte for byte in full; Y on 528 rows x 528 columns chosen so that each of the
+    1,024 output tiles of 256 x 256 holds 256 checked elements at random positions."""
     d = W.prefill()
     a, w = d["a"], d["w"]
     wq = nv.quantize_2d(dev_bf16(w))
     aq = nv.empty_qtensor(8192, 8192, 1)
     y = nv.gemm_w4a4(dev_bf16(a), wq, a_q=aq)
-    ga = O.global_scale(float(np.max(np.abs(W.bf16_bits_to_float32(a)))))
-    gw = O.global_scale(float(np.max(np.abs(W.bf16_bits_to_float32(w)))))
     ac, as_, ag = host_q(aq)
     wc, ws, wg = host_q(wq)
-    assert np.float32(ag) == ga and np.float32(wg) == gw
+    oa = O.quantize_1d(a)
+    assert np.float32(ag) == oa[2]
+    assert_codes_equal(as_, oa[1], "prefill A scales")
+    assert_codes_equal(ac, oa[0], "prefill A codes")
+    del ac, as_
+    ow = O.quantize_2d(w)
+    assert np.float32(wg) == ow[2]
+    assert_codes_equal(ws, ow[1], "prefill W scales")
+    assert_codes_equal(wc, ow[0], "prefill W codes")
+    del wc, ws
     rng = np.random.default_rng(2)
-    arows = np.unique(np.concatenate([[0, 8191], rng.choice(8192, 30, replace=False)]))
-    bands = np.unique(np.concatenate([[0, 511], rng.choice(512, 14, replace=False)]))
-    wrows = (bands[:, None] * 16 + np.arange(16)).ravel()
-    oac, oas = O.encode_1d(a[arows], ga)
-    owc, ows = O.encode_2d(w[wrows], gw)
-    assert_codes_equal(ac[arows], oac, "prefill A codes")
-    assert_codes_equal(as_[arows], oas, "prefill A scales")
-    assert_codes_equal(wc[wrows], owc, "prefill W codes")
-    assert_codes_equal(ws[bands], ows, "prefill W scales")
-    y64 = O.gemm64((oac, oas, ga, 1), (owc, ows, gw, 16))
-    ys = y.cpu()[arows][:, wrows]
-    check_gemm(ys, y64, what="prefill sampled")
+    rows = tile_cover(rng, 8192, 256, 16)
+    cols = tile_cover(rng, 8192, 256, 16)
+    assert len(rows) >= 512 and len(cols) >= 512
+    a64 = O.dequantize(oa[0][rows], oa[1][rows], oa[2], 1, out="f64")
+    w64 = O.dequantize(ow[0], ow[1], ow[2], 16, out="f64")[cols]
+    y64 = a64 @ w64.T
+    ys = y[torch.from_numpy(rows).cuda()][:, torch.from_numpy(cols).cuda()]
+    check_gemm(ys, y64, what="prefill tile-covering sample", min_agree=0.99)

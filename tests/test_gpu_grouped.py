@@ -19,27 +19,34 @@ def nv():
     return nvfp4
 
 
-def quantize_experts(nv, w_stacked, experts, n):
-    """Each expert's weights quantized on its own (own global scale) into one stacked tensor."""
+def quantize_experts(nv, w_stacked, experts, n, br=16):
+    """Each expert's weights quantized on its own (own global scale) into one stacked tensor
+    (16x16 tiles, or 1D blocks with br = 1)."""
     k = w_stacked.shape[1]
-    wq = nv.empty_qtensor(experts * n, k, 16, n_global_scales=experts)
+    wq = nv.empty_qtensor(experts * n, k, br, n_global_scales=experts)
     for e in range(experts):
-        part = nv.QTensor(wq.codes[e * n:(e + 1) * n], wq.scales[e * n // 16:(e + 1) * n // 16],
-                          wq.global_scale[e:e + 1], n, k, 16)
-        nv.quantize_2d(dev_bf16(w_stacked[e * n:(e + 1) * n]), out=part)
+        part = nv.QTensor(wq.codes[e * n:(e + 1) * n], wq.scales[e * n // br:(e + 1) * n // br],
+                          wq.global_scale[e:e + 1], n, k, br)
+        (nv.quantize_2d if br == 16 else nv.quantize_1d)(dev_bf16(w_stacked[e * n:(e + 1) * n]),
+                                                        out=part)
     return wq
 
 
-def oracle_experts(w_stacked, experts, n):
-    return [O.quantize_2d(w_stacked[e * n:(e + 1) * n]) + (16,) for e in range(experts)]
+def oracle_experts(w_stacked, experts, n, br=16):
+    q = O.quantize_2d if br == 16 else O.quantize_1d
+    return [q(w_stacked[e * n:(e + 1) * n]) + (br,) for e in range(experts)]
 
 
-@pytest.mark.parametrize("tokens,hidden,experts,topk,n", [(256, 256, 8, 2, 128),
-                                                           (300, 528, 16, 4, 80),
-                                                           (64, 1024, 5, 5, 256)])
-def test_small_moe(nv, tokens, hidden, experts, topk, n):
+# hidden 528 is not a multiple of 64 (the register-prefetch grouped kernel); br = 1 takes the 1D
+# weight-scale forms of both grouped kernels.
+@pytest.mark.parametrize("tokens,hidden,experts,topk,n,br", [(256, 256, 8, 2, 128, 16),
+                                                              (300, 528, 16, 4, 80, 16),
+                                                              (64, 1024, 5, 5, 256, 16),
+                                                              (256, 512, 8, 2, 136, 1),
+                                                              (300, 528, 16, 4, 72, 1)])
+def test_small_moe(nv, tokens, hidden, experts, topk, n, br):
     d = W.moe(seed=tokens, tokens=tokens, hidden=hidden, experts=experts, topk=topk, n=n)
-    wq = quantize_experts(nv, d["w"], experts, n)
+    wq = quantize_experts(nv, d["w"], experts, n, br)
     ri = torch.from_numpy(d["row_index"]).cuda()
     off = torch.from_numpy(d["offsets"]).cuda()
     total = int(d["offsets"][-1])
@@ -49,11 +56,12 @@ def test_small_moe(nv, tokens, hidden, experts, topk, n):
     ac, as_, ag = host_q(aq)
     assert np.float32(ag) == oa[2]
     assert_codes_equal(ac, oa[0], "moe A codes")
-    ows = oracle_experts(d["w"], experts, n)
+    ows = oracle_experts(d["w"], experts, n, br)
     wc, ws, wg = host_q(wq)
     for e in range(experts):
         assert np.float32(wg[e]) == ows[e][2]
         assert_codes_equal(wc[e * n:(e + 1) * n], ows[e][0], f"expert {e} codes")
+        assert_codes_equal(ws[e * n // br:(e + 1) * n // br], ows[e][1], f"expert {e} scales")
     y64 = O.grouped_gemm64(oa + (1,), d["row_index"], d["offsets"], ows)
     check_gemm(y, y64, what="small moe")
 
@@ -72,9 +80,11 @@ def test_empty_groups_and_pregrouped_rows(nv):
     check_gemm(y, y64, what="pregrouped")
 
 
-def test_moe_config_full_size_sampled(nv):
-    """4096 tokens, hidden 2048, 128 experts of 768 x 2048, top-8 Zipf routing: every output row
-    of 12 sampled experts (including the hottest and the coldest) against the oracle."""
+def test_moe_config_full_size(nv):
+    """4096 tokens, hidden 2048, 128 experts of 768 x 2048, top-8 Zipf routing: the quantized
+    tokens the call writes and every expert's weights byte for byte, then every output row of
+    every expert (37 to 3,699 rows each) against a float64 product of the reconstructed
+    operands."""
     d = W.moe()
     experts, n = d["experts"], d["n"]
     wq = quantize_experts(nv, d["w"], experts, n)
@@ -82,18 +92,66 @@ def test_moe_config_full_size_sampled(nv):
     off = torch.from_numpy(d["offsets"]).cuda()
     total = int(d["offsets"][-1])
     assert total == 4096 * 8
-    y = nv.grouped_gemm_w4a4(dev_bf16(d["a"]), ri, off, wq, n, total).cpu()
+    aq = nv.empty_qtensor(4096, 2048, 1)
+    y = nv.grouped_gemm_w4a4(dev_bf16(d["a"]), ri, off, wq, n, total, a_q=aq).cpu()
     oa = O.quantize_1d(d["a"]) + (1,)
+    ac, as_, ag = host_q(aq)
+    assert np.float32(ag) == oa[2]
+    assert_codes_equal(ac, oa[0], "moe A codes")
+    assert_codes_equal(as_, oa[1], "moe A scales")
     ahat = O.dequantize(*oa, out="f64")
-    counts = d["counts"]
-    rng = np.random.default_rng(3)
-    sample = np.unique(np.concatenate([[int(np.argmax(counts)), int(np.argmin(counts))],
-                                       rng.choice(experts, 10, replace=False)]))
     wc, ws, wg = host_q(wq)
-    for e in sample:
+    worst = 0.0
+    for e in range(experts):
         ow = O.quantize_2d(d["w"][e * n:(e + 1) * n]) + (16,)
         assert np.float32(wg[e]) == ow[2]
         assert_codes_equal(wc[e * n:(e + 1) * n], ow[0], f"expert {e} codes")
+        assert_codes_equal(ws[e * n // 16:(e + 1) * n // 16], ow[1], f"expert {e} scales")
         lo, hi = d["offsets"][e], d["offsets"][e + 1]
         y64 = ahat[d["row_index"][lo:hi]] @ O.dequantize(*ow, out="f64").T
-        check_gemm(y[lo:hi], y64, what=f"expert {e} ({hi - lo} rows)")
+        worst = max(worst, check_gemm(y[lo:hi], y64, what=f"expert {e} ({hi - lo} rows)",
+                                      min_agree=0.99))
+    print(f"moe: all {experts} experts, worst err/tol {worst:.4f}")
+
+
+def test_debug_routing_checks(nv):
+    """NVFP4_DEBUG=1: the grouped call copies its routing arrays to the host first and rejects
+    bad ones with NVFP4_ERR_SHAPE, launching nothing; good ones give the same result as without
+    the check.  (The environment variable is read on every grouped call.)"""
+    import os
+    d = W.moe(seed=7, tokens=64, hidden=256, experts=4, topk=2, n=64)
+    wq = quantize_experts(nv, d["w"], 4, 64)
+    a = dev_bf16(d["a"])
+    total = int(d["offsets"][-1])
+    ri = torch.from_numpy(d["row_index"]).cuda()
+    off = torch.from_numpy(d["offsets"]).cuda()
+    y_ref = nv.grouped_gemm_w4a4(a, ri, off, wq, 64, total)
+    bad_cases = {
+        "offsets[0] != 0": (ri, np.array([1, 40, 80, 100, 128], dtype=np.int32)),
+        "decreasing offsets": (ri, np.array([0, 60, 50, 100, 128], dtype=np.int32)),
+        "last offset past total_rows": (ri, np.array([0, 40, 80, 100, 129], dtype=np.int32)),
+        "row index >= tokens": (torch.from_numpy(np.where(np.arange(total) == 5, 64,
+                                                          d["row_index"]).astype(np.int32)).cuda(),
+                                d["offsets"]),
+        "negative row index": (torch.from_numpy(np.where(np.arange(total) == 9, -1,
+                                                         d["row_index"]).astype(np.int32)).cuda(),
+                               d["offsets"]),
+    }
+    old = os.environ.get("NVFP4_DEBUG")
+    os.environ["NVFP4_DEBUG"] = "1"
+    try:
+        y = nv.grouped_gemm_w4a4(a, ri, off, wq, 64, total)
+        assert torch.equal(y, y_ref)
+        for what, (rix, offs) in bad_cases.items():
+            y_bad = torch.full((total, 64), 7.0, dtype=torch.bfloat16, device="cuda")
+            with pytest.raises(nv.Nvfp4Error) as ei:
+                nv.grouped_gemm_w4a4(a, rix, torch.from_numpy(offs).cuda(), wq, 64, total,
+                                     y=y_bad)
+            assert ei.value.status == nv.ERR_SHAPE, what
+            torch.cuda.synchronize()
+            assert torch.all(y_bad == 7.0), what + ": output written"
+    finally:
+        if old is None:
+            del os.environ["NVFP4_DEBUG"]
+        else:
+            os.environ["NVFP4_DEBUG"] = old

@@ -1,6 +1,15 @@
-"""GPU parity of the MSE-observer quantizer against the oracle: codes, scale bytes and the global
-scale bit for bit (the observer's fp32 error evaluation is specified, so the decisions match);
-the result is an ordinary NVFP4 tensor that the GEMM consumes."""
+"""GPU check of the MSE-observer quantizer against the oracle.
+
+The oracle's scale choice is the exact minimum of each block's squared error over the candidate
+scales.  The library evaluates the errors in fp32, so where two candidates' exact errors differ
+by less than the fp32 evaluation can resolve it may pick the other one.  So the tests check:
+  * the global scale bit for bit;
+  * every block's scale is one of its candidates and its exact error exceeds the exact minimum
+    by no more than the two candidates' fp32 evaluation bounds (oracle `fp32_evaluation_bound`);
+  * every code bit for bit under the scale the library chose;
+  * the share of blocks whose scale equals the exact choice (>= 99.9 %; the fp32 rule and the
+    exact rule differ on 4 of 524,288 row blocks of the decode weight in a CPU comparison).
+The result is an ordinary NVFP4 tensor that the GEMM consumes."""
 
 import numpy as np
 import pytest
@@ -22,14 +31,33 @@ def nv():
     return nvfp4
 
 
-def check(nv, u16, br, what):
+def check_choice(u16, c, s, g, br, what, gs=None, min_equal=0.999):
+    """Validity of the library's result (codes c, scale bytes s, global scale g) against the
+    exact-minimum oracle; returns the oracle's (codes, scales, gs, block_rows)."""
+    osc, og = M.mse_scale_codes(u16, br, gs=gs)
+    assert np.float32(g) == og, what
+    s = np.asarray(s)
+    xb = np.abs(M._blocks(O._as_f64(u16), br)).max(axis=-1)
+    c0 = O.block_scale_codes(xb, og).astype(np.int64)
+    lo, hi = np.maximum(c0 - 16, 0), np.minimum(c0 + 1, 126)
+    assert np.all((s >= lo) & (s <= hi)), f"{what}: scale outside the candidate set"
+    e_lib = M.block_errors(u16, s, og, br)
+    e_orc = M.block_errors(u16, osc, og, br)
+    slack = M.fp32_evaluation_bound(u16, s, og, br) + M.fp32_evaluation_bound(u16, osc, og, br)
+    over = e_lib - e_orc - slack
+    assert np.all(over <= 0), f"{what}: {int(np.sum(over > 0))} blocks beyond the fp32 bound"
+    oc, _ = M.encode_with_scales(u16, s, og, br)
+    assert_codes_equal(c, oc, what + " codes under the chosen scales")
+    differ = int(np.sum(s != osc))
+    assert differ <= 1 + (1 - min_equal) * s.size, f"{what}: {differ} of {s.size} scales differ " \
+        "from the exact choice"
+    return (oc, s, og, br)
+
+
+def check(nv, u16, br, what, min_equal=0.999):
     q = nv.quantize_mse(dev_bf16(u16), br)
     c, s, g = host_q(q)
-    oc, os_, og = M.quantize_mse(u16, br)
-    assert np.float32(g) == og, what
-    assert_codes_equal(s, os_, what + " scales")
-    assert_codes_equal(c, oc, what + " codes")
-    return q, (oc, os_, og, br)
+    return q, check_choice(u16, c, s, g, br, what, min_equal=min_equal)
 
 
 def weights(rng, rows, cols, kind):
@@ -65,8 +93,9 @@ def test_edge_blocks(nv):
 
 
 def test_decode_weight_sampled_bands(nv):
-    """The 14336 x 4096 decode weight with 16x16 tiles: sampled bands bit for bit (under the
-    tensor's global scale), and the observer's total error below the amax rule's."""
+    """The 14336 x 4096 decode weight with 16x16 tiles: the global scale, then 128 of the 896
+    tile bands (the first, the last and 126 at random; the exact oracle takes about 12 s per 100
+    bands) checked as above, and the observer's total error below the amax rule's."""
     d = W.decode()
     w = d["w"]
     q = nv.quantize_mse(dev_bf16(w), 16)
@@ -74,11 +103,11 @@ def test_decode_weight_sampled_bands(nv):
     gw = O.global_scale(float(np.max(np.abs(W.bf16_bits_to_float32(w)))))
     assert np.float32(g) == gw
     rng = np.random.default_rng(5)
-    bands = np.unique(np.concatenate([[0, 895], rng.choice(896, 24, replace=False)]))
+    bands = np.unique(np.concatenate([[0, 895], rng.choice(np.arange(1, 895), 126,
+                                                              replace=False)]))
+    assert bands.size == 128
     rows = (bands[:, None] * 16 + np.arange(16)).ravel()
-    oc, os_, _ = M.quantize_mse(w[rows], 16, gs=gw)
-    assert_codes_equal(c[rows], oc, "decode W codes")
-    assert_codes_equal(s[bands], os_, "decode W scales")
+    oc, os_, _, _ = check_choice(w[rows], c[rows], s[bands], g, 16, "decode W", gs=gw)
     xf = O.bf16_bits_to_f64(w[rows])
     e_mse = np.sum((O.dequantize(oc, os_, gw, 16, out="f64") - xf) ** 2)
     base = O.encode_2d(w[rows], gw)

@@ -150,20 +150,35 @@ def test_quantize_2d(nv, rows, cols):
     assert np.array_equal(f32.view(np.uint32), O.dequantize(c, s, g, 16, out="f32").view(np.uint32))
 
 
-def test_activation_full_size_sampled(nv):
+def test_activation_full_size(nv):
     """The 8192 x 8192 activation workload (the single-read path, as timed by the benchmark):
-    the global scale against the oracle's (from the full amax), every byte of 96 sampled rows
-    against the oracle."""
+    the global scale and every code and scale byte of the whole tensor against the oracle."""
     x = W.activation()["x"]
     q = nv.quantize_1d(dev_bf16(x))
     c, s, g = host_q(q)
-    og = O.global_scale(float(np.max(np.abs(W.bf16_bits_to_float32(x)))))
+    oc, os_, og = O.quantize_1d(x)
     assert np.float32(g) == og
-    rng = np.random.default_rng(0)
-    rows = np.unique(np.concatenate([[0, 1, 8191], rng.choice(8192, 93, replace=False)]))
-    oc, os_ = O.encode_1d(x[rows], og)
-    assert_codes_equal(s[rows], os_, "full-size scales")
-    assert_codes_equal(c[rows], oc, "full-size codes")
+    assert_codes_equal(s, os_, "full-size scales")
+    assert_codes_equal(c, oc, "full-size codes")
+    # dequantize of the whole tensor, fp32 and bf16 outputs, bit for bit
+    f32 = nv.dequantize(q, torch.float32).cpu().numpy()
+    assert np.array_equal(f32.view(np.uint32), O.dequantize(oc, os_, og, 1, out="f32").view(np.uint32))
+    del f32
+    b16 = nv.dequantize(q, torch.bfloat16).cpu().view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(b16, O.dequantize(oc, os_, og, 1, out="bf16"))
+
+
+@pytest.mark.parametrize("rows,cols,br", [(257, 1040, 1), (48, 272, 16), (130, 4112, 1)])
+def test_dequantize_ragged(nv, rows, cols, br):
+    """Dequantize (fp32 and bf16) on shapes that leave partial tiles, 1D and 16x16 scales."""
+    rng = np.random.default_rng(rows * 3 + cols)
+    x = W.to_bf16_bits(rng.laplace(0, 1, (rows, cols)) * np.exp(rng.standard_normal(cols)))
+    q = (nv.quantize_2d if br == 16 else nv.quantize_1d)(dev_bf16(x))
+    c, s, g = host_q(q)
+    f32 = nv.dequantize(q, torch.float32).cpu().numpy()
+    assert np.array_equal(f32.view(np.uint32), O.dequantize(c, s, g, br, out="f32").view(np.uint32))
+    b16 = nv.dequantize(q, torch.bfloat16).cpu().view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(b16, O.dequantize(c, s, g, br, out="bf16"))
 
 
 def test_empty_tensors(nv):
@@ -179,18 +194,27 @@ def test_empty_tensors(nv):
     torch.cuda.synchronize()
 
 
-@pytest.mark.parametrize("path", ["two_pass", "cooperative"])
-def test_other_quantize_paths(path):
-    """The two-kernel path (taken when one workgroup per CU cannot be resident) and the
-    cooperative launch of the single-read kernel, selected through NVFP4_QUANT_PATH in a
-    separate process (the library reads it once per process)."""
+@pytest.mark.parametrize("path,spin", [("two_pass", ""), ("plain", ""), ("", "0"),
+                                       ("plain", "0")])
+def test_other_quantize_paths(path, spin):
+    """The two-kernel path (taken when the cooperative launch is unavailable), a plain launch of
+    the single-read kernel, and the single-read kernel with a poll bound of 0 (cooperative and
+    plain launch), so that every workgroup takes the barrier's fallback (the whole-tensor
+    maximum): selected through NVFP4_QUANT_PATH / NVFP4_QUANT_SPIN_LIMIT in a separate process
+    (the library reads them once per process).  Every kernel ends normally in all four."""
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     import os
     import subprocess
     import sys
     here = os.path.dirname(os.path.abspath(__file__))
-    env = dict(os.environ, NVFP4_QUANT_PATH=path)
+    env = dict(os.environ)
+    env.pop("NVFP4_QUANT_PATH", None)
+    env.pop("NVFP4_QUANT_SPIN_LIMIT", None)
+    if path:
+        env["NVFP4_QUANT_PATH"] = path
+    if spin:
+        env["NVFP4_QUANT_SPIN_LIMIT"] = spin
     r = subprocess.run([sys.executable, "-u", os.path.join(here, "quantize_path_check.py")],
                        env=env, capture_output=True, text=True, timeout=110)
     assert r.returncode == 0, r.stdout[-2000:] + r.stderr[-2000:]

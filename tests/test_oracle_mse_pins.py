@@ -1,7 +1,8 @@
 """Pins of the MSE-observer oracle (CPU only): blocks the amax scale already reconstructs exactly
-keep it, all-zero blocks keep scale 0, the chosen scale is (up to the fp32 evaluation) the exact
-minimum over the candidates, computed independently in rational arithmetic, and the observer
-never does worse than the amax rule."""
+keep it, all-zero blocks keep scale 0, the chosen scale is the exact minimum over the candidates
+(computed independently in rational arithmetic, ties by R20), the float64 filter and the fp32
+evaluation bound hold against exact errors, and the observer never does worse than the amax
+rule."""
 
 from fractions import Fraction
 
@@ -80,25 +81,106 @@ def test_zero_blocks_keep_scale_zero():
     assert sc[0].tolist() == [0, 0, 0, 0] and sc[1, 0] == 0 and sc[1, 2] == 0
 
 
+def exact_choice(vals, c0):
+    """R18-R20 by brute force: exact errors of every candidate, the nearest-to-c0 (then smaller)
+    code among the exact minima."""
+    cands = sorted({min(max(c0 + d, 0), 126) for d in range(-16, 2)})
+    errs = {c: exact_error(vals, c, GS_OF[0]) for c in cands}
+    emin = min(errs.values())
+    return min((abs(c - c0), c) for c in cands if errs[c] == emin)[1], errs
+
+
+GS_OF = [None]
+
+
 @pytest.mark.parametrize("seed", range(4))
 def test_choice_is_the_exact_minimum(seed):
-    """Independent exact check: for each block, the chosen code's exact error is the exact
-    minimum over the candidates up to the fp32 evaluation of reading R19 (relative 2^-16)."""
+    """Independent exact check: every block's chosen code is the exact minimizer of the squared
+    error over the candidates (rational arithmetic, all 18 candidates), with R20's tie order."""
     rng = np.random.default_rng(seed + 40)
     x = rng.standard_normal((3, 64)) * np.exp(rng.uniform(-4, 4, (3, 1)))
     x[1, :16] = rng.laplace(size=16) * 5
     x[2, 16:32] = np.where(rng.random(16) < 0.2, 20.0, 1.0) * rng.standard_normal(16)
     u = W.to_bf16_bits(x)
     sc, gs = M.mse_scale_codes(u, 1)
+    GS_OF[0] = gs
     c0 = O.block_scale_codes(np.abs(O.bf16_bits_to_f64(u)).reshape(3, 4, 16).max(axis=2), gs)
     for r in range(3):
         for b in range(4):
             vals = [Fraction(float(v)) for v in O.bf16_bits_to_f64(u[r, 16 * b:16 * b + 16])]
-            cands = sorted({min(max(int(c0[r, b]) + d, 0), 126) for d in M.candidate_offsets()})
-            errs = {c: exact_error(vals, c, gs) for c in cands}
-            emin = min(errs.values())
-            assert int(sc[r, b]) in errs
-            assert errs[int(sc[r, b])] <= emin * (1 + Fraction(1, 2 ** 16)) + Fraction(1, 2 ** 300)
+            want, _ = exact_choice(vals, int(c0[r, b]))
+            assert int(sc[r, b]) == want, (r, b)
+
+
+@pytest.mark.parametrize("vals,c0,tied,want", [
+    # c0 ties with c0 + 1: c0 is nearer
+    ([0] * 9 + [-14.0, 0, 0, -8.0, 0, 0, 0], 89, (89, 90), 89),
+    # c0 + 1 ties with c0 - 2 (c0 itself worse): the nearer c0 + 1 wins over the smaller code
+    ([0, 0, 0, 8.0, 0, 0, 0, 0, 0, 0, 8.0, 0, 0, 0, 10.0, 8.0], 85, (83, 86), 86),
+    ([0, 0, 0, 0, 0, 4.0, 0, -5.0, 0, 0, -4.0, 0, 0, 0, 0, 4.0], 77, (75, 78), 78),
+])
+def test_exact_ties_follow_r20(vals, c0, tied, want):
+    """Blocks whose exact minimum is shared by two candidates (found by an exhaustive rational
+    search over small-integer blocks under gs = 2^-3): the tie goes to the code nearer c0."""
+    x = np.array([vals + [336.0] + [0.0] * 15])           # amax 336 -> gs = 336 / 2688 = 2^-3
+    u = W.to_bf16_bits(x)
+    sc, gs = M.mse_scale_codes(u, 1)
+    assert gs == np.float32(0.125)
+    assert int(O.block_scale_codes(np.array([np.max(np.abs(vals))]), gs)[0]) == c0
+    GS_OF[0] = gs
+    fr = [Fraction(v) for v in vals]
+    got, errs = exact_choice(fr, c0)
+    emin = min(errs.values())
+    assert sorted(c for c in errs if errs[c] == emin) == sorted(tied)
+    assert got == want and int(sc[0, 0]) == want
+
+
+def test_float64_errors_are_within_2_pow_44_of_exact():
+    """The oracle's float64 block errors (its fast filter) against rational arithmetic, on blocks
+    spanning many binades, 1D and 16x16: within the relative 2^-44 its near-tie rule assumes."""
+    rng = np.random.default_rng(77)
+    x = rng.standard_normal((16, 64)) * np.exp(rng.uniform(-30, 30, (16, 64)))
+    u = W.to_bf16_bits(x)
+    gs = O.global_scale(O.global_amax(O.bf16_bits_to_f64(u)))
+    xf = O.bf16_bits_to_f64(u)
+    for br in (1, 16):
+        c0 = O.block_scale_codes(np.abs(M._blocks(xf, br)).max(axis=-1), gs).astype(np.int64)
+        for d in (-9, -1, 0, 1):
+            sc = np.clip(c0 + d, 0, 126)
+            e64 = M.block_errors(u, sc, gs, br)
+            xb = M._blocks(xf, br)
+            for idx in zip(*np.nonzero(np.ones(sc.shape, bool))):
+                vals = xb[idx]
+                codes = O.element_codes(vals, O.E4M3_POS[sc[idx]], gs)
+                ex = M._exact_error(vals, codes, O.E4M3_POS[sc[idx]], gs)
+                assert abs(Fraction(float(e64[idx])) - ex) <= ex * Fraction(1, 2 ** 44)
+
+
+def test_fp32_evaluation_bound_covers_an_fp32_evaluation():
+    """The bound the GPU tests use: an fp32 evaluation of the error (d, e, e^2 rounded to fp32, a
+    sequential fp32 sum) lies within it of the exact error, for every candidate of every block."""
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((32, 64)) * np.exp(rng.uniform(-3, 3, (32, 1)))
+    u = W.to_bf16_bits(x)
+    xf = O.bf16_bits_to_f64(u)
+    gs = O.global_scale(O.global_amax(xf))
+    for br in (1, 16):
+        xb = M._blocks(xf, br)
+        c0 = O.block_scale_codes(np.abs(xb).max(axis=-1), gs).astype(np.int64)
+        for d in M.candidate_offsets():
+            sc = np.clip(c0 + d, 0, 126)
+            sbv = O.E4M3_POS[sc][..., None]
+            codes = O.element_codes(xb, sbv, gs)
+            dd = (O.E2M1_MAG[codes & 7] * np.where(codes & 8, -1.0, 1.0) * sbv).astype(np.float32)
+            dd = (dd * np.float32(gs)).astype(np.float32)
+            e = (xb.astype(np.float32) - dd).astype(np.float32)
+            q = (e * e).astype(np.float32)
+            s32 = np.zeros(q.shape[:-1], dtype=np.float32)
+            for i in range(q.shape[-1]):
+                s32 = (s32 + q[..., i]).astype(np.float32)
+            exact = M.block_errors(u, sc, gs, br)
+            bound = M.fp32_evaluation_bound(u, sc, gs, br)
+            assert np.all(np.abs(s32.astype(np.float64) - exact) <= bound)
 
 
 def test_never_worse_than_amax_and_often_better():
@@ -131,4 +213,6 @@ def test_tile_form_matches_exact_minimum():
         vals = [Fraction(float(v)) for v in xf[:, 16 * t:16 * t + 16].ravel()]
         cands = sorted({min(max(int(c0[0, t]) + d, 0), 126) for d in M.candidate_offsets()})
         errs = {c: exact_error(vals, c, gs) for c in cands}
-        assert errs[int(sc[0, t])] <= min(errs.values()) * (1 + Fraction(1, 2 ** 16))
+        emin = min(errs.values())
+        want = min((abs(c - int(c0[0, t])), c) for c in cands if errs[c] == emin)[1]
+        assert int(sc[0, t]) == want

@@ -448,6 +448,29 @@ def test_dequantize_bf16_is_rne_of_fp32():
     assert np.array_equal(b, want)
 
 
+def test_f32_to_bf16_ties_match_torch_cast():
+    """The fp32 -> bf16 rounding behind the bf16 dequantize, pinned against torch's cast (round
+    to nearest, ties to even) on every exact tie: all fp32 patterns whose low half is 0x8000,
+    with both signs, every finite exponent and every bf16 mantissa (so both parities of the
+    kept bit), plus their neighbours 0x7FFF and 0x8001.  A round-half-up (or half-down) rule
+    fails on the ties, a truncating one on the 0x8001 neighbours."""
+    sign = np.arange(2, dtype=np.uint32)[:, None, None, None] << 31
+    expo = np.arange(255, dtype=np.uint32)[None, :, None, None] << 23
+    mant = np.arange(128, dtype=np.uint32)[None, None, :, None] << 16
+    low = np.array([0x7FFF, 0x8000, 0x8001], dtype=np.uint32)[None, None, None, :]
+    bits = (sign | expo | mant | low).ravel()
+    f32 = bits.view(np.float32)
+    got = O.f32_to_bf16_bits(f32)
+    want = torch.from_numpy(f32.copy()).to(torch.bfloat16).view(torch.int16).numpy()
+    want = want.astype(np.uint16)
+    assert np.array_equal(got, want)
+    ties = (bits & 0xFFFF) == 0x8000
+    kept_odd = ((bits >> 16) & 1) == 1
+    # on a tie the result is the even neighbour: up when the kept bit is odd, down when even
+    assert np.all(got[ties & kept_odd] == ((bits[ties & kept_odd] >> 16) + 1).astype(np.uint16))
+    assert np.all(got[ties & ~kept_odd] == (bits[ties & ~kept_odd] >> 16).astype(np.uint16))
+
+
 # ---------------------------------------------------------------------------------------------
 # W4A16 (weights NVFP4, activations bf16)
 # ---------------------------------------------------------------------------------------------
@@ -501,3 +524,33 @@ def test_w4a16_equals_w4a4_on_representable_activations():
     assert np.array_equal(O.bf16_bits_to_f64(a_bits), a_hat)
     wq = O.quantize_2d(rand_bf16(rng, (32, 64), 0.02)) + (16,)
     assert np.array_equal(O.gemm64_w4a16(a_bits, wq), O.gemm64(aq + (1,), wq))
+
+
+def test_rn_bf16_helper_against_exact_rounding():
+    """The GPU tests' report of outputs equal to RN_bf16(Y64) rounds float64 values to bf16 once;
+    pinned against exact rational rounding (nearest of the two bf16 neighbours, ties to the even
+    one) on random values and on constructed ties."""
+    import sys
+    import os
+    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    from gpu_helpers import rn_bf16_f64
+    rng = np.random.default_rng(3)
+    v = rng.standard_normal(300) * np.exp(rng.uniform(-40, 40, 300))
+    ties = np.array([1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8, -(3 + 2.0 ** -6), 2.0 ** 20 * (1 + 2.0 ** -8)])
+    v = np.concatenate([v, ties, [0.0, -0.0]])
+    got = rn_bf16_f64(v)
+    for x, g in zip(v, got):
+        if x == 0:
+            assert g == 0
+            continue
+        e = int(np.floor(np.log2(abs(x))))
+        ulp = Fraction(2) ** (e - 7)
+        fx = Fraction(float(x))
+        lo = (fx / ulp).__floor__() * ulp
+        hi = lo + ulp
+        dlo, dhi = fx - lo, hi - fx
+        if dlo < dhi or (dlo == dhi and (lo / ulp) % 2 == 0):
+            want = lo
+        else:
+            want = hi
+        assert Fraction(float(g)) == want, (x, g, float(want))

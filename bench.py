@@ -46,9 +46,11 @@ def parse():
     return p.parse_args()
 
 
-def timed(fn, steps, warmup, torch):
-    """Average ms per call of fn(i) over `steps` calls, bracketed by HIP events on the current
-    stream (the one the library launches on), after `warmup` calls."""
+def timed(fn, steps, warmup, torch, stats=True):
+    """ms per call of fn(i): the average over `steps` calls bracketed by two HIP events on the
+    current stream (the one the library launches on), after `warmup` calls.  With `stats`, a
+    second pass records an event between consecutive calls and adds the median, p10 and p90 of
+    the per-call times.  Returns (mean_ms, stats dict or None)."""
     for i in range(warmup):
         fn(i)
     torch.cuda.synchronize()
@@ -60,7 +62,50 @@ def timed(fn, steps, warmup, torch):
         fn(i)
     end.record(stream)
     torch.cuda.synchronize()
-    return start.elapsed_time(end) / steps
+    mean = start.elapsed_time(end) / steps
+    if not stats:
+        return mean, None
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record(stream)
+    for i in range(steps):
+        fn(i)
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    per = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
+    q = lambda f: per[min(len(per) - 1, int(round(f * (len(per) - 1))))]
+    return mean, {"median_ms": q(0.5), "p10_ms": q(0.1), "p90_ms": q(0.9), "calls": steps}
+
+
+def clocks():
+    """Current GPU clocks as the SMI tools report them (amd-smi, else rocm-smi), or the error."""
+    import subprocess
+    for cmd in (["amd-smi", "metric", "--clock", "--json"], ["rocm-smi", "--showclocks", "--json"]):
+        try:
+            r = subprocess.run(cmd, capture_output=True, text=True, timeout=30)
+        except (OSError, subprocess.TimeoutExpired) as e:
+            err = str(e)
+            continue
+        if r.returncode == 0 and r.stdout.strip():
+            try:
+                return {"tool": cmd[0], "report": json.loads(r.stdout)}
+            except ValueError:
+                return {"tool": cmd[0], "report": r.stdout.strip()[:2000]}
+        err = (r.stderr or r.stdout).strip()[:300]
+    return {"error": err}
+
+
+def copy_bandwidth(torch):
+    """Attainable HBM rate on this machine: a device-to-device copy of 1 GiB (torch's copy kernel),
+    counted as bytes read plus bytes written; 10 timed copies cycling over 2 sources and 2
+    destinations (4 GiB, far beyond the Infinity Cache)."""
+    n = 1 << 30
+    src = [torch.empty(n, dtype=torch.uint8, device="cuda").fill_(i) for i in range(2)]
+    dst = [torch.empty(n, dtype=torch.uint8, device="cuda") for _ in range(2)]
+    ms, st = timed(lambda i: dst[i % 2].copy_(src[(i // 2) % 2]), 10, 3, torch)
+    del src, dst
+    return {"copy_gbs_median": 2 * n / (st["median_ms"] * 1e-3) / 1e9,
+            "copy_gbs_mean": 2 * n / (ms * 1e-3) / 1e9, "bytes_per_copy": 2 * n,
+            "what": "torch device copy of 1 GiB, read + write bytes / time"}
 
 
 def dev_bf16(torch, np, u16):
@@ -79,7 +124,7 @@ def headline(args, torch, np, nv, W):
     def step(i):
         nv.quantize_1d(xs[i % nbuf], out=qs[i % nbuf], ws=ws)
 
-    ms = timed(step, args.steps, args.warmup, torch)
+    ms, st = timed(step, args.steps, args.warmup, torch)
     nbytes = rows * cols * 2 + rows * cols // 2 + rows * cols // 16 + 4
     gbs = nbytes / (ms * 1e-3) / 1e9
     if args.copy_calibration:
@@ -87,7 +132,8 @@ def headline(args, torch, np, nv, W):
         for i in range(5):
             dst.copy_(xs[i % nbuf])
         torch.cuda.synchronize()
-    return {"ms": ms, "bytes": nbytes, "gbs": gbs, "x_host": x_host}
+    return {"ms": ms, "bytes": nbytes, "gbs": gbs, "x_host": x_host, "stats": st,
+            "median_gbs": nbytes / (st["median_ms"] * 1e-3) / 1e9}
 
 
 TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
@@ -126,13 +172,30 @@ def measured_traffic():
         return None
 
 
+def _rec(ms, st, nbytes=None, flops=None, bound="hbm", peak=None, **extra):
+    """One workload record: time per call (mean and per-call statistics) and its roofline."""
+    r = {"ms": ms, "median_ms": st["median_ms"], "p10_ms": st["p10_ms"], "p90_ms": st["p90_ms"],
+         "bound": bound}
+    if nbytes is not None:
+        r["algorithmic_bytes"] = nbytes
+        r["gbs"] = nbytes / (ms * 1e-3) / 1e9
+    if flops is not None:
+        r["tflops"] = flops / (ms * 1e-3) / 1e12
+    if bound == "hbm":
+        r.update(achieved=r["gbs"], unit="GB/s", peak=HBM_PEAK_GBS, frac=r["gbs"] / HBM_PEAK_GBS)
+    elif bound == "mfma":
+        r.update(achieved=r["tflops"], unit="TFLOP/s", peak=peak, frac=r["tflops"] / peak)
+    r.update(extra)
+    return r
+
+
 def extra_workloads(args, torch, np, nv, W, only):
     out = {}
     steps = max(10, args.steps // 2)
     warm = max(2, args.warmup)
 
     if not only or "decode" in only:
-        # M = 1, 8, 16 (the decode configuration) and a batched M = 64 (split-K tiled product)
+        # M = 1, 8, 16 (the decode configuration) and a batched M = 64 (mid-size product)
         d = W.decode(ms=(1, 8, 16, 64))
         wq0 = nv.quantize_2d(dev_bf16(torch, np, d["w"]))
         nw = 10  # 10 x 29.6 MB of weights > the 256 MB Infinity Cache
@@ -143,39 +206,92 @@ def extra_workloads(args, torch, np, nv, W, only):
             a = dev_bf16(torch, np, a_host)
             y = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
             ws = nv.Workspace.get(nv.lib().nvfp4_gemm_workspace_bytes(m, n, k), a.device)
-            ms = timed(lambda i: nv.gemm_w4a4(a, wqs[i % nw], y=y, ws=ws), steps, warm, torch)
             nbytes = n * k // 2 + (n // 16) * (k // 16) + 4 + m * k * 2 + m * n * 2
-            gbs = nbytes / (ms * 1e-3) / 1e9
-            out[f"decode_m{m}"] = {
-                "shape": [m, n, k], "ms": ms, "bound": "hbm", "achieved": gbs,
-                "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
-                "tflops": 2 * m * n * k / (ms * 1e-3) / 1e12}
+            ms, st = timed(lambda i: nv.gemm_w4a4(a, wqs[i % nw], y=y, ws=ws), steps, warm, torch)
+            out[f"decode_m{m}"] = _rec(ms, st, nbytes, 2 * m * n * k, shape=[m, n, k],
+                                       note="activation quantized inside the call")
             if m > 16:  # the weight-only form serves m <= 16
                 continue
+            # The product alone, A already quantized (what the kernel's W stream costs).
+            aq = nv.quantize_1d(a)
+            ms, st = timed(lambda i: nv.gemm_w4a4(aq, wqs[i % nw], y=y, ws=ws), steps, warm,
+                           torch)
+            pbytes = nbytes - m * k * 2 + m * k // 2 + m * k // 16 + 4
+            out[f"decode_prequantized_m{m}"] = _rec(ms, st, pbytes, 2 * m * n * k,
+                                                    shape=[m, n, k])
             # Weight-only form of the same product: the bf16 A is used as is.
-            ms = timed(lambda i: nv.gemm_w4a16(a, wqs[i % nw], y=y), steps, warm, torch)
-            gbs = nbytes / (ms * 1e-3) / 1e9
-            out[f"decode_w4a16_m{m}"] = {
-                "shape": [m, n, k], "ms": ms, "bound": "hbm", "achieved": gbs,
-                "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
-                "tflops": 2 * m * n * k / (ms * 1e-3) / 1e12}
+            ms, st = timed(lambda i: nv.gemm_w4a16(a, wqs[i % nw], y=y), steps, warm, torch)
+            out[f"decode_w4a16_m{m}"] = _rec(ms, st, nbytes, 2 * m * n * k, shape=[m, n, k])
         del wqs, wq0
 
     if not only or "prefill" in only:
+        # Three sets of (A, W, Y): 3 x (128 MiB + 36 MiB + 128 MiB) > 2 x the Infinity Cache.
         d = W.prefill()
-        a = dev_bf16(torch, np, d["a"])
-        wq = nv.quantize_2d(dev_bf16(torch, np, d["w"]))
         m = n = k = 8192
-        y = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
-        ws = nv.Workspace.get(nv.lib().nvfp4_gemm_workspace_bytes(m, n, k), a.device)
-        ps = max(5, steps // 5)
-        ms = timed(lambda i: nv.gemm_w4a4(a, wq, y=y, ws=ws), ps, warm, torch)
-        tf = 2 * m * n * k / (ms * 1e-3) / 1e12
-        out["prefill"] = {"shape": [m, n, k], "ms": ms, "bound": "mfma", "achieved": tf,
-                          "unit": "TFLOP/s", "peak": FP16_MFMA_PEAK_TFLOPS,
-                          "frac": tf / FP16_MFMA_PEAK_TFLOPS,
-                          "note": "includes the dynamic quantization of A inside the call"}
-        del a, wq, y
+        a0 = dev_bf16(torch, np, d["a"])
+        wq0 = nv.quantize_2d(dev_bf16(torch, np, d["w"]))
+        ns = 3
+        As = [a0] + [a0.clone() for _ in range(ns - 1)]
+        Ws = [wq0] + [nv.QTensor(wq0.codes.clone(), wq0.scales.clone(), wq0.global_scale.clone(),
+                                 m, k, 16) for _ in range(ns - 1)]
+        Ys = [torch.empty((m, n), dtype=torch.bfloat16, device="cuda") for _ in range(ns)]
+        ws = nv.Workspace.get(nv.lib().nvfp4_gemm_workspace_bytes(m, n, k), a0.device)
+        ps = max(6, steps // 4)
+        ms, st = timed(lambda i: nv.gemm_w4a4(As[i % ns], Ws[i % ns], y=Ys[i % ns], ws=ws), ps,
+                       warm, torch)
+        out["prefill"] = _rec(ms, st, None, 2 * m * n * k, "mfma", FP16_MFMA_PEAK_TFLOPS,
+                              shape=[m, n, k],
+                              note="includes the dynamic quantization of A inside the call; "
+                                   "3 rotating input/output sets")
+        aq = nv.quantize_1d(a0)
+        ms, st = timed(lambda i: nv.gemm_w4a4(aq, Ws[i % ns], y=Ys[i % ns], ws=ws), ps, warm,
+                       torch)
+        out["prefill_prequantized"] = _rec(ms, st, None, 2 * m * n * k, "mfma",
+                                           FP16_MFMA_PEAK_TFLOPS, shape=[m, n, k],
+                                           note="A quantized beforehand (the product kernel)")
+        del As, Ws, Ys, aq
+
+    if not only or "moe" in only:
+        d = W.moe()
+        experts, n = d["experts"], d["n"]
+        k = d["a"].shape[1]
+        tokens = d["a"].shape[0]
+        wq = nv.empty_qtensor(experts * n, k, 16, n_global_scales=experts)
+        wdev = dev_bf16(torch, np, d["w"])
+        for e in range(experts):
+            part = nv.QTensor(wq.codes[e * n:(e + 1) * n], wq.scales[e * n // 16:(e + 1) * n // 16],
+                              wq.global_scale[e:e + 1], n, k, 16)
+            nv.quantize_2d(wdev[e * n:(e + 1) * n], out=part)
+        del wdev
+        ri = torch.from_numpy(d["row_index"]).cuda()
+        off = torch.from_numpy(d["offsets"]).cuda()
+        total = int(d["offsets"][-1])
+        # Four sets of (tokens, expert weights, Y): 4 x 166 MB > 2 x the Infinity Cache.
+        ns = 4
+        a0 = dev_bf16(torch, np, d["a"])
+        As = [a0] + [a0.clone() for _ in range(ns - 1)]
+        Ws = [wq] + [nv.QTensor(wq.codes.clone(), wq.scales.clone(), wq.global_scale.clone(),
+                                wq.rows, wq.cols, 16) for _ in range(ns - 1)]
+        Ys = [torch.empty((total, n), dtype=torch.bfloat16, device="cuda") for _ in range(ns)]
+        ws = nv.Workspace.get(nv.lib().nvfp4_grouped_gemm_workspace_bytes(tokens, k, total,
+                                                                          experts), a0.device)
+        ms, st = timed(lambda i: nv.grouped_gemm_w4a4(As[i % ns], ri, off, Ws[i % ns], n, total,
+                                                      y=Ys[i % ns], ws=ws), steps, warm, torch)
+        flops = 2 * total * n * k
+        # Mixed roofline: the token quantize at HBM rate, then each expert at the slower of its
+        # MFMA time and its HBM time (weights, gathered packed rows, bf16 outputs).
+        bw, pk = HBM_PEAK_GBS * 1e9, FP16_MFMA_PEAK_TFLOPS * 1e12
+        t_roof = (tokens * k * 2 + tokens * k // 2 + tokens * k // 16) / bw
+        for rows in d["counts"]:
+            rows = int(rows)
+            wb = n * k // 2 + (n // 16) * (k // 16) + 4
+            t_roof += max(2 * rows * n * k / pk, (wb + rows * (k // 2 + k // 16) + rows * n * 2) / bw)
+        out["moe"] = _rec(ms, st, None, flops, "mfma", FP16_MFMA_PEAK_TFLOPS,
+                          shape=[total, n, k, experts],
+                          mixed_roofline_ms=t_roof * 1e3, mixed_roofline_frac=t_roof * 1e3 / ms,
+                          note="includes the dynamic quantization of the 4096 x 2048 tokens; "
+                               "4 rotating input/weight/output sets")
+        del As, Ws, Ys
 
     if not only or "mxfp4" in only:
         # MXFP4 (E8M0 per 32 values): the headline activation quantized in one pass, and the
@@ -185,12 +301,9 @@ def extra_workloads(args, torch, np, nv, W, only):
         for i in range(1, 4):
             xs[i] = xs[0].clone()
         qs = [nv.empty_mxtensor(8192, 8192) for _ in range(4)]
-        ms = timed(lambda i: nv.mxfp4_quantize(xs[i % 4], out=qs[i % 4]), steps, warm, torch)
         nbytes = 8192 * 8192 * 2 + 8192 * 8192 // 2 + 8192 * 8192 // 32
-        gbs = nbytes / (ms * 1e-3) / 1e9
-        out["mxfp4_quantize"] = {"shape": [8192, 8192], "ms": ms, "bound": "hbm",
-                                 "achieved": gbs, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
-                                 "algorithmic_bytes": nbytes}
+        ms, st = timed(lambda i: nv.mxfp4_quantize(xs[i % 4], out=qs[i % 4]), steps, warm, torch)
+        out["mxfp4_quantize"] = _rec(ms, st, nbytes, shape=[8192, 8192])
         del xs, qs
         d = W.prefill()
         a = dev_bf16(torch, np, d["a"])
@@ -198,13 +311,11 @@ def extra_workloads(args, torch, np, nv, W, only):
         m = n = k = 8192
         y = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
         ws = nv.Workspace.get(nv.lib().nvfp4_mxfp4_gemm_workspace_bytes(m, k), a.device)
-        ps = max(5, steps // 5)
-        ms = timed(lambda i: nv.mxfp4_gemm(a, wq, y=y, ws=ws), ps, warm, torch)
-        tf = 2 * m * n * k / (ms * 1e-3) / 1e12
-        out["mxfp4_prefill"] = {"shape": [m, n, k], "ms": ms, "bound": "mfma", "achieved": tf,
-                                "unit": "TFLOP/s", "peak": FP4_MFMA_PEAK_TFLOPS,
-                                "frac": tf / FP4_MFMA_PEAK_TFLOPS,
-                                "note": "includes the MXFP4 quantization of A inside the call"}
+        ps = max(6, steps // 4)
+        ms, st = timed(lambda i: nv.mxfp4_gemm(a, wq, y=y, ws=ws), ps, warm, torch)
+        out["mxfp4_prefill"] = _rec(ms, st, None, 2 * m * n * k, "mfma", FP4_MFMA_PEAK_TFLOPS,
+                                    shape=[m, n, k],
+                                    note="includes the MXFP4 quantization of A inside the call")
         del a, wq, y
         # Decode-shaped MXFP4 products against the decode weight (14336 x 4096) rotating over 10
         # copies so that W comes from HBM; the activation is quantized inside each call.
@@ -218,13 +329,11 @@ def extra_workloads(args, torch, np, nv, W, only):
             a = dev_bf16(torch, np, a_host)
             y = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
             ws = nv.Workspace.get(nv.lib().nvfp4_mxfp4_gemm_workspace_bytes(m, k), a.device)
-            ms = timed(lambda i: nv.mxfp4_gemm(a, wqs[i % nw], y=y, ws=ws), steps, warm, torch)
             nbytes = n * k // 2 + n * k // 32 + m * k * 2 + m * n * 2
-            gbs = nbytes / (ms * 1e-3) / 1e9
-            out[f"mxfp4_decode_m{m}"] = {
-                "shape": [m, n, k], "ms": ms, "bound": "hbm", "achieved": gbs, "unit": "GB/s",
-                "frac": gbs / HBM_PEAK_GBS, "tflops": 2 * m * n * k / (ms * 1e-3) / 1e12,
-                "note": "includes the MXFP4 quantization of A inside the call"}
+            ms, st = timed(lambda i: nv.mxfp4_gemm(a, wqs[i % nw], y=y, ws=ws), steps, warm,
+                           torch)
+            out[f"mxfp4_decode_m{m}"] = _rec(ms, st, nbytes, 2 * m * n * k, shape=[m, n, k],
+                                             note="includes the MXFP4 quantization of A")
         del wqs, wq0
 
     if not only or "mse" in only:
@@ -234,54 +343,95 @@ def extra_workloads(args, torch, np, nv, W, only):
         wdev = dev_bf16(torch, np, d["w"])
         q = nv.empty_qtensor(14336, 4096, 16)
         ws = nv.Workspace.get(nv.lib().nvfp4_quantize_workspace_bytes(14336, 4096), wdev.device)
-        ms = timed(lambda i: nv.quantize_mse(wdev, 16, out=q, ws=ws), max(5, steps // 5), warm,
-                   torch)
+        ms, st = timed(lambda i: nv.quantize_mse(wdev, 16, out=q, ws=ws), max(5, steps // 5),
+                       warm, torch)
         vals = 14336 * 4096
-        out["mse_quantize_2d"] = {"shape": [14336, 4096], "ms": ms, "bound": "alu",
-                                  "gvalues_per_s": vals / (ms * 1e-3) / 1e9,
-                                  "note": "offline; 18 candidate scales per 16x16 tile"}
+        out["mse_quantize_2d"] = _rec(ms, st, bound="alu", shape=[14336, 4096],
+                                      gvalues_per_s=vals / (ms * 1e-3) / 1e9,
+                                      note="offline; 18 candidate scales per 16x16 tile")
         del wdev, q
-
-    if not only or "moe" in only:
-        d = W.moe()
-        experts, n = d["experts"], d["n"]
-        k = d["a"].shape[1]
-        wq = nv.empty_qtensor(experts * n, k, 16, n_global_scales=experts)
-        wdev = dev_bf16(torch, np, d["w"])
-        for e in range(experts):
-            part = nv.QTensor(wq.codes[e * n:(e + 1) * n], wq.scales[e * n // 16:(e + 1) * n // 16],
-                              wq.global_scale[e:e + 1], n, k, 16)
-            nv.quantize_2d(wdev[e * n:(e + 1) * n], out=part)
-        del wdev
-        a = dev_bf16(torch, np, d["a"])
-        ri = torch.from_numpy(d["row_index"]).cuda()
-        off = torch.from_numpy(d["offsets"]).cuda()
-        total = int(d["offsets"][-1])
-        y = torch.empty((total, n), dtype=torch.bfloat16, device="cuda")
-        ws = nv.Workspace.get(nv.lib().nvfp4_grouped_gemm_workspace_bytes(4096, k, total, experts),
-                              a.device)
-        ms = timed(lambda i: nv.grouped_gemm_w4a4(a, ri, off, wq, n, total, y=y, ws=ws),
-                   steps, warm, torch)
-        flops = 2 * total * n * k
-        tf = flops / (ms * 1e-3) / 1e12
-        out["moe"] = {"shape": [total, n, k, experts], "ms": ms, "bound": "mfma",
-                      "achieved": tf, "unit": "TFLOP/s", "peak": FP16_MFMA_PEAK_TFLOPS,
-                      "frac": tf / FP16_MFMA_PEAK_TFLOPS,
-                      "note": "includes the dynamic quantization of the 4096 x 2048 tokens"}
     return out
 
 
-def cpu_baseline(x_host, nbytes):
-    """The CPU oracle (float64 numpy, test infrastructure) quantizing the same 8192 x 8192
-    input; numpy's elementwise work runs on one thread."""
+def host_info():
+    """Host cores as the CPU oracle sees them: os.cpu_count(), the affinity mask and the BLAS
+    thread pools numpy's matmul uses."""
+    import numpy as np
+    np.ones((8, 8)) @ np.ones((8, 8))  # make sure the BLAS library is loaded
+    info = {"os_cpu_count": os.cpu_count(), "affinity_cpus": len(os.sched_getaffinity(0))}
+    try:
+        import threadpoolctl
+        info["blas"] = [{"api": p.get("internal_api"), "num_threads": p.get("num_threads")}
+                        for p in threadpoolctl.threadpool_info() if p.get("user_api") == "blas"]
+    except Exception as e:  # threadpoolctl missing or failing: say so
+        info["blas"] = f"unknown ({e})"
+    return info
+
+
+def blas_threads(info):
+    try:
+        return max(p["num_threads"] for p in info["blas"])
+    except (TypeError, ValueError, KeyError):
+        return None
+
+
+def cpu_baseline(x_host, nbytes, W, with_gemms=True):
+    """The CPU oracle (float64 numpy, test infrastructure), timed on this host as it stands.
+
+    Headline: quantize_1d of the same 8192 x 8192 input (numpy elementwise work: one thread).
+    With `with_gemms`, bounded samples of the product configurations, each on the same seeded
+    inputs as the GPU run and rated with the GPU rows' algorithmic bytes / flops:
+      tiny   quantize A and W, then the float64 product (the whole 32 x 512 x 512 round trip);
+      decode quantize A (M = 1, 8, 16), then the float64 product with the 14336 x 4096 weight
+             (the weight's quantization is offline on both sides and not timed);
+      moe    quantize the 4096 x 2048 tokens, then the float64 products of 16 of the 128
+             experts (the first 16: the most-routed ones, 19,479 of the 32,768 rows), rated on
+             the flops of those rows.
+    The products run in numpy's BLAS with the threads host_info reports."""
     sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    import numpy as np
     from oracle import nvfp4_oracle as O
+    info = host_info()
     t0 = time.perf_counter()
     O.quantize_1d(x_host)
     dt = time.perf_counter() - t0
-    return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": "the full 8192 x 8192 activation workload, one quantize_1d call "
-                      f"({dt:.1f} s)"}
+    rec = {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+           "sample": "the full 8192 x 8192 activation workload, one quantize_1d call "
+                     f"({dt:.1f} s, numpy elementwise on one thread)", "host": info}
+    if not with_gemms:
+        return rec
+    gemms = {}
+    bt = blas_threads(info)
+    d = W.tiny()
+    t0 = time.perf_counter()
+    O.gemm64(O.quantize_1d(d["a"]) + (1,), O.quantize_1d(d["w"]) + (1,))
+    dt = time.perf_counter() - t0
+    gemms["tiny"] = {"s": dt, "gflops": 2 * 32 * 512 * 512 / dt / 1e9, "threads": bt}
+    d = W.decode()
+    ow = O.quantize_2d(d["w"]) + (16,)
+    n, k = 14336, 4096
+    for m, a in d["a"].items():
+        t0 = time.perf_counter()
+        O.gemm64(O.quantize_1d(a) + (1,), ow)
+        dt = time.perf_counter() - t0
+        nb = n * k // 2 + (n // 16) * (k // 16) + 4 + m * k * 2 + m * n * 2
+        gemms[f"decode_m{m}"] = {"s": dt, "gbs": nb / dt / 1e9, "threads": bt}
+    del ow, d
+    d = W.moe()
+    n, e_s = d["n"], 16
+    ws = [O.quantize_2d(d["w"][e * n:(e + 1) * n]) + (16,) for e in range(e_s)]  # offline
+    off = d["offsets"][:e_s + 1]
+    rows = int(off[-1])
+    t0 = time.perf_counter()
+    oa = O.quantize_1d(d["a"]) + (1,)
+    O.grouped_gemm64(oa, d["row_index"][:rows], off, ws)
+    dt = time.perf_counter() - t0
+    gemms["moe_16_experts"] = {"s": dt, "rows": rows, "gflops": 2 * rows * n * 2048 / dt / 1e9,
+                               "threads": bt, "note": "token quantize + the 16 experts' "
+                                                      "products; their weight quantization "
+                                                      "(offline) not timed"}
+    rec["gemms"] = gemms
+    return rec
 
 
 def main():
@@ -323,8 +473,12 @@ def main():
     if not args.no_extra:
         only = [s for s in args.only.split(",") if s]
         rec["workloads"] = extra_workloads(args, torch, np, nv, W, only)
+    rec["roofline"]["median_gbs"] = h["median_gbs"]
+    rec["roofline"]["per_call"] = h["stats"]
+    rec["clocks"] = clocks()
+    rec["attainable"] = copy_bandwidth(torch)
     if not args.no_cpu:
-        rec["cpu_baseline"] = cpu_baseline(h["x_host"], h["bytes"])
+        rec["cpu_baseline"] = cpu_baseline(h["x_host"], h["bytes"], W, not args.no_extra)
     print(json.dumps(rec), flush=True)
 
 

@@ -112,11 +112,11 @@ size_t nvfp4_grouped_gemm_workspace_bytes(int64_t tokens, int64_t k, int64_t tot
  *   out    : out->codes / scales / global_scale receive the result; out->rows == rows,
  *            out->cols == cols, out->block_rows == 1; codes 16-byte aligned, ld_codes % 16 == 0.
  * Computes amax (pass 1) then block scales and codes (pass 2).  cols % 16 == 0.
- * Large tensors run as one workgroup per compute unit, started with HIP's cooperative launch
- * (all of them resident at once), that read the tensor once and wait for each other between the
- * passes.  Where the cooperative launch is unavailable or refused, the call takes a two-kernel
- * form (amax, then encode) with the same result.  The wait is bounded: a workgroup that gives up
- * waiting reads the whole tensor for the maximum itself, so the result never depends on it.
+ * Large tensors run as one workgroup per compute unit that read the tensor once and wait for
+ * each other between the passes (a two-kernel form, amax then encode, serves graph capture and
+ * devices where one such workgroup per CU does not fit).  The wait is bounded: should other work
+ * on the device keep some workgroups from starting, a workgroup that gives up waiting reads the
+ * whole tensor for the maximum itself, so the result is the same, only slower.
  * ------------------------------------------------------------------------------------------- */
 nvfp4_status nvfp4_quantize_1d(const void *x, int64_t rows, int64_t cols, int64_t ld_x,
                                const nvfp4_tensor *out, void *ws, size_t ws_bytes, void *stream);

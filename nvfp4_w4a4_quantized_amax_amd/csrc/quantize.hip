@@ -178,16 +178,16 @@ __global__ __launch_bounds__(kQThreads) void k_encode_1d(const uint4 *__restrict
 }
 
 // ---------------------------------------------------------------------------------------------
-// Single-read path: one persistent workgroup per CU, started with the cooperative launch, which
-// guarantees that all of them are resident at once.  Phase 1 reads each wave's tiles once,
+// Single-read path: one persistent workgroup per CU (all of them resident at once when nothing
+// else occupies the device).  Phase 1 reads each wave's tiles once,
 // keeping the first RT of them in registers and the next LT in LDS, and publishes the
 // workgroup's partial max.  A grid barrier without read-modify-write atomics follows: every
 // workgroup stores (epoch << 16 | max) into its own 64-bit slot, and one wave per workgroup polls
 // all slots until every slot carries this call's epoch (a per-call 48-bit number, so stale slots
 // never match).  The poll is bounded (spin_limit rounds); a workgroup whose poll runs out
-// (possible only if the workgroups were not all resident, e.g. after a plain launch next to
-// other work) computes the global maximum itself by reading the whole tensor, so the result is
-// the same either way, and counts itself in the status word.  Phase 2 builds the tables and
+// (possible only if the workgroups were not all resident, e.g. next to other work on the
+// device) computes the global maximum itself by reading the whole tensor, so the result is the
+// same either way, and counts itself in the status word.  Phase 2 builds the tables and
 // encodes the resident tiles without touching memory again; tiles beyond RT + LT per wave are
 // read a second time.
 // ---------------------------------------------------------------------------------------------
@@ -534,17 +534,20 @@ constexpr int kPResidentS = 8, kPLdsS = 4;
 #define K_PERSISTENT_S k_quantize_persistent<kPWaves, kPResidentS, kPLdsS, false>
 
 // How the single-read kernel is started, chosen once per process by NVFP4_QUANT_PATH (a switch
-// for measurement and tests): by default the cooperative launch; "plain" launches it as an
-// ordinary kernel (all workgroups are then resident only when nothing else occupies the
-// device; the bounded barrier covers the rest); "two_pass" turns the single-read path off.
-// NVFP4_QUANT_SPIN_LIMIT overrides the barrier's poll bound (a test switch: 0 makes every
-// workgroup take the whole-tensor maximum of a barrier that did not complete).
+// for measurement and tests).  By default it is an ordinary launch: one workgroup per CU fits
+// (the occupancy query says so), so all of them are resident whenever nothing else occupies the
+// device, and a workgroup whose bounded barrier runs out still computes the right maximum.
+// "cooperative" starts it with HIP's cooperative launch, which guarantees co-residency (on the
+// MI355X measured here that call ended in the two-kernel form, 55 us per 8192 x 8192 call
+// against 38 us); "two_pass" turns the single-read path off.  NVFP4_QUANT_SPIN_LIMIT overrides
+// the barrier's poll bound (a test switch: 0 makes every workgroup take the whole-tensor
+// maximum of a barrier that did not complete).
 enum class QuantLaunch { kCooperative, kPlain, kOff };
 
 struct DeviceInfo {
   int cus = 0;
   bool coop = false;
-  QuantLaunch mode = QuantLaunch::kCooperative;
+  QuantLaunch mode = QuantLaunch::kPlain;
   uint32_t spin_limit = kSpinLimit;
   int fits_contig = 0, fits_strided = 0;
 };
@@ -574,7 +577,7 @@ static DeviceInfo device_info() {
     (void)hipGetLastError();
     const char *path = getenv("NVFP4_QUANT_PATH");
     if (path && strcmp(path, "two_pass") == 0) d.mode = QuantLaunch::kOff;
-    if (path && strcmp(path, "plain") == 0) d.mode = QuantLaunch::kPlain;
+    if (path && strcmp(path, "cooperative") == 0) d.mode = QuantLaunch::kCooperative;
     if (d.mode == QuantLaunch::kCooperative && !d.coop) d.mode = QuantLaunch::kOff;
     const char *spin = getenv("NVFP4_QUANT_SPIN_LIMIT");
     if (spin && *spin) d.spin_limit = (uint32_t)strtoul(spin, nullptr, 10);

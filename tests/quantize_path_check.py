@@ -23,7 +23,9 @@ def main():
     import torch
     path = os.environ.get("NVFP4_QUANT_PATH", "") + " spin=" + os.environ.get(
         "NVFP4_QUANT_SPIN_LIMIT", "default")
-    spin0 = os.environ.get("NVFP4_QUANT_SPIN_LIMIT") == "0"
+    # the default (ordinary) launch of the single-read kernel with a poll bound of 0
+    spin0 = (os.environ.get("NVFP4_QUANT_SPIN_LIMIT") == "0"
+             and not os.environ.get("NVFP4_QUANT_PATH"))
     ws = nv.Workspace.get(nv.lib().nvfp4_quantize_workspace_bytes(1, 16), "cuda")
     status_off = 8192 - 64
     cus = torch.cuda.get_device_properties(0).multi_processor_count

@@ -194,14 +194,13 @@ def test_empty_tensors(nv):
     torch.cuda.synchronize()
 
 
-@pytest.mark.parametrize("path,spin", [("two_pass", ""), ("plain", ""), ("", "0"),
-                                       ("plain", "0")])
+@pytest.mark.parametrize("path,spin", [("two_pass", ""), ("cooperative", ""), ("", "0")])
 def test_other_quantize_paths(path, spin):
-    """The two-kernel path (taken when the cooperative launch is unavailable), a plain launch of
-    the single-read kernel, and the single-read kernel with a poll bound of 0 (cooperative and
-    plain launch), so that every workgroup takes the barrier's fallback (the whole-tensor
-    maximum): selected through NVFP4_QUANT_PATH / NVFP4_QUANT_SPIN_LIMIT in a separate process
-    (the library reads them once per process).  Every kernel ends normally in all four."""
+    """The two-kernel path, the cooperative launch of the single-read kernel (or the two-kernel
+    path where the device refuses it), and the single-read kernel with a poll bound of 0, so
+    that every workgroup takes the barrier's fallback (the whole-tensor maximum): selected
+    through NVFP4_QUANT_PATH / NVFP4_QUANT_SPIN_LIMIT in a separate process (the library reads
+    them once per process).  Every kernel ends normally in all three."""
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     import os

@@ -179,6 +179,26 @@ nvfp4_status nvfp4_gemm_w4a4(const void *a_bf16, int64_t m, int64_t k, int64_t l
                              int64_t ld_y, void *ws, size_t ws_bytes, void *stream);
 
 /* ---------------------------------------------------------------------------------------------
+ * nvfp4_gemm_w4a4_noalloc — nvfp4_gemm_w4a4 without a caller workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation).  Same arguments, results and errors as nvfp4_gemm_w4a4, with the
+ * library's own scratch in place of `ws`: a static device array of NVFP4_NOALLOC_SCRATCH_BYTES
+ * (64 MiB) per GPU, loaded on a device at the first call there and held until the process ends.
+ *   - Shapes whose nvfp4_gemm_workspace_bytes(m, n, k) exceeds NVFP4_NOALLOC_SCRATCH_BYTES return
+ *     NVFP4_ERR_WORKSPACE, launching nothing (e.g. activations quantized inside the call up to
+ *     about 59 million values for k = 4096 without a K split).
+ *   - The call allocates nothing (no hipMalloc / hipFree); its first call on a device looks up
+ *     the array's device address (hipGetSymbolAddress) and keeps it.
+ *   - Every call on one GPU shares that GPU's array and leaves its contents behind (nothing in
+ *     it needs clearing between calls): calls that may overlap in time on one GPU (different
+ *     streams, or host threads) race on it and must be serialized by the caller.
+ * ------------------------------------------------------------------------------------------- */
+#define NVFP4_NOALLOC_SCRATCH_BYTES (64u * 1024u * 1024u)
+nvfp4_status nvfp4_gemm_w4a4_noalloc(const void *a_bf16, int64_t m, int64_t k, int64_t ld_a,
+                                     const nvfp4_tensor *a_q, const nvfp4_tensor *w, void *y,
+                                     int64_t ld_y, void *stream);
+
+/* ---------------------------------------------------------------------------------------------
  * nvfp4_gemm_w4a16 — weight-only product: NVFP4 weights, 16-bit activations ("NVFP4 Dynamic
  * Quantization in Practice", section "The Meaning and Advantages of W4A4": in W4A16 the 4-bit
  * weights are reconstructed to 16-bit floating point for the multiply, which mainly relieves

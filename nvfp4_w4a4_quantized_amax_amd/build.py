@@ -12,7 +12,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(HERE, "libnvfp4.so")
-SOURCES = ["quantize.hip", "dequantize.hip", "gemm.hip", "mxfp4.hip", "mse.hip", "api.hip"]
+SOURCES = ["quantize.hip", "dequantize.hip", "gemm.hip", "mxfp4.hip", "mse.hip", "api.hip",
+           "noalloc.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

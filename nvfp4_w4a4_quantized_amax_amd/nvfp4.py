@@ -28,6 +28,7 @@ EXPORTED = (
     "nvfp4_quantize_2d", "nvfp4_dequantize", "nvfp4_gemm_w4a4", "nvfp4_grouped_gemm_w4a4",
     "nvfp4_gemm_w4a16", "nvfp4_mxfp4_quantize", "nvfp4_mxfp4_dequantize",
     "nvfp4_mxfp4_gemm_workspace_bytes", "nvfp4_mxfp4_gemm", "nvfp4_quantize_mse",
+    "nvfp4_gemm_w4a4_noalloc",
 )
 
 
@@ -69,6 +70,9 @@ _lib.nvfp4_dequantize.restype = ctypes.c_int
 _lib.nvfp4_dequantize.argtypes = [_pt, _vp, _i64, ctypes.c_int, _vp]
 _lib.nvfp4_gemm_w4a4.restype = ctypes.c_int
 _lib.nvfp4_gemm_w4a4.argtypes = [_vp, _i64, _i64, _i64, _pt, _pt, _vp, _i64, _vp, _sz, _vp]
+_lib.nvfp4_gemm_w4a4_noalloc.restype = ctypes.c_int
+_lib.nvfp4_gemm_w4a4_noalloc.argtypes = [_vp, _i64, _i64, _i64, _pt, _pt, _vp, _i64, _vp]
+NOALLOC_SCRATCH_BYTES = 64 * 1024 * 1024
 _lib.nvfp4_gemm_w4a16.restype = ctypes.c_int
 _lib.nvfp4_gemm_w4a16.argtypes = [_vp, _i64, _i64, _i64, _pt, _vp, _i64, _vp]
 _lib.nvfp4_mxfp4_quantize.restype = ctypes.c_int
@@ -236,6 +240,26 @@ def gemm_w4a4(a, w, y=None, a_q=None, ws=None):
                                 ctypes.byref(ac) if ac is not None else None, ctypes.byref(wc),
                                 _ptr(y), y.stride(0), _ptr(ws), ws.numel(), _stream(dev)),
            "nvfp4_gemm_w4a4")
+    return y
+
+
+def gemm_w4a4_noalloc(a, w, y, a_q=None):
+    """gemm_w4a4 with the library's own scratch instead of a workspace (nothing is allocated;
+    `y` must be given).  Calls that overlap on one GPU race on that scratch."""
+    if isinstance(a, QTensor):
+        m, k = a.rows, a.cols
+        a_bf16, a_q = None, a
+        dev = a.codes.device
+    else:
+        assert a.dtype == torch.bfloat16 and a.dim() == 2 and a.stride(1) == 1
+        m, k = a.shape
+        a_bf16, dev = a, a.device
+    wc = w.c()
+    ac = a_q.c() if a_q is not None else None
+    _check(_lib.nvfp4_gemm_w4a4_noalloc(
+        _ptr(a_bf16), m, k, a_bf16.stride(0) if a_bf16 is not None else 0,
+        ctypes.byref(ac) if ac is not None else None, ctypes.byref(wc), _ptr(y), y.stride(0),
+        _stream(dev)), "nvfp4_gemm_w4a4_noalloc")
     return y
 
 

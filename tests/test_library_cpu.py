@@ -213,3 +213,17 @@ def test_empty_problems_need_no_buffers():
     assert L.nvfp4_quantize_1d(None, 0, 40, 64, ctypes.byref(q1), None, 0, None) != nv.OK
     assert L.nvfp4_grouped_gemm_w4a4(None, 0, 64, 64, None, None, 5, None, 2, ctypes.byref(w),
                                      16, None, 16, None, 0, None) == nv.ERR_SHAPE
+
+
+def test_noalloc_validation():
+    """The allocation-free product refuses, before touching a device, shapes whose workspace
+    would exceed its fixed scratch, and the usual bad arguments."""
+    w = qt(1024, 8192, 16)
+    f = L.nvfp4_gemm_w4a4_noalloc
+    assert f(FAKE, 16, 8192, 8192, None, None, FAKE, 1024, None) == nv.ERR_NULL
+    assert f(FAKE, 16, 8200, 8200, None, ctypes.byref(w), FAKE, 1024, None) == nv.ERR_SHAPE
+    assert f(FAKE, -1, 8192, 8192, None, ctypes.byref(w), FAKE, 1024, None) == nv.ERR_SHAPE
+    assert f(FAKE, 0, 8192, 8192, None, ctypes.byref(w), FAKE, 1024, None) == nv.OK
+    assert L.nvfp4_gemm_workspace_bytes(16384, 1024, 8192) > nv.NOALLOC_SCRATCH_BYTES
+    assert f(FAKE, 16384, 8192, 8192, None, ctypes.byref(w), FAKE, 1024,
+             None) == nv.ERR_WORKSPACE

@@ -49,8 +49,9 @@ def parse():
 def timed(fn, steps, warmup, torch, stats=True):
     """ms per call of fn(i): the average over `steps` calls bracketed by two HIP events on the
     current stream (the one the library launches on), after `warmup` calls.  With `stats`, a
-    second pass records an event between consecutive calls and adds the median, p10 and p90 of
-    the per-call times.  Returns (mean_ms, stats dict or None)."""
+    second pass times up to 10 batches of consecutive calls the same way (no event between the
+    calls of a batch: an event per call adds its own gap to every small kernel) and adds the
+    median, p10 and p90 of the batches' per-call times.  Returns (mean_ms, stats or None)."""
     for i in range(warmup):
         fn(i)
     torch.cuda.synchronize()
@@ -65,15 +66,21 @@ def timed(fn, steps, warmup, torch, stats=True):
     mean = start.elapsed_time(end) / steps
     if not stats:
         return mean, None
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
-    ev[0].record(stream)
-    for i in range(steps):
-        fn(i)
-        ev[i + 1].record(stream)
+    nb = min(10, steps)
+    per_batch = max(1, steps // nb)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * nb)]
+    i = 0
+    for b in range(nb):
+        ev[2 * b].record(stream)
+        for _ in range(per_batch):
+            fn(i)
+            i += 1
+        ev[2 * b + 1].record(stream)
     torch.cuda.synchronize()
-    per = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
+    per = sorted(ev[2 * b].elapsed_time(ev[2 * b + 1]) / per_batch for b in range(nb))
     q = lambda f: per[min(len(per) - 1, int(round(f * (len(per) - 1))))]
-    return mean, {"median_ms": q(0.5), "p10_ms": q(0.1), "p90_ms": q(0.9), "calls": steps}
+    return mean, {"median_ms": q(0.5), "p10_ms": q(0.1), "p90_ms": q(0.9), "batches": nb,
+                  "calls_per_batch": per_batch}
 
 
 def clocks():
@@ -243,13 +250,13 @@ def extra_workloads(args, torch, np, nv, W, only):
                               shape=[m, n, k],
                               note="includes the dynamic quantization of A inside the call; "
                                    "3 rotating input/output sets")
-        aq = nv.quantize_1d(a0)
-        ms, st = timed(lambda i: nv.gemm_w4a4(aq, Ws[i % ns], y=Ys[i % ns], ws=ws), ps, warm,
-                       torch)
+        aqs = [nv.quantize_1d(a) for a in As]
+        ms, st = timed(lambda i: nv.gemm_w4a4(aqs[i % ns], Ws[i % ns], y=Ys[i % ns], ws=ws), ps,
+                       warm, torch)
         out["prefill_prequantized"] = _rec(ms, st, None, 2 * m * n * k, "mfma",
                                            FP16_MFMA_PEAK_TFLOPS, shape=[m, n, k],
                                            note="A quantized beforehand (the product kernel)")
-        del As, Ws, Ys, aq
+        del As, Ws, Ys, aqs
 
     if not only or "moe" in only:
         d = W.moe()

@@ -312,6 +312,62 @@ __device__ __forceinline__ int scale_code(uint32_t bam, const QuantTables &tab, 
   return scale_code(bam, tab, tab.inv6gs, k_out);
 }
 
+// Direct block-scale lookup for the encode loops.  Every |max| bf16 pattern p from the first
+// scale threshold T1 (the smallest pattern whose code is >= 1) up to the last one T126 gets its
+// own entry, filled with scale_code(p) itself, so the lookup is exact by construction:
+//   entry 0       : p < T1          -> code 0, multiplier 0
+//   entry i       : p = T1 - 1 + i  (1 <= i <= T126 - T1)
+//   entry top     : p >= T126       -> code 126 (top = T126 - T1 + 1)
+// The thresholds span log2(432 * 2^10) = 18.75 binades of bf16, about 2400 patterns, for every
+// global scale of the supported input range (amax in [2^-96, bf16 max]), and fewer where they
+// fall among bf16 subnormals.  With gs = 0 (an all-zero tensor) the table is the single entry
+// 0 (code 0, multiplier 0) for every pattern.  A block's code is then one subtraction, one
+// clamp and two independent LDS reads.
+constexpr int kCodeLutEntries = 2432;
+struct CodeLut {
+  int32_t off;  // T1 - 1
+  int32_t top;  // index of the last entry
+  uint8_t code[kCodeLutEntries];
+  float k[kCodeLutEntries];
+};
+
+// Fill `L` from the tables `t` (already built: call after build_tables).  Every thread of the
+// workgroup must call it; ends with a barrier.  Returns false (and fills the single zero entry)
+// for a global scale without usable thresholds: gs = 0, or outside the supported range, where
+// the thresholds leave the table's size (never for the supported range).
+__device__ inline bool build_code_lut(CodeLut &L, const QuantTables &t) {
+  const float inv6gs = t.inv6gs;
+  const int32_t t1 = (int32_t)t.ent[0].x, t126 = (int32_t)t.ent[125].x;
+  const int32_t top = t126 - t1 + 1;
+  const bool use = inv6gs > 0.0f && t1 >= 1 && top >= 1 && top < kCodeLutEntries;
+  if (use) {
+    for (int i = threadIdx.x; i <= top; i += blockDim.x) {
+      float k;
+      const int c = scale_code((uint32_t)(t1 - 1 + i), t, inv6gs, &k);
+      L.code[i] = (uint8_t)c;
+      L.k[i] = k;
+    }
+  } else if (threadIdx.x == 0) {
+    L.code[0] = 0;
+    L.k[0] = 0.0f;
+  }
+  if (threadIdx.x == 0) {
+    L.off = use ? t1 - 1 : 0x7FFF;
+    L.top = use ? top : 0;
+  }
+  __syncthreads();
+  return use;
+}
+
+// Block-scale code and multiplier from the lookup table; off and top as loaded from L once per
+// wave.
+__device__ __forceinline__ int lut_code(uint32_t bam, const CodeLut &L, int32_t off, int32_t top,
+                                        float *k_out) {
+  const int32_t i = min(max((int32_t)bam - off, 0), top);
+  *k_out = L.k[i];
+  return L.code[i];
+}
+
 // Exact magnitude code of |x| (as a float) for block scale value sbv: compare with each
 // midpoint * sbv * gs through one FMA (mid * sbv has <= 7 bits, so the product is exact and the
 // sign of the FMA result is the sign of the exact difference).

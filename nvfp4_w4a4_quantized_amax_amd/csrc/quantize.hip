@@ -105,14 +105,14 @@ struct EncOut {
   int64_t ld_scales;
 };
 
-// Same, for a block whose |max| bf16 pattern `bam` is already known.
-template <bool CONTIG>
-__device__ __forceinline__ void encode_block_1d_bam(const uint4 &a, const uint4 &b, uint32_t bam,
-                                                    uint32_t blk, FastDiv bpr, const EncOut &o,
-                                                    const QuantTables &tab, float inv6gs,
-                                                    float gs) {
+// Encode one block whose |max| bf16 pattern `bam` is already known; `code_of(bam, &k)` gives
+// its scale code and element multiplier (the table search or the direct lookup).
+template <bool CONTIG, class CodeOf>
+__device__ __forceinline__ void encode_block_1d_with(const uint4 &a, const uint4 &b, uint32_t bam,
+                                                     uint32_t blk, FastDiv bpr, const EncOut &o,
+                                                     float gs, CodeOf code_of) {
   float k;
-  const int code = scale_code(bam, tab, inv6gs, &k);
+  const int code = code_of(bam, &k);
   const uint2 packed = encode16(a, b, k, code, gs);
   size_t co, so;
   if (CONTIG) {
@@ -126,6 +126,16 @@ __device__ __forceinline__ void encode_block_1d_bam(const uint4 &a, const uint4 
   }
   ntstore8(o.codes + co, packed);
   ntstore_u8(o.scales + so, (uint32_t)code);
+}
+
+template <bool CONTIG>
+__device__ __forceinline__ void encode_block_1d_bam(const uint4 &a, const uint4 &b, uint32_t bam,
+                                                    uint32_t blk, FastDiv bpr, const EncOut &o,
+                                                    const QuantTables &tab, float inv6gs,
+                                                    float gs) {
+  encode_block_1d_with<CONTIG>(a, b, bam, blk, bpr, o, gs, [&](uint32_t m, float *k) {
+    return scale_code(m, tab, inv6gs, k);
+  });
 }
 
 template <bool CONTIG>
@@ -199,6 +209,7 @@ __global__ __launch_bounds__(WAVES * 64, 1) void k_quantize_persistent(
     unsigned long long *__restrict__ slots, unsigned long long epoch, uint32_t spin_limit,
     float *__restrict__ gs_out, uint32_t *__restrict__ status) {
   __shared__ QuantTables tab;
+  __shared__ CodeLut lut;
   __shared__ uint32_t red[WAVES];
   __shared__ uint32_t s_amax, s_done;
   // LDS-resident tiles: [tile][half][wave][lane], one 16-byte half-block per lane, and each
@@ -338,46 +349,53 @@ __global__ __launch_bounds__(WAVES * 64, 1) void k_quantize_persistent(
   const float gs = global_scale_from_amax_bits(s_amax);
   if (blockIdx.x == 0 && threadIdx.x == 0) *gs_out = gs;
   build_tables(tab, gs);
-  const float inv6gs = tab.inv6gs;
+  build_code_lut(lut, tab);
+  const int32_t lut_off = __builtin_amdgcn_readfirstlane(lut.off);
+  const int32_t lut_top = __builtin_amdgcn_readfirstlane(lut.top);
 
   // Phase 2: encode the register tiles; each freed register pair immediately starts the re-read
   // of one overflow tile.  Then the LDS tiles, then the prefetched overflow tiles; any further
-  // tiles are re-read and encoded one by one.
+  // tiles are re-read and encoded one by one.  Block scales come from the direct lookup table.
+  auto phase2 = [&](auto code_of) {
 #pragma unroll
-  for (int i = 0; i < RT; ++i) {
-    const uint32_t b = tile_block(LT + i);
-    if ((uint32_t)(LT + i) < cnt && b < n_blocks)
-      encode_block_1d_bam<CONTIG>(reg[2 * i], reg[2 * i + 1],
-                                  (i % 2 == 0) ? (bamr[i / 2] & 0xFFFFu) : (bamr[i / 2] >> 16), b,
-                                  bpr, o, tab, inv6gs, gs);
-    const uint32_t b2 = tile_block(LT + RT + i);
-    if ((uint32_t)(LT + RT + i) < cnt && b2 < n_blocks) {
-      const size_t idx = block_index<CONTIG>(b2, bpr, ld_x8);
-      reg[2 * i] = x[idx];
-      reg[2 * i + 1] = x[idx + 1];
+    for (int i = 0; i < RT; ++i) {
+      const uint32_t b = tile_block(LT + i);
+      if ((uint32_t)(LT + i) < cnt && b < n_blocks)
+        encode_block_1d_with<CONTIG>(reg[2 * i], reg[2 * i + 1],
+                                     (i % 2 == 0) ? (bamr[i / 2] & 0xFFFFu) : (bamr[i / 2] >> 16),
+                                     b, bpr, o, gs, code_of);
+      const uint32_t b2 = tile_block(LT + RT + i);
+      if ((uint32_t)(LT + RT + i) < cnt && b2 < n_blocks) {
+        const size_t idx = block_index<CONTIG>(b2, bpr, ld_x8);
+        reg[2 * i] = x[idx];
+        reg[2 * i + 1] = x[idx + 1];
+      }
     }
-  }
 #pragma unroll 2
-  for (int i = 0; i < LT; ++i) {
-    const uint32_t b = tile_block(i);
-    if ((uint32_t)i < cnt && b < n_blocks)
-      encode_block_1d_bam<CONTIG>(s_tiles[(2 * i) * WAVES + wave][lane],
-                                  s_tiles[(2 * i + 1) * WAVES + wave][lane],
-                                  s_bam[i * WAVES + wave][lane], b, bpr, o, tab, inv6gs, gs);
-  }
-#pragma unroll
-  for (int i = 0; i < RT; ++i) {
-    const uint32_t b = tile_block(LT + RT + i);
-    if ((uint32_t)(LT + RT + i) < cnt && b < n_blocks)
-      encode_block_1d<CONTIG>(reg[2 * i], reg[2 * i + 1], b, bpr, o, tab);
-  }
-  for (uint32_t i = LT + 2 * RT; i < cnt; ++i) {
-    const uint32_t b = tile_block(i);
-    if (b < n_blocks) {
-      const size_t idx = block_index<CONTIG>(b, bpr, ld_x8);
-      encode_block_1d<CONTIG>(x[idx], x[idx + 1], b, bpr, o, tab);
+    for (int i = 0; i < LT; ++i) {
+      const uint32_t b = tile_block(i);
+      if ((uint32_t)i < cnt && b < n_blocks)
+        encode_block_1d_with<CONTIG>(s_tiles[(2 * i) * WAVES + wave][lane],
+                                     s_tiles[(2 * i + 1) * WAVES + wave][lane],
+                                     s_bam[i * WAVES + wave][lane], b, bpr, o, gs, code_of);
     }
-  }
+#pragma unroll
+    for (int i = 0; i < RT; ++i) {
+      const uint32_t b = tile_block(LT + RT + i);
+      if ((uint32_t)(LT + RT + i) < cnt && b < n_blocks)
+        encode_block_1d_with<CONTIG>(reg[2 * i], reg[2 * i + 1],
+                                     absmax16(reg[2 * i], reg[2 * i + 1]), b, bpr, o, gs, code_of);
+    }
+    for (uint32_t i = LT + 2 * RT; i < cnt; ++i) {
+      const uint32_t b = tile_block(i);
+      if (b < n_blocks) {
+        const size_t idx = block_index<CONTIG>(b, bpr, ld_x8);
+        const uint4 a0 = x[idx], a1 = x[idx + 1];
+        encode_block_1d_with<CONTIG>(a0, a1, absmax16(a0, a1), b, bpr, o, gs, code_of);
+      }
+    }
+  };
+  phase2([&](uint32_t m, float *k) { return lut_code(m, lut, lut_off, lut_top, k); });
 }
 
 // ---------------------------------------------------------------------------------------------

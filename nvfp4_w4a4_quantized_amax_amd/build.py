@@ -40,6 +40,24 @@ def _compile(src, verbose):
     return obj
 
 
+PROBES = [("probes/mfma_routes.hip", "probes/mfma_routes")]
+
+
+def build_probes(verbose=False):
+    """Measurement programs beside the library (not linked into it): built as executables."""
+    outs = []
+    for src, exe in PROBES:
+        out = os.path.join(HERE, exe)
+        cmd = [HIPCC, *[f for f in FLAGS if f not in ("-fPIC",)], os.path.join(HERE, src), "-o", out]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}{r.stderr}")
+        outs.append(out)
+    return outs
+
+
 def build(verbose=False):
     os.makedirs(BUILD_DIR, exist_ok=True)
     with concurrent.futures.ThreadPoolExecutor(max_workers=4) as ex:
@@ -52,6 +70,7 @@ def build(verbose=False):
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
     os.replace(tmp, LIB_PATH)
+    build_probes(verbose)
     return LIB_PATH
 
 

@@ -40,7 +40,9 @@ def _compile(src, verbose):
     return obj
 
 
-PROBES = [("probes/mfma_routes.hip", "probes/mfma_routes")]
+PROBES = [("probes/mfma_routes.hip", "probes/mfma_routes"),
+          ("probes/hbm_rates.hip", "probes/hbm_rates"),
+          ("probes/launch_cost.hip", "probes/launch_cost")]
 
 
 def build_probes(verbose=False):

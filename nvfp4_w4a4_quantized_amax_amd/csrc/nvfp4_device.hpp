@@ -56,7 +56,9 @@ static_assert(kPersistentSlotOffset + kMaxPersistentSlots * 8 <= kPersistentStat
 // Small helpers
 // ---------------------------------------------------------------------------------------------
 
-// Fast unsigned division by a runtime constant d >= 1, valid for n < 2^31:
+// Fast unsigned division by a runtime constant d >= 1, valid for n < 2^31 (the published
+// division-by-invariant-integers method of Granlund and Montgomery, "Division by Invariant
+// Integers using Multiplication", 1994):
 // q = (umulhi(n, mul) + n) >> shift with shift = ceil(log2 d), mul = 2^32 (2^shift - d) / d + 1.
 struct FastDiv {
   uint32_t d, mul, shift;

@@ -610,6 +610,7 @@ static std::atomic<unsigned long long> g_epoch{0};
 static unsigned long long next_epoch() {
   unsigned long long e = g_epoch.fetch_add(1) + 1;
   if (e == 1) {  // first call in this process: start from an unpredictable 48-bit value
+    // (the seed is mixed with the SplitMix64 finalizer, a published 64-bit mixing function)
     const unsigned long long seed =
         (unsigned long long)std::chrono::steady_clock::now().time_since_epoch().count() ^
         ((unsigned long long)getpid() << 32) ^ (unsigned long long)(uintptr_t)&g_epoch;

@@ -96,6 +96,8 @@ int nvfp4_version(void);
  * of the single-read quantizer); the rest holds the quantized activations of the GEMM calls
  * and, for product shapes that split K across workgroups, their fp32 partial sums.
  * Calls that may overlap in time (different streams) need different workspaces.
+ * Sizes: every row count, column count, K and leading dimension passed to this library must lie
+ * below 2^31 (else NVFP4_ERR_SHAPE); for such sizes the workspace queries return SIZE_MAX.
  * ------------------------------------------------------------------------------------------- */
 size_t nvfp4_quantize_workspace_bytes(int64_t rows, int64_t cols);
 size_t nvfp4_gemm_workspace_bytes(int64_t m, int64_t n, int64_t k);

@@ -16,6 +16,11 @@ namespace {
 
 constexpr size_t kAlign = 256;
 
+// Every size and leading dimension the calls accept lies in [0, 2^31): products of two of them
+// (byte counts, element counts) then fit in 62 bits, so no size computation below can overflow.
+constexpr int64_t kDimLimit = (int64_t)1 << 31;
+inline bool dim_ok(int64_t v) { return v >= 0 && v < kDimLimit; }
+
 inline size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 inline bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
@@ -54,6 +59,8 @@ nvfp4_status check_mx_tensor(const mxfp4_tensor *t, int64_t rows, int64_t cols) 
   if (!t) return NVFP4_ERR_NULL;
   if (!t->codes || !t->scales) return NVFP4_ERR_NULL;
   if (t->rows != rows || t->cols != cols) return NVFP4_ERR_SHAPE;
+  if (!dim_ok(rows) || !dim_ok(cols) || !dim_ok(t->ld_codes) || !dim_ok(t->ld_scales))
+    return NVFP4_ERR_SHAPE;
   if (cols <= 0 || cols % 32 || rows < 0) return NVFP4_ERR_SHAPE;
   if (t->ld_codes < cols / 2 || t->ld_scales < cols / 32) return NVFP4_ERR_SHAPE;
   if (!aligned(t->codes, 16) || t->ld_codes % 16) return NVFP4_ERR_ALIGN;
@@ -83,6 +90,8 @@ nvfp4_status check_tensor(const nvfp4_tensor *t, int64_t rows, int64_t cols, boo
   if (t->reserved != 0) return NVFP4_ERR_UNSUPPORTED;
   if (t->block_rows != 1 && t->block_rows != 16) return NVFP4_ERR_UNSUPPORTED;
   if (t->rows != rows || t->cols != cols) return NVFP4_ERR_SHAPE;
+  if (!dim_ok(rows) || !dim_ok(cols) || !dim_ok(t->ld_codes) || !dim_ok(t->ld_scales))
+    return NVFP4_ERR_SHAPE;
   if (cols <= 0 || cols % 16 || rows < 0) return NVFP4_ERR_SHAPE;
   if (t->block_rows == 16 && rows % 16) return NVFP4_ERR_SHAPE;
   if (t->ld_codes < cols / 2 || t->ld_scales < cols / 16) return NVFP4_ERR_SHAPE;
@@ -93,7 +102,8 @@ nvfp4_status check_tensor(const nvfp4_tensor *t, int64_t rows, int64_t cols, boo
 
 nvfp4_status check_bf16_input(const void *x, int64_t rows, int64_t cols, int64_t ld) {
   if (!x) return NVFP4_ERR_NULL;
-  if (rows < 0 || cols <= 0 || cols % 16 || ld < cols) return NVFP4_ERR_SHAPE;
+  if (!dim_ok(rows) || !dim_ok(cols) || !dim_ok(ld)) return NVFP4_ERR_SHAPE;
+  if (cols <= 0 || cols % 16 || ld < cols) return NVFP4_ERR_SHAPE;
   if (!aligned(x, 16) || ld % 8) return NVFP4_ERR_ALIGN;
   // 32-bit chunk indexing inside the quantize kernels
   if (rows * (cols / 8) >= (int64_t)1 << 31) return NVFP4_ERR_SHAPE;
@@ -182,6 +192,7 @@ size_t nvfp4_quantize_workspace_bytes(int64_t rows, int64_t cols) {
 
 size_t nvfp4_gemm_workspace_bytes(int64_t m, int64_t n, int64_t k) {
   if (m < 0 || k <= 0) return kWsHeaderBytes;
+  if (!dim_ok(m) || !dim_ok(k) || n >= kDimLimit) return SIZE_MAX;  // no call accepts these
   return packed_layout(m, k).end + partial_bytes(m, n, k);
 }
 
@@ -190,6 +201,7 @@ size_t nvfp4_grouped_gemm_workspace_bytes(int64_t tokens, int64_t k, int64_t tot
   (void)total_rows;
   (void)num_groups;
   if (tokens < 0 || k <= 0) return kWsHeaderBytes;
+  if (!dim_ok(tokens) || !dim_ok(k)) return SIZE_MAX;  // no call accepts these
   return packed_layout(tokens, k).end;
 }
 
@@ -252,7 +264,7 @@ nvfp4_status nvfp4_dequantize(const nvfp4_tensor *q, void *y, int64_t ld_y, int 
   if (s) return s;
   if (!y) return NVFP4_ERR_NULL;
   if (out_dtype != NVFP4_OUT_BF16 && out_dtype != NVFP4_OUT_F32) return NVFP4_ERR_UNSUPPORTED;
-  if (ld_y < q->cols) return NVFP4_ERR_SHAPE;
+  if (ld_y < q->cols || !dim_ok(ld_y)) return NVFP4_ERR_SHAPE;
   if (!aligned(q->codes, 4) || q->ld_codes % 4 || !aligned(y, 16) || ld_y % 8)
     return NVFP4_ERR_ALIGN;
   if (q->rows == 0) return NVFP4_OK;
@@ -272,7 +284,7 @@ nvfp4_status nvfp4_gemm_w4a4(const void *a_bf16, int64_t m, int64_t k, int64_t l
   nvfp4_status s = check_tensor(w, n, k, true);
   if (s) return s;
   if (n < 1 || n >= ((int64_t)1 << 30) || m >= ((int64_t)1 << 30)) return NVFP4_ERR_SHAPE;
-  if (ld_y < n) return NVFP4_ERR_SHAPE;
+  if (ld_y < n || !dim_ok(ld_y)) return NVFP4_ERR_SHAPE;
   if (!aligned(y, 4) || ld_y % 2) return NVFP4_ERR_ALIGN;
   if (a_bf16) {
     s = check_bf16_input(a_bf16, m, k, ld_a);
@@ -345,7 +357,7 @@ nvfp4_status nvfp4_gemm_w4a16(const void *a_bf16, int64_t m, int64_t k, int64_t 
   nvfp4_status s = check_tensor(w, n, k, true);
   if (s) return s;
   if (n < 1 || n >= ((int64_t)1 << 30)) return NVFP4_ERR_SHAPE;
-  if (ld_y < n) return NVFP4_ERR_SHAPE;
+  if (ld_y < n || !dim_ok(ld_y)) return NVFP4_ERR_SHAPE;
   if (!aligned(y, 4) || ld_y % 2) return NVFP4_ERR_ALIGN;
   s = check_bf16_input(a_bf16, m, k, ld_a);
   if (s) return s;
@@ -370,10 +382,11 @@ nvfp4_status nvfp4_grouped_gemm_w4a4(const void *a_bf16, int64_t tokens, int64_t
   if (!y || !offsets) return NVFP4_ERR_NULL;
   if (total_rows >= ((int64_t)1 << 30) || tokens >= ((int64_t)1 << 30)) return NVFP4_ERR_SHAPE;
   if (!row_index && tokens != total_rows) return NVFP4_ERR_SHAPE;
+  if (!dim_ok(n)) return NVFP4_ERR_SHAPE;  // num_groups * n below stays within 2^41
   nvfp4_status s = check_tensor(w, (int64_t)num_groups * n, k, true);
   if (s) return s;
   if (w->block_rows == 16 && n % 16) return NVFP4_ERR_SHAPE;
-  if (ld_y < n) return NVFP4_ERR_SHAPE;
+  if (ld_y < n || !dim_ok(ld_y)) return NVFP4_ERR_SHAPE;
   if (!aligned(y, 4) || ld_y % 2) return NVFP4_ERR_ALIGN;
   if (a_bf16) {
     s = check_bf16_input(a_bf16, tokens, k, ld_a);
@@ -427,6 +440,7 @@ nvfp4_status nvfp4_grouped_gemm_w4a4(const void *a_bf16, int64_t tokens, int64_t
 
 size_t nvfp4_mxfp4_gemm_workspace_bytes(int64_t m, int64_t k) {
   if (m <= 0 || k <= 0) return 0;
+  if (!dim_ok(m) || !dim_ok(k)) return SIZE_MAX;  // no call accepts these
   return mx_layout(m, k).end;
 }
 
@@ -450,7 +464,7 @@ nvfp4_status nvfp4_mxfp4_dequantize(const mxfp4_tensor *q, void *y, int64_t ld_y
   if (s) return s;
   if (!y) return NVFP4_ERR_NULL;
   if (out_dtype != NVFP4_OUT_BF16 && out_dtype != NVFP4_OUT_F32) return NVFP4_ERR_UNSUPPORTED;
-  if (ld_y < q->cols) return NVFP4_ERR_SHAPE;
+  if (ld_y < q->cols || !dim_ok(ld_y)) return NVFP4_ERR_SHAPE;
   if (!aligned(y, 16) || ld_y % 8) return NVFP4_ERR_ALIGN;
   if (q->rows * (q->cols / 8) >= (int64_t)1 << 31) return NVFP4_ERR_SHAPE;
   return hip_status(launch_mx_dequantize(q->codes, q->ld_codes, q->scales, q->ld_scales, q->rows,
@@ -469,7 +483,7 @@ nvfp4_status nvfp4_mxfp4_gemm(const void *a_bf16, int64_t m, int64_t k, int64_t 
   nvfp4_status s = check_mx_tensor(w, n, k);
   if (s) return s;
   if (n < 1 || n >= ((int64_t)1 << 30) || m >= ((int64_t)1 << 30)) return NVFP4_ERR_SHAPE;
-  if (ld_y < n) return NVFP4_ERR_SHAPE;
+  if (ld_y < n || !dim_ok(ld_y)) return NVFP4_ERR_SHAPE;
   if (!aligned(y, 4) || ld_y % 2) return NVFP4_ERR_ALIGN;
   if (a_q) {
     s = check_mx_tensor(a_q, m, k);

@@ -227,3 +227,24 @@ def test_noalloc_validation():
     assert L.nvfp4_gemm_workspace_bytes(16384, 1024, 8192) > nv.NOALLOC_SCRATCH_BYTES
     assert f(FAKE, 16384, 8192, 8192, None, ctypes.byref(w), FAKE, 1024,
              None) == nv.ERR_WORKSPACE
+
+
+def test_sizes_below_two_to_the_31():
+    """Every size and leading dimension must lie below 2^31: larger ones are refused before any
+    size arithmetic, and the workspace queries answer SIZE_MAX for them instead of a wrapped
+    product (the same edges run under the sanitizers in test_host_sanitizers)."""
+    size_max = 2 ** 64 - 1
+    big = 1 << 31
+    assert L.nvfp4_gemm_workspace_bytes(big, 4096, 4096) == size_max
+    assert L.nvfp4_gemm_workspace_bytes(64, 4096, big) == size_max
+    assert L.nvfp4_gemm_workspace_bytes(64, big, 4096) == size_max
+    assert L.nvfp4_grouped_gemm_workspace_bytes(big, 4096, 64, 8) == size_max
+    assert L.nvfp4_mxfp4_gemm_workspace_bytes(64, big) == size_max
+    assert L.nvfp4_gemm_workspace_bytes(big - 1, 16, 4096) < size_max
+    assert q1d(FAKE, big, 64, 64, qt(big, 64)) == nv.ERR_SHAPE
+    assert q1d(FAKE, 32, 64, big, qt(32, 64)) == nv.ERR_SHAPE
+    assert L.nvfp4_dequantize(ctypes.byref(qt(32, 64)), FAKE, big, 0, None) == nv.ERR_SHAPE
+    w = qt(128, 256, 16)
+    assert gemm(FAKE, 64, 256, 256, None, w, ld_y=big) == nv.ERR_SHAPE
+    assert grouped(FAKE, 32, 128, None, FAKE, 64, FAKE, 8, qt(8 * 64, 128, 16), big) == \
+        nv.ERR_SHAPE

@@ -1100,12 +1100,18 @@ __device__ __forceinline__ void decode_band_loop(const SmallMArgs &p, const WBuf
 }
 
 // W4A4.  FUSED: A arrives as bf16 and every workgroup quantizes it itself (amax over all of A,
-// the FP32 global scale and the scale tables, then its waves encode their own K slices), exactly
-// as nvfp4_quantize_1d would; workgroup 0 also writes the quantized A when asked to.  A is at
-// most 16 rows, so the redundant work is small and no workgroup waits for another.
-template <bool W2D, bool FUSED, bool FULL, int WIN>
+// the FP32 global scale and the scale tables, then the codes of every K slice), exactly as
+// nvfp4_quantize_1d would; workgroup 0 also writes the quantized A when asked to.  A is at most
+// 16 rows, so the redundant work is small and no workgroup waits for another.
+// LEAD (FUSED with one activation row): wave 0 alone loads the row, finds its amax, builds the
+// tables and encodes every slice, while the other waves' W rings are already in flight; they
+// meet it at one barrier.  Otherwise each wave loads and encodes its own slice, and the rings
+// start after the amax barrier (a W ring issued before it delays the activation loads of the
+// waves that start later).
+template <bool W2D, bool FUSED, bool FULL, int WIN, bool LEAD = false>
 __global__ __launch_bounds__(kDecWaves * 64) void k_gemm_decode(SmallMArgs p) {
-  constexpr int D = dec_depth(WIN, FULL && !FUSED);
+  static_assert(!LEAD || FUSED, "the lead-wave form quantizes A");
+  constexpr int D = dec_depth(WIN, FULL && (!FUSED || LEAD));
   __shared__ floatx4_t s_red[D][kDecWaves][kWave];
   __shared__ QuantTables tab;
   __shared__ uint32_t red[kDecWaves];
@@ -1130,65 +1136,112 @@ __global__ __launch_bounds__(kDecWaves * 64) void k_gemm_decode(SmallMArgs p) {
   float gs_a = 0.0f;
   DecodeW<WIN> ring[D];
   if (FUSED) {
-    // Each wave loads its own K slice of all m rows of A, coalesced: step j gives lane l the
-    // 16-value block j * 64 + l of the slice (row = block / bps, bps blocks per row); lanes past
-    // the slice reload its last block (or A's first block when the slice is empty), which leaves
-    // the maximum unchanged; steps wholly past the slice load nothing.  The registers give this
-    // workgroup's share of the global amax and are then encoded in place; the codes reach the
-    // MFMA layout through the wave's own corner of LDS.  W's ring is issued once every wave
-    // holds its A: issued earlier, the A loads of the later waves wait behind the W stream of
-    // the whole chip (measured: A of the last wave slot about 2 us after the first), and the
-    // amax that every wave needs waits for the last of them.
     const int64_t kb0 = win0 * 8;                                       // first block of the slice
     const int bps = (int)max((int64_t)0, min(per * 8, kblocks - kb0));  // blocks per row
-    const int nblk = (int)p.m * bps;                                    // <= 16 * 16
-    uint4 xa[4][2];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if (j == 0 || j * 64 < nblk) {  // steps past the slice (small M) load nothing
-        const int blk = min(j * 64 + lane, max(nblk - 1, 0));
-        const int r = bps > 0 ? blk / bps : 0, c = bps > 0 ? blk - r * bps : 0;
-        const uint16_t *src = p.a_bf16 + r * p.ld_a + (bps > 0 ? kb0 + c : 0) * 16;
-        xa[j][0] = *(const uint4 *)src;
-        xa[j][1] = *(const uint4 *)(src + 8);
-      } else {
-        xa[j][0] = xa[j][1] = make_uint4(0u, 0u, 0u, 0u);
-      }
-    }
-    uint32_t mx = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) mx = max(mx, absmax16(xa[j][0], xa[j][1]));
-    mx = wave_max_u32(mx);
-    if (lane == 0) red[wave] = mx;
-    __syncthreads();
-    decode_ring_start<W2D, FULL, WIN>(p, buf, nbands, i16, q, win0, nw, ring);
-    mx = red[0];
-#pragma unroll
-    for (int w2 = 1; w2 < kDecWaves; ++w2) mx = max(mx, red[w2]);
-    gs_a = global_scale_from_amax_bits(mx);
-    build_tables(tab, gs_a);
-    if (p.aq_gs && blockIdx.x == 0 && threadIdx.x == 0) *p.aq_gs = gs_a;
-    const float inv6gs = tab.inv6gs;
-    // Encode; codes and scales of the slice go to this wave's LDS corner (row-major, 16 blocks
-    // per row at most) and, for workgroup 0, to the caller's quantized A.
     uint8_t *lc = s_acodes[wave], *ls = s_ascales[wave];
+    if (LEAD) {
+      // Wave 0: lane l takes blocks l, l + 64, l + 128, l + 192 of the row (K <= 4096); lanes
+      // past the row reload its last block, which leaves the maximum unchanged.  Its own W ring
+      // goes out after these loads; the other waves issue theirs at once.
+      if (wave == 0) {
+        constexpr int kLB = 4;
+        const int nb = (int)kblocks;
+        uint4 xa[kLB][2];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int blk = j * 64 + lane;
-      if (blk < nblk) {
-        const int r = blk / bps, c = blk - r * bps;
-        float kq;
-        const int code = scale_code(absmax16(xa[j][0], xa[j][1]), tab, inv6gs, &kq);
-        const uint2 e = encode16(xa[j][0], xa[j][1], kq, code, gs_a);
-        *(uint2 *)(lc + (r * 16 + c) * 8) = e;
-        ls[r * 16 + c] = (uint8_t)code;
-        if (blockIdx.x == 0) {
-          if (p.aq_codes) ntstore8(p.aq_codes + r * p.a.ld_codes + (kb0 + c) * 8, e);
-          if (p.aq_scales) ntstore_u8(p.aq_scales + r * p.a.ld_scales + kb0 + c, (uint32_t)code);
+        for (int j = 0; j < kLB; ++j) {
+          const uint16_t *src = p.a_bf16 + (int64_t)min(j * 64 + lane, nb - 1) * 16;
+          xa[j][0] = *(const uint4 *)src;
+          xa[j][1] = *(const uint4 *)(src + 8);
+        }
+        decode_ring_start<W2D, FULL, WIN>(p, buf, nbands, i16, q, win0, nw, ring);
+        uint32_t mx = 0;
+#pragma unroll
+        for (int j = 0; j < kLB; ++j) mx = max(mx, absmax16(xa[j][0], xa[j][1]));
+        mx = wave_max_u32(mx);
+        const float g = global_scale_from_amax_bits(mx);
+        build_tables_one_wave(tab, g);
+        if (p.aq_gs && blockIdx.x == 0 && lane == 0) *p.aq_gs = g;
+        const float inv6gs = inv6gs_of(g);
+        const int spw = (int)per * 8;  // blocks of one wave's slice
+#pragma unroll
+        for (int j = 0; j < kLB; ++j) {
+          const int b = j * 64 + lane;
+          if (b < nb) {
+            float kq;
+            const int code = scale_code(absmax16(xa[j][0], xa[j][1]), tab, inv6gs, &kq);
+            const uint2 e = encode16(xa[j][0], xa[j][1], kq, code, g);
+            const int w = b / spw, c = b - w * spw;
+            *(uint2 *)(s_acodes[w] + c * 8) = e;
+            s_ascales[w][c] = (uint8_t)code;
+            if (blockIdx.x == 0) {
+              if (p.aq_codes) ntstore8(p.aq_codes + b * 8, e);
+              if (p.aq_scales) ntstore_u8(p.aq_scales + b, (uint32_t)code);
+            }
+          }
+        }
+      } else {
+        decode_ring_start<W2D, FULL, WIN>(p, buf, nbands, i16, q, win0, nw, ring);
+      }
+      __syncthreads();
+      gs_a = tab.gs;
+    } else {
+      // Each wave loads its own K slice of all m rows of A, coalesced: step j gives lane l the
+      // 16-value block j * 64 + l of the slice (row = block / bps, bps blocks per row); lanes past
+      // the slice reload its last block (or A's first block when the slice is empty), which leaves
+      // the maximum unchanged; steps wholly past the slice load nothing.  The registers give this
+      // workgroup's share of the global amax and are then encoded in place; the codes reach the
+      // MFMA layout through the wave's own corner of LDS.  W's ring is issued once every wave
+      // holds its A: issued earlier, the A loads of the later waves wait behind the W stream of
+      // the whole chip (measured: A of the last wave slot about 2 us after the first), and the
+      // amax that every wave needs waits for the last of them.
+      const int nblk = (int)p.m * bps;                                    // <= 16 * 16
+      uint4 xa[4][2];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (j == 0 || j * 64 < nblk) {  // steps past the slice (small M) load nothing
+          const int blk = min(j * 64 + lane, max(nblk - 1, 0));
+          const int r = bps > 0 ? blk / bps : 0, c = bps > 0 ? blk - r * bps : 0;
+          const uint16_t *src = p.a_bf16 + r * p.ld_a + (bps > 0 ? kb0 + c : 0) * 16;
+          xa[j][0] = *(const uint4 *)src;
+          xa[j][1] = *(const uint4 *)(src + 8);
+        } else {
+          xa[j][0] = xa[j][1] = make_uint4(0u, 0u, 0u, 0u);
         }
       }
+      uint32_t mx = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) mx = max(mx, absmax16(xa[j][0], xa[j][1]));
+      mx = wave_max_u32(mx);
+      if (lane == 0) red[wave] = mx;
+      __syncthreads();
+      decode_ring_start<W2D, FULL, WIN>(p, buf, nbands, i16, q, win0, nw, ring);
+      mx = red[0];
+#pragma unroll
+      for (int w2 = 1; w2 < kDecWaves; ++w2) mx = max(mx, red[w2]);
+      gs_a = global_scale_from_amax_bits(mx);
+      build_tables(tab, gs_a);
+      if (p.aq_gs && blockIdx.x == 0 && threadIdx.x == 0) *p.aq_gs = gs_a;
+      const float inv6gs = tab.inv6gs;
+      // Encode; codes and scales of the slice go to this wave's LDS corner (row-major, 16 blocks
+      // per row at most) and, for workgroup 0, to the caller's quantized A.
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int blk = j * 64 + lane;
+        if (blk < nblk) {
+          const int r = blk / bps, c = blk - r * bps;
+          float kq;
+          const int code = scale_code(absmax16(xa[j][0], xa[j][1]), tab, inv6gs, &kq);
+          const uint2 e = encode16(xa[j][0], xa[j][1], kq, code, gs_a);
+          *(uint2 *)(lc + (r * 16 + c) * 8) = e;
+          ls[r * 16 + c] = (uint8_t)code;
+          if (blockIdx.x == 0) {
+            if (p.aq_codes) ntstore8(p.aq_codes + r * p.a.ld_codes + (kb0 + c) * 8, e);
+            if (p.aq_scales) ntstore_u8(p.aq_scales + r * p.a.ld_scales + kb0 + c, (uint32_t)code);
+          }
+        }
+      }
+      __syncthreads();
     }
-    __syncthreads();
     // MFMA layout: lane (i16, q), window u holds blocks 8u + 2q and 8u + 2q + 1 of row i16.
     const bool a_ok = i16 < p.m;
 #pragma unroll
@@ -1821,23 +1874,30 @@ static bool decode_full(const SmallMArgs &p) {
          (srows - 1) * p.w.ld_scales + p.k / 16 < lim;
 }
 
-template <bool FUSED, bool FULL, int WIN>
+template <bool FUSED, bool FULL, int WIN, bool LEAD = false>
 static void launch_decode_t(const SmallMArgs &p, bool w2d, hipStream_t stream) {
   const dim3 grid(decode_grid(p.n)), block(kDecWaves * 64);
   if (w2d)
-    hipLaunchKernelGGL((k_gemm_decode<true, FUSED, FULL, WIN>), grid, block, 0, stream, p);
+    hipLaunchKernelGGL((k_gemm_decode<true, FUSED, FULL, WIN, LEAD>), grid, block, 0, stream, p);
   else
-    hipLaunchKernelGGL((k_gemm_decode<false, FUSED, FULL, WIN>), grid, block, 0, stream, p);
+    hipLaunchKernelGGL((k_gemm_decode<false, FUSED, FULL, WIN, LEAD>), grid, block, 0, stream, p);
+}
+
+// The fused form with one activation row takes the lead-wave kernel.
+template <bool FUSED, bool FULL, int WIN>
+static void launch_decode_m(const SmallMArgs &p, bool w2d, hipStream_t stream) {
+  if (FUSED && p.m == 1) launch_decode_t<FUSED, FULL, WIN, FUSED>(p, w2d, stream);
+  else launch_decode_t<FUSED, FULL, WIN>(p, w2d, stream);
 }
 
 template <bool FUSED>
 static hipError_t launch_decode(const SmallMArgs &p, bool w2d, hipStream_t stream) {
   const bool full = decode_full(p);
   const bool one = (p.k + 127) / 128 <= kDecWaves;  // one window per wave
-  if (full && one) launch_decode_t<FUSED, true, 1>(p, w2d, stream);
-  if (full && !one) launch_decode_t<FUSED, true, 2>(p, w2d, stream);
-  if (!full && one) launch_decode_t<FUSED, false, 1>(p, w2d, stream);
-  if (!full && !one) launch_decode_t<FUSED, false, 2>(p, w2d, stream);
+  if (full && one) launch_decode_m<FUSED, true, 1>(p, w2d, stream);
+  if (full && !one) launch_decode_m<FUSED, true, 2>(p, w2d, stream);
+  if (!full && one) launch_decode_m<FUSED, false, 1>(p, w2d, stream);
+  if (!full && !one) launch_decode_m<FUSED, false, 2>(p, w2d, stream);
   return hipGetLastError();
 }
 

@@ -216,63 +216,93 @@ __device__ __forceinline__ uint32_t scale_threshold(int s, double gsd) {
   return min(th, 0xFFFFu);
 }
 
-// Fill `t` (in LDS) for global scale gs.  Must be called by every thread of a workgroup of at
-// least 128 threads; ends with a barrier (the only one).  A usable gs lies in (0, 3e38);
-// otherwise every block gets scale 0.
-//
 // Scaling a block scale by 2^j scales the critical bf16 values around each midpoint by 2^j and
 // RN(1/S) by 2^-j, leaving x * k and every decision unchanged (no value leaves the normal range
 // for amax in the supported range).  So the multiplier only has to be checked for the 8 E4M3
 // mantissas (1 + m/8) * gs; the multiplier of any code is that of its mantissa times a power of
 // two.  Subnormal E4M3 codes normalize onto the same mantissas.
 //
-// Threads 0..127 (two whole waves) each write one entry.  Both waves run the 8 x 7 multiplier
-// checks themselves (lane 7m + i checks mantissa m at E2M1 midpoint i), combine them with a
-// ballot and pass the base multipliers around with shuffles, so nothing has to meet in LDS
-// before the entries are written.  When a mantissa's rounded reciprocal fails somewhere (about
-// one mantissa in six), its neighbouring floats are checked the same way, one midpoint per
-// lane, so the repair costs two more checks rather than up to fourteen in a row.
+// A wave runs the 8 x 7 multiplier checks itself (lane 7m + i checks mantissa m at E2M1
+// midpoint i), combines them with a ballot and passes the base multipliers around with
+// shuffles, so nothing has to meet in LDS before the entries are written.  When a mantissa's
+// rounded reciprocal fails somewhere (about one mantissa in six), its neighbouring floats are
+// checked the same way, one midpoint per lane, so the repair costs two more checks rather than
+// up to fourteen in a row.
+
+// The lane's base multiplier (lanes 7m, m = 0..7, hold mantissa m's; a negative value means no
+// float passed and blocks with that mantissa take the exact slow path).  Every lane of the wave
+// must call it (ballots).
+__device__ inline float table_base_multiplier(double gsd, bool usable) {
+  const int lane = threadIdx.x & 63;
+  const int m = lane / 7, i = lane - m * 7;
+  const bool checker = usable && lane < 56;
+  const double S = (1.0 + m * 0.125) * gsd;
+  float kb = checker ? (float)(1.0 / S) : 0.0f;
+  const bool ok = checker ? multiplier_ok_at(kb, S, i) : true;
+  const unsigned long long bad = __ballot(!ok);
+  if (bad) {  // uniform: the ballot is the same in every lane
+    // The rounded reciprocal of some mantissa fails somewhere: try the float above it, then
+    // the one below, else take the exact path (negative multiplier).
+    const float ku = __uint_as_float(__float_as_uint(kb) + 1u);
+    const float kd = __uint_as_float(__float_as_uint(kb) - 1u);
+    const unsigned long long bad_u = __ballot(checker && !multiplier_ok_at(ku, S, i));
+    const unsigned long long bad_d = __ballot(checker && !multiplier_ok_at(kd, S, i));
+    const unsigned long long mine = 0x7Full << (7 * m);
+    if (checker && (bad & mine)) kb = !(bad_u & mine) ? ku : (!(bad_d & mine) ? kd : -kb);
+  }
+  return kb;
+}
+
+// Table entry c (0..127) from the wave's base multipliers kb (table_base_multiplier); every lane
+// of the wave must call it (shuffles), each with its own c.  The multiplier of block-scale code
+// c is its mantissa's base multiplier (held by lane 7m) scaled by 2^-exponent; 0 outside 1..126.
+__device__ inline uint4 table_entry(int c, float kb, double gsd, bool usable) {
+  auto code_multiplier = [&](int cc) {
+    const uint32_t vb = __float_as_uint(e4m3_to_float((uint32_t)min(max(cc, 1), 126)));
+    const int mc = (int)((vb >> 20) & 7u);
+    const int E = (int)((vb >> 23) & 0xFFu) - 127;
+    const float base = __shfl(kb, 7 * mc, kWave);
+    return (usable && cc >= 1 && cc <= 126) ? ldexpf(base, -E) : 0.0f;
+  };
+  const uint32_t th = (c + 1 > 126 || !usable) ? 0xFFFFu : scale_threshold(c + 1, gsd);
+  const float k0 = code_multiplier(c), k1 = code_multiplier(c + 1);
+  return make_uint4(th, __float_as_uint(k0), __float_as_uint(k1), 0u);
+}
+
+__device__ __forceinline__ bool gs_usable(float gs) { return gs > 0.0f && gs < 3.0e38f; }
+
+// Fill `t` (in LDS) for global scale gs.  Must be called by every thread of a workgroup of at
+// least 128 threads; ends with a barrier (the only one).  A usable gs lies in (0, 3e38);
+// otherwise every block gets scale 0.  Threads 0..127 (two whole waves) each write one entry.
 __device__ inline void build_tables(QuantTables &t, float gs) {
   const int tid = threadIdx.x;
   const double gsd = (double)gs;
-  const bool usable = gs > 0.0f && gs < 3.0e38f;
+  const bool usable = gs_usable(gs);
   if (tid < 128) {
-    const int lane = tid & 63;
-    const int m = lane / 7, i = lane - m * 7;
-    const bool checker = usable && lane < 56;
-    const double S = (1.0 + m * 0.125) * gsd;
-    float kb = checker ? (float)(1.0 / S) : 0.0f;
-    const bool ok = checker ? multiplier_ok_at(kb, S, i) : true;
-    const unsigned long long bad = __ballot(!ok);
-    if (bad) {  // uniform: the ballot is the same in every lane
-      // The rounded reciprocal of some mantissa fails somewhere: try the float above it, then
-      // the one below, else take the exact path (negative multiplier).
-      const float ku = __uint_as_float(__float_as_uint(kb) + 1u);
-      const float kd = __uint_as_float(__float_as_uint(kb) - 1u);
-      const unsigned long long bad_u = __ballot(checker && !multiplier_ok_at(ku, S, i));
-      const unsigned long long bad_d = __ballot(checker && !multiplier_ok_at(kd, S, i));
-      const unsigned long long mine = 0x7Full << (7 * m);
-      if (checker && (bad & mine)) kb = !(bad_u & mine) ? ku : (!(bad_d & mine) ? kd : -kb);
-    }
-    // Multiplier of block-scale code c: its mantissa's base multiplier (held by lane 7m) scaled
-    // by 2^-exponent; 0 outside 1..126.
-    auto code_multiplier = [&](int c) {
-      const uint32_t vb = __float_as_uint(e4m3_to_float((uint32_t)min(max(c, 1), 126)));
-      const int mc = (int)((vb >> 20) & 7u);
-      const int E = (int)((vb >> 23) & 0xFFu) - 127;
-      const float base = __shfl(kb, 7 * mc, kWave);
-      return (usable && c >= 1 && c <= 126) ? ldexpf(base, -E) : 0.0f;
-    };
-    const int c = tid;
-    const uint32_t th = (c + 1 > 126 || !usable) ? 0xFFFFu : scale_threshold(c + 1, gsd);
-    const float k0 = code_multiplier(c), k1 = code_multiplier(c + 1);
-    t.ent[c] = make_uint4(th, __float_as_uint(k0), __float_as_uint(k1), 0u);
+    const float kb = table_base_multiplier(gsd, usable);
+    t.ent[tid] = table_entry(tid, kb, gsd, usable);
   }
   if (tid == 0) {
     t.gs = gs;
     t.inv6gs = usable ? (float)(1.0 / (6.0 * gsd)) : 0.0f;
   }
   __syncthreads();
+}
+
+// The same tables built by one wave alone (all 64 lanes call it; each writes entries lane and
+// lane + 64), with no barrier: the calling wave may read them at once (its LDS accesses complete
+// in order), other waves only after a barrier that follows this call.
+__device__ inline void build_tables_one_wave(QuantTables &t, float gs) {
+  const int lane = threadIdx.x & 63;
+  const double gsd = (double)gs;
+  const bool usable = gs_usable(gs);
+  const float kb = table_base_multiplier(gsd, usable);
+  t.ent[lane] = table_entry(lane, kb, gsd, usable);
+  t.ent[lane + 64] = table_entry(lane + 64, kb, gsd, usable);
+  if (lane == 0) {
+    t.gs = gs;
+    t.inv6gs = usable ? (float)(1.0 / (6.0 * gsd)) : 0.0f;
+  }
 }
 
 __device__ __forceinline__ float global_scale_from_amax_bits(uint32_t amax_bf16_bits) {

@@ -113,11 +113,13 @@ def test_prequantized_a(nv, m):
     check_gemm(y, y64, what=f"prequantized m={m}")
 
 
-# A single activation row: K <= 4096 takes the decode kernel, which quantizes the bf16
-# activation inside it (the quantized A it writes is checked); K = 8192 a quantize launch and
-# the small-M kernel.
+# A single activation row: K <= 4096 takes the decode kernel, whose first wave quantizes the
+# bf16 activation for the whole workgroup (the quantized A it writes is checked; K = 2064 and
+# 1040 leave the last waves' K slices short or empty); K = 8192 a quantize launch and the
+# small-M kernel.
 @pytest.mark.parametrize("n,k,br", [(1000, 2048, 1), (4112, 4096, 16), (272, 8192, 16),
-                                    (48, 4096, 1)])
+                                    (48, 4096, 1), (528, 2064, 16), (100, 1040, 1),
+                                    (64, 256, 16)])
 def test_single_row_shapes(nv, n, k, br):
     rng = np.random.default_rng(n * 3 + k + br)
     a = W.to_bf16_bits(W.normal_with_outliers(rng, 1, k, 0.01, 20.0))

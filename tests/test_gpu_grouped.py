@@ -66,6 +66,27 @@ def test_small_moe(nv, tokens, hidden, experts, topk, n, br):
     check_gemm(y, y64, what="small moe")
 
 
+@pytest.mark.parametrize("br", [16, 1])
+def test_partial_last_tiles(nv, br):
+    """Groups whose last 128-row tile holds 1 to 128 rows: the grouped kernel multiplies only
+    the 32-row fragments of A that hold rows of the group (1, 2, 3 or 4 of them), and every
+    class, with its boundary row counts, is checked against the oracle."""
+    rng = np.random.default_rng(11 + br)
+    counts = np.array([1, 31, 32, 33, 64, 65, 96, 97, 127, 128, 129, 160, 193, 250, 0, 5])
+    experts, n, k, tokens = len(counts), 272, 512, 700
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    total = int(offsets[-1])
+    row_index = rng.integers(0, tokens, total).astype(np.int32)
+    a = W.to_bf16_bits(rng.standard_normal((tokens, k)))
+    w = W.to_bf16_bits(rng.standard_normal((experts * n, k)) * 0.02)
+    wq = quantize_experts(nv, w, experts, n, br)
+    y = nv.grouped_gemm_w4a4(dev_bf16(a), torch.from_numpy(row_index).cuda(),
+                             torch.from_numpy(offsets).cuda(), wq, n, total)
+    y64 = O.grouped_gemm64(O.quantize_1d(a) + (1,), row_index, offsets,
+                           oracle_experts(w, experts, n, br))
+    check_gemm(y, y64, what=f"partial last tiles br={br}")
+
+
 def test_empty_groups_and_pregrouped_rows(nv):
     rng = np.random.default_rng(9)
     experts, n, k = 6, 64, 256

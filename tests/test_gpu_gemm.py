@@ -129,6 +129,30 @@ def test_single_row_shapes(nv, n, k, br):
     assert torch.equal(y, y_pre)
 
 
+# Decode shapes with A quantized inside the call read A with its row stride: one row by the
+# first wave's loads, 2-16 rows through the LDS staging copy (K = 1040 leaves the last 1 KiB
+# chunk of each staged row partly past the row's end).
+@pytest.mark.parametrize("m,k", [(1, 1040), (6, 1040), (16, 4096), (2, 2064)])
+def test_strided_activation_rows(nv, m, k):
+    rng = np.random.default_rng(m * 31 + k)
+    n, ld = 272, k + 72
+    a_full = W.to_bf16_bits(W.normal_with_outliers(rng, m, ld, 0.01, 20.0))
+    a = a_full[:, :k]
+    w = W.to_bf16_bits(rng.standard_normal((n, k)) * 0.02)
+    wq = nv.quantize_2d(dev_bf16(w))
+    a_dev = dev_bf16(np.ascontiguousarray(a_full))[:, :k]
+    assert a_dev.stride(0) == ld
+    aq = nv.empty_qtensor(m, k, 1)
+    y = nv.gemm_w4a4(a_dev, wq, a_q=aq)
+    oa = O.quantize_1d(np.ascontiguousarray(a)) + (1,)
+    ac, as_, ag = host_q(aq)
+    assert np.float32(ag) == oa[2]
+    assert_codes_equal(ac, oa[0], f"strided A {m}x{k} codes")
+    assert_codes_equal(as_, oa[1], f"strided A {m}x{k} scales")
+    y64 = O.gemm64(oa, O.quantize_2d(w) + (16,))
+    check_gemm(y, y64, what=f"strided A {m}x{k}")
+
+
 def test_identity_weight_closed_form(nv):
     """W = I with 16x16 blocks makes W_hat = 2688 gs_W I: Y must be RN_bf16(A_hat * 2688 gs_W)
     up to the fp32 epilogue (pins transposes, nibble order and scale indexing on the GPU)."""

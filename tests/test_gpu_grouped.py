@@ -87,6 +87,30 @@ def test_partial_last_tiles(nv, br):
     check_gemm(y, y64, what=f"partial last tiles br={br}")
 
 
+@pytest.mark.parametrize("k", [64, 48])
+def test_most_groups_the_library_takes(nv, k):
+    """1024 experts (the largest count the call accepts), most of them empty, a few rows in the
+    others: the device scan of the offsets covers its whole range, in both grouped kernels (K a
+    multiple of 64, and not)."""
+    rng = np.random.default_rng(21 + k)
+    experts, n, tokens = 1024, 16, 96
+    counts = np.zeros(experts, dtype=np.int64)
+    hot = rng.choice(experts, size=40, replace=False)
+    counts[hot] = rng.integers(1, 20, size=40)
+    counts[experts - 1] = 3  # the last group is not empty
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    total = int(offsets[-1])
+    row_index = rng.integers(0, tokens, total).astype(np.int32)
+    a = W.to_bf16_bits(rng.standard_normal((tokens, k)))
+    w = W.to_bf16_bits(rng.standard_normal((experts * n, k)) * 0.02)
+    wq = quantize_experts(nv, w, experts, n)
+    y = nv.grouped_gemm_w4a4(dev_bf16(a), torch.from_numpy(row_index).cuda(),
+                             torch.from_numpy(offsets).cuda(), wq, n, total)
+    y64 = O.grouped_gemm64(O.quantize_1d(a) + (1,), row_index, offsets,
+                           oracle_experts(w, experts, n))
+    check_gemm(y, y64, what=f"1024 groups k={k}")
+
+
 def test_empty_groups_and_pregrouped_rows(nv):
     rng = np.random.default_rng(9)
     experts, n, k = 6, 64, 256

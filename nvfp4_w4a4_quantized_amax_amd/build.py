@@ -42,7 +42,8 @@ def _compile(src, verbose):
 
 PROBES = [("probes/mfma_routes.hip", "probes/mfma_routes"),
           ("probes/hbm_rates.hip", "probes/hbm_rates"),
-          ("probes/launch_cost.hip", "probes/launch_cost")]
+          ("probes/launch_cost.hip", "probes/launch_cost"),
+          ("probes/decode_stream.hip", "probes/decode_stream")]
 
 
 def build_probes(verbose=False):

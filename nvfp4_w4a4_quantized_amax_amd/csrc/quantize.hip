@@ -605,24 +605,29 @@ static DeviceInfo device_info() {
   return cache[dev];
 }
 
-static std::atomic<unsigned long long> g_epoch{0};
+// Per-call barrier epochs.  They start from an unpredictable 48-bit value, so that slots left in
+// a reused workspace by an earlier process never carry a current epoch; the counter is a
+// function-local static, whose one-time initialization is thread-safe, so concurrent first calls
+// cannot see it before it is seeded.
+static unsigned long long initial_epoch() {
+  static int anchor;
+  const unsigned long long seed =
+      (unsigned long long)std::chrono::steady_clock::now().time_since_epoch().count() ^
+      ((unsigned long long)getpid() << 32) ^ (unsigned long long)(uintptr_t)&anchor;
+  // the SplitMix64 finalizer, a published 64-bit mixing function
+  unsigned long long z = seed + 0x9E3779B97F4A7C15ull;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
 
 static unsigned long long next_epoch() {
-  unsigned long long e = g_epoch.fetch_add(1) + 1;
-  if (e == 1) {  // first call in this process: start from an unpredictable 48-bit value
-    // (the seed is mixed with the SplitMix64 finalizer, a published 64-bit mixing function)
-    const unsigned long long seed =
-        (unsigned long long)std::chrono::steady_clock::now().time_since_epoch().count() ^
-        ((unsigned long long)getpid() << 32) ^ (unsigned long long)(uintptr_t)&g_epoch;
-    unsigned long long z = seed + 0x9E3779B97F4A7C15ull;
-    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
-    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
-    z ^= z >> 31;
-    unsigned long long expected = 1;
-    g_epoch.compare_exchange_strong(expected, z | 1ull);
-    e = g_epoch.fetch_add(1) + 1;
-  }
-  return e & 0xFFFFFFFFFFFFull;
+  static std::atomic<unsigned long long> counter{initial_epoch()};
+  unsigned long long e;
+  do {  // epoch 0 would match the zeros of freshly cleared memory
+    e = (counter.fetch_add(1) + 1) & 0xFFFFFFFFFFFFull;
+  } while (e == 0);
+  return e;
 }
 
 hipError_t launch_quantize_persistent(const void *x, int64_t rows, int64_t cols, int64_t ld_x,

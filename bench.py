@@ -15,7 +15,8 @@ Infinity Cache left there by the previous step.
 
 "workloads" adds the other shapes the library serves (decode-, prefill- and MoE-shaped W4A4
 GEMMs, activation quantization inside the call; the weight-only W4A16 form of the decode
-shapes), each timed the same way with its own roofline.
+shapes; the dequantization of the headline activation; the MXFP4 variant and the MSE-observer
+weight quantization), each timed the same way with its own roofline.
 "cpu_baseline" times the CPU oracle (test infrastructure, float64 numpy) on the same headline
 input on the host.
 """
@@ -272,6 +273,24 @@ def extra_workloads(args, torch, np, nv, W, only):
                                            FP16_MFMA_PEAK_TFLOPS, shape=[m, n, k],
                                            note="A quantized beforehand (the product kernel)")
         del As, Ws, Ys, aqs
+
+    if not only or "dequantize" in only:
+        # Reconstruction of the quantized 8192 x 8192 activation (row a6), bf16 and fp32 out,
+        # over 4 rotating inputs and outputs (4 x (36 MiB + 128 or 256 MiB), past the Infinity
+        # Cache, so that neither side is served from it).
+        q0 = nv.quantize_1d(dev_bf16(torch, np, W.activation(seed=1, rows=8192, cols=8192)["x"]))
+        m = n = 8192
+        qs = [q0] + [nv.QTensor(q0.codes.clone(), q0.scales.clone(), q0.global_scale.clone(),
+                                m, n, 1) for _ in range(3)]
+        inb = m * n // 2 + m * n // 16 + 4
+        for dtype, name, esz in ((torch.bfloat16, "dequantize_bf16", 2),
+                                 (torch.float32, "dequantize_f32", 4)):
+            ys = [torch.empty((m, n), dtype=dtype, device="cuda") for _ in range(4)]
+            ms, st = timed(lambda i: nv.dequantize(qs[i % 4], dtype, out=ys[i % 4]), steps, warm,
+                           torch)
+            out[name] = _rec(ms, st, inb + m * n * esz, shape=[m, n])
+            del ys
+        del qs, q0
 
     if not only or "moe" in only:
         d = W.moe()

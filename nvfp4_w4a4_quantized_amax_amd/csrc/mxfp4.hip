@@ -58,46 +58,67 @@ __global__ __launch_bounds__(256) void k_mx_quantize(const uint16_t *__restrict_
 }
 
 // ---------------------------------------------------------------------------------------------
-// Dequantize: one thread = 8 values (one code word); value = code value * 2^(byte - 127).
+// Dequantize: value = code value * 2^(byte - 127).  bf16 output: one thread = 8 values (one code
+// word, 16 bytes out).  fp32 output: one thread = 4 values (16 bits of codes, 16 bytes out), so
+// that one store instruction of a wave covers 1 KiB of contiguous output; with 8 values per
+// thread the two 16-byte stores of a lane interleave at a 32-byte stride, which wrote at about a
+// third of the HBM rate.
 // ---------------------------------------------------------------------------------------------
-template <bool OUT_F32>
-__global__ __launch_bounds__(256) void k_mx_dequantize(const uint8_t *__restrict__ codes,
-                                                       int64_t ld_codes,
-                                                       const uint8_t *__restrict__ scales,
-                                                       int64_t ld_scales, uint32_t n_chunks,
-                                                       FastDiv cpr, void *__restrict__ y,
-                                                       int64_t ld_y) {
+__device__ __forceinline__ float mx_scale_value(uint32_t b) {
+  // 2^(b - 127) for b in [0, 254]: b = 0 is the fp32 subnormal 2^-127.
+  return b ? __uint_as_float(b << 23) : 0x1p-127f;
+}
+
+__global__ __launch_bounds__(256) void k_mx_dequantize_bf16(const uint8_t *__restrict__ codes,
+                                                            int64_t ld_codes,
+                                                            const uint8_t *__restrict__ scales,
+                                                            int64_t ld_scales, uint32_t n_chunks,
+                                                            FastDiv cpr,
+                                                            uint16_t *__restrict__ y,
+                                                            int64_t ld_y) {
   const uint32_t stride = gridDim.x * blockDim.x;
   for (uint32_t u = blockIdx.x * blockDim.x + threadIdx.x; u < n_chunks; u += stride) {
     const uint32_t r = fdiv(u, cpr), c = u - r * cpr.d;
     const uint32_t q = *(const uint32_t *)(codes + (int64_t)r * ld_codes + (int64_t)c * 4);
-    const uint32_t b = scales[(int64_t)r * ld_scales + (c >> 2)];
-    // 2^(b - 127) for b in [0, 254]: b = 0 is the fp32 subnormal 2^-127.
-    const float s = b ? __uint_as_float(b << 23) : 0x1p-127f;
+    const float s = mx_scale_value(scales[(int64_t)r * ld_scales + (c >> 2)]);
     const floatx2_t f[4] = {__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, 1.0f, 0),
                             __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, 1.0f, 1),
                             __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, 1.0f, 2),
                             __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, 1.0f, 3)};
-    float v[8];
+    uint32_t h[8];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      v[2 * j] = f[j][0] * s;
-      v[2 * j + 1] = f[j][1] * s;
+      h[2 * j] = f32_to_bf16_rne(f[j][0] * s);
+      h[2 * j + 1] = f32_to_bf16_rne(f[j][1] * s);
     }
-    if (OUT_F32) {
-      float *p = (float *)y + (int64_t)r * ld_y + (int64_t)c * 8;
-      ntstore16(p, make_uint4(__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
-                              __float_as_uint(v[3])));
-      ntstore16(p + 4, make_uint4(__float_as_uint(v[4]), __float_as_uint(v[5]),
-                                  __float_as_uint(v[6]), __float_as_uint(v[7])));
-    } else {
-      uint4 o;
-      o.x = f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16);
-      o.y = f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16);
-      o.z = f32_to_bf16_rne(v[4]) | (f32_to_bf16_rne(v[5]) << 16);
-      o.w = f32_to_bf16_rne(v[6]) | (f32_to_bf16_rne(v[7]) << 16);
-      ntstore16((uint16_t *)y + (int64_t)r * ld_y + (int64_t)c * 8, o);
-    }
+    ntstore16(y + (int64_t)r * ld_y + (int64_t)c * 8,
+              make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
+                         h[6] | (h[7] << 16)));
+  }
+}
+
+// n_quads = rows * cols / 4 < 2^32; the loop counter is 64-bit so that the last stride step
+// cannot wrap, and the quotient's sum is taken in 64 bits for the same reason.
+__global__ __launch_bounds__(256) void k_mx_dequantize_f32(const uint8_t *__restrict__ codes,
+                                                           int64_t ld_codes,
+                                                           const uint8_t *__restrict__ scales,
+                                                           int64_t ld_scales, uint32_t n_quads,
+                                                           FastDiv qpr, float *__restrict__ y,
+                                                           int64_t ld_y) {
+  const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+  for (uint64_t u64 = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; u64 < n_quads;
+       u64 += stride) {
+    const uint32_t u = (uint32_t)u64;
+    // fdiv's 32-bit sum holds below 2^31 only; u can reach 2^32 here, so sum in 64 bits.
+    const uint32_t r = (uint32_t)(((uint64_t)__umulhi(u, qpr.mul) + u) >> qpr.shift);
+    const uint32_t c = u - r * qpr.d;
+    const uint32_t q = *(const uint16_t *)(codes + (int64_t)r * ld_codes + (int64_t)c * 2);
+    const float s = mx_scale_value(scales[(int64_t)r * ld_scales + (c >> 3)]);
+    const floatx2_t f0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, 1.0f, 0);
+    const floatx2_t f1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, 1.0f, 1);
+    ntstore16(y + (int64_t)r * ld_y + (int64_t)c * 4,
+              make_uint4(__float_as_uint(f0[0] * s), __float_as_uint(f0[1] * s),
+                         __float_as_uint(f1[0] * s), __float_as_uint(f1[1] * s)));
   }
 }
 
@@ -770,13 +791,16 @@ hipError_t launch_mx_quantize(const void *x, int64_t rows, int64_t cols, int64_t
 hipError_t launch_mx_dequantize(const uint8_t *codes, int64_t ld_codes, const uint8_t *scales,
                                 int64_t ld_scales, int64_t rows, int64_t cols, void *y,
                                 int64_t ld_y, int out_f32, hipStream_t stream) {
-  const uint32_t cpr = (uint32_t)(cols / 8), n = (uint32_t)(rows * (cols / 8));
-  if (out_f32)
-    hipLaunchKernelGGL(k_mx_dequantize<true>, dim3(mx_grid(n)), dim3(256), 0, stream, codes,
-                       ld_codes, scales, ld_scales, n, mx_fastdiv(cpr), y, ld_y);
-  else
-    hipLaunchKernelGGL(k_mx_dequantize<false>, dim3(mx_grid(n)), dim3(256), 0, stream, codes,
-                       ld_codes, scales, ld_scales, n, mx_fastdiv(cpr), y, ld_y);
+  // The caller keeps rows * cols / 8 below 2^31, so rows * cols / 4 fits 32 bits.
+  if (out_f32) {
+    const uint32_t qpr = (uint32_t)(cols / 4), n = (uint32_t)(rows * (cols / 4));
+    hipLaunchKernelGGL(k_mx_dequantize_f32, dim3(mx_grid(n)), dim3(256), 0, stream, codes,
+                       ld_codes, scales, ld_scales, n, mx_fastdiv(qpr), (float *)y, ld_y);
+  } else {
+    const uint32_t cpr = (uint32_t)(cols / 8), n = (uint32_t)(rows * (cols / 8));
+    hipLaunchKernelGGL(k_mx_dequantize_bf16, dim3(mx_grid(n)), dim3(256), 0, stream, codes,
+                       ld_codes, scales, ld_scales, n, mx_fastdiv(cpr), (uint16_t *)y, ld_y);
+  }
   return hipGetLastError();
 }
 

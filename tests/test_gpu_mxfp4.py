@@ -109,6 +109,28 @@ def test_dequantize(nv, dtype):
         assert np.array_equal(y.cpu().view(torch.int16).numpy().view(np.uint16), want)
 
 
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_dequantize_ragged_strided(nv, dtype):
+    """A shape that spans many workgroups with a ragged row count, written into rows of a wider
+    matrix (ld_y = cols + 40): the view bit for bit against the oracle, the padding untouched."""
+    rng = np.random.default_rng(61)
+    rows, cols = 257, 1056
+    x = W.to_bf16_bits(rng.standard_normal((rows, cols)) * np.exp(rng.uniform(-30, 30, (rows, 1))))
+    q, oq = check_quantize(nv, x, "strided dequantize input")
+    big = torch.full((rows, cols + 40), -3.0, dtype=dtype, device="cuda")
+    nv.mxfp4_dequantize(q, dtype, out=big[:, :cols])
+    torch.cuda.synchronize()
+    host = big.cpu()
+    assert bool((host[:, cols:] == -3.0).all()), "padding columns written"
+    if dtype == torch.float32:
+        want = MX.dequantize_mx(*oq, out="f32")
+        assert np.array_equal(host[:, :cols].numpy().view(np.uint32), want.view(np.uint32))
+    else:
+        want = MX.dequantize_mx(*oq, out="bf16")
+        got = host[:, :cols].contiguous().view(torch.int16).numpy().view(np.uint16)
+        assert np.array_equal(got, want)
+
+
 # M > 128 takes a pipelined kernel: the wide-window one when K is a multiple of 512 (one and
 # three window pairs appear; 4100 x 4200 has more tiles than workgroups, so workgroups carry the
 # pipeline from one ragged tile into the next), else the 64-wide one (one window, an odd window

@@ -181,6 +181,28 @@ def test_dequantize_ragged(nv, rows, cols, br):
     assert np.array_equal(b16, O.dequantize(c, s, g, br, out="bf16"))
 
 
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("rows,cols,br", [(257, 1040, 1), (48, 272, 16)])
+def test_dequantize_strided_output(nv, rows, cols, br, dtype):
+    """Dequantize into rows of a wider matrix (ld_y = cols + 24): every value of the view
+    against the oracle, bit for bit, and the padding columns left as they were."""
+    rng = np.random.default_rng(rows + 7 * cols)
+    x = W.to_bf16_bits(rng.standard_normal((rows, cols)) * np.exp(rng.uniform(-4, 4, (rows, 1))))
+    q = (nv.quantize_2d if br == 16 else nv.quantize_1d)(dev_bf16(x))
+    c, s, g = host_q(q)
+    big = torch.full((rows, cols + 24), -7.0, dtype=dtype, device="cuda")
+    nv.dequantize(q, dtype, out=big[:, :cols])
+    torch.cuda.synchronize()
+    host = big.cpu()
+    assert bool((host[:, cols:] == -7.0).all()), "padding columns written"
+    if dtype == torch.float32:
+        got = host[:, :cols].numpy().view(np.uint32)
+        assert np.array_equal(got, O.dequantize(c, s, g, br, out="f32").view(np.uint32))
+    else:
+        got = host[:, :cols].contiguous().view(torch.int16).numpy().view(np.uint16)
+        assert np.array_equal(got, O.dequantize(c, s, g, br, out="bf16"))
+
+
 def test_empty_tensors(nv):
     """Zero-row inputs through the binding: every call succeeds and leaves its outputs alone."""
     x = torch.empty((0, 64), dtype=torch.bfloat16, device="cuda")

@@ -15,6 +15,7 @@
 // straight into registers and feeds them to four K=16 MFMAs; A and W use the same mapping.
 
 #include <mutex>
+#include <type_traits>
 
 #include "nvfp4_device.hpp"
 #include "gemm_common.hpp"
@@ -327,6 +328,25 @@ __device__ __forceinline__ void read_stage_frags(const Stage &S, int wave, int w
   }
 }
 
+// read_stage_frags for the first NF A fragments only (the tile's rows past them are padding).
+template <bool W2D, int NF, class Stage>
+__device__ __forceinline__ void read_stage_frags_nf(const Stage &S, int wave, int wn, int lr,
+                                                    int kh, Frags<4, 4> &fr) {
+  const int ra = lr, rw = wn * 128 + lr;
+#pragma unroll
+  for (int f = 0; f < NF; ++f) {
+    fr.a[f] = *(const uint4 *)(S.a + code_offset(ra + f * 32, kh));
+    fr.sa[f] = *(const uint16_t *)(S.as + (ra + f * 32) * 4 + kh * 2);
+  }
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    fr.w[g] = *(const uint4 *)(S.w + code_offset(rw + g * 32, kh));
+    fr.sw[g] = W2D ? *(const uint16_t *)(S.ws + wave * 256 + (wn * 8 + g * 2 + (lr >> 4)) * 4 +
+                                         kh * 2)
+                   : *(const uint16_t *)(S.ws + (rw + g * 32) * 4 + kh * 2);
+  }
+}
+
 // Decoded operands of one K=16 step: 4 A fragments then 4 W fragments (8 fp16 each).
 struct StepOps {
   half8_t v[8];
@@ -392,6 +412,70 @@ __device__ __forceinline__ void end_step(const StepOps &d) {
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int i = 0; i < 8; ++i) asm volatile("" ::"v"(d.v[i]));
+}
+
+// The same steps for a tile whose first NF 32-row A fragments hold rows (NF < 4: the last
+// tile of a group); the fragments past them are neither read, decoded nor multiplied.  A step
+// then has 4 NF MFMAs and (NF + 4) decodes of 8 VALU operations each.
+template <int NF>
+__device__ __forceinline__ void decode_step_nf(const Frags<4, 4> &fr, const half2_t (&sa)[4],
+                                               const half2_t (&sw)[4], int kk, StepOps &d) {
+#pragma unroll
+  for (int f = 0; f < NF; ++f)
+    d.v[f] = decode8_f16(word(fr.a[f], kk), kk < 2 ? splat_lo(sa[f]) : splat_hi(sa[f]));
+#pragma unroll
+  for (int g = 0; g < 4; ++g)
+    d.v[4 + g] = decode8_f16(word(fr.w[g], kk), kk < 2 ? splat_lo(sw[g]) : splat_hi(sw[g]));
+}
+
+template <int NF>
+__device__ __forceinline__ void mfma_step_nf(const StepOps &d, floatx16_t (&acc)[NF][4]) {
+#pragma unroll
+  for (int f = 0; f < NF; ++f)
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+      acc[f][g] = __builtin_amdgcn_mfma_f32_32x32x16_f16(d.v[f], d.v[4 + g], acc[f][g], 0, 0, 0);
+}
+
+template <int NF>
+__device__ __forceinline__ void window_scales_nf(const Frags<4, 4> &fr, half2_t (&sa)[4],
+                                                 half2_t (&sw)[4]) {
+#pragma unroll
+  for (int f = 0; f < NF; ++f) sa[f] = scales_f16x2(fr.sa[f]);
+#pragma unroll
+  for (int g = 0; g < 4; ++g) sw[g] = scales_f16x2(fr.sw[g]);
+}
+
+// Interleave for 4 NF MFMAs: after each, its share of the next step's decode VALU and of up
+// to two kinds of memory instructions: one per MFMA from the first while they are no more than
+// the MFMAs (the full tile's pattern), else spread evenly.
+template <int NF, int MEM_MASK = 0, int NMEM = 0, int MEM_MASK2 = 0, int NMEM2 = 0>
+__device__ __forceinline__ void interleave_step_nf() {
+  constexpr int kSlots = 4 * NF;
+  constexpr int kValu = ((NF + 4) * 8 + kSlots - 1) / kSlots;
+  constexpr int kPer1 = (NMEM + kSlots - 1) / kSlots, kPer2 = (NMEM2 + kSlots - 1) / kSlots;
+#pragma unroll
+  for (int i = 0; i < kSlots; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+#pragma unroll
+    for (int j = 0; j < kPer1; ++j)
+      if (NMEM <= kSlots ? i < NMEM : j < (i + 1) * NMEM / kSlots - i * NMEM / kSlots)
+        __builtin_amdgcn_sched_group_barrier(MEM_MASK, 1, 0);
+#pragma unroll
+    for (int j = 0; j < kPer2; ++j)
+      if (NMEM2 <= kSlots ? i < NMEM2 : j < (i + 1) * NMEM2 / kSlots - i * NMEM2 / kSlots)
+        __builtin_amdgcn_sched_group_barrier(MEM_MASK2, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, kValu, 0);
+  }
+}
+
+template <int NF>
+__device__ __forceinline__ void end_step_nf(const StepOps &d) {
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 0; i < NF; ++i) asm volatile("" ::"v"(d.v[i]));
+#pragma unroll
+  for (int i = 4; i < 8; ++i) asm volatile("" ::"v"(d.v[i]));
 }
 
 template <bool W2D>
@@ -657,6 +741,90 @@ struct WindowRegsG {
   uint32_t as, ws0, ws1;
 };
 
+// One tile of the grouped kernel whose first NF 32-row A fragments hold rows of the group
+// (NF < 4 only for a group's last tile): the fragments past them would be padding and are
+// neither read from LDS, decoded nor multiplied.  (A separate function rather than a lambda in
+// the kernel: inside a generic lambda the scheduler bunched the LDS reads that the interleave
+// hints spread over the MFMAs.)
+template <bool W2D, int NF, class Load, class Store>
+__device__ __forceinline__ void grouped_lds_tile(const GroupedArgs &p, LdsStageG (&st)[2],
+                                                 const Load &load, const Store &store, int wave,
+                                                 int wn, int lr, int kh, int64_t nwin, int e,
+                                                 int64_t m_tile, int64_t n_tile, int r_end) {
+    floatx16_t acc[NF][4];
+#pragma unroll
+    for (int f = 0; f < NF; ++f)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) acc[f][g] = floatx16_t{};
+
+    __syncthreads();  // the previous tile's last fragment reads are done with both stages
+    WindowRegsG r;
+    load(0, r);
+    store(r, st[0]);
+    load(min((int64_t)1, nwin - 1), r);
+    lds_barrier();
+    Frags<4, 4> cur, nxt;
+    read_stage_frags_nf<W2D, NF>(st[0], wave, wn, lr, kh, cur);
+    half2_t sa[4], sw[4];
+    window_scales_nf<NF>(cur, sa, sw);
+    StepOps ev, od;
+    decode_step_nf<NF>(cur, sa, sw, 0, ev);
+    for (int64_t w = 0; w + 1 < nwin; ++w) {
+      store(r, st[(w + 1) & 1]);
+      load(min(w + 2, nwin - 1), r);
+      decode_step_nf<NF>(cur, sa, sw, 1, od);
+      mfma_step_nf<NF>(ev, acc);
+      interleave_step_nf<NF, 0x200, 9, 0x020, 9>();
+      end_step_nf<NF>(ev);
+      lds_barrier();
+      read_stage_frags_nf<W2D, NF>(st[(w + 1) & 1], wave, wn, lr, kh, nxt);
+      decode_step_nf<NF>(cur, sa, sw, 2, ev);
+      mfma_step_nf<NF>(od, acc);
+      interleave_step_nf<NF, 0x100, 2 * NF + 8>();
+      end_step_nf<NF>(od);
+      decode_step_nf<NF>(cur, sa, sw, 3, od);
+      mfma_step_nf<NF>(ev, acc);
+      interleave_step_nf<NF>();
+      end_step_nf<NF>(ev);
+      window_scales_nf<NF>(nxt, sa, sw);
+      decode_step_nf<NF>(nxt, sa, sw, 0, ev);
+      mfma_step_nf<NF>(od, acc);
+      interleave_step_nf<NF>();
+      end_step_nf<NF>(od);
+      cur = nxt;
+    }
+    decode_step_nf<NF>(cur, sa, sw, 1, od);
+    mfma_step_nf<NF>(ev, acc);
+    interleave_step_nf<NF>();
+    end_step_nf<NF>(ev);
+    decode_step_nf<NF>(cur, sa, sw, 2, ev);
+    mfma_step_nf<NF>(od, acc);
+    interleave_step_nf<NF>();
+    end_step_nf<NF>(od);
+    decode_step_nf<NF>(cur, sa, sw, 3, od);
+    mfma_step_nf<NF>(ev, acc);
+    interleave_step_nf<NF>();
+    end_step_nf<NF>(ev);
+    mfma_step_nf<NF>(od, acc);
+
+    const float alpha = (*p.a.gs) * p.w.gs[e];
+    const int64_t n0 = n_tile + wn * 128;
+#pragma unroll
+    for (int f = 0; f < NF; ++f)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int64_t col = n0 + g * 32 + lr;
+#pragma unroll
+        for (int r2 = 0; r2 < 16; r2 += 2) {  // rows r2 and r2 + 1 are adjacent
+          const int64_t row = m_tile + f * 32 + 8 * (r2 >> 2) + 4 * kh + (r2 & 3);
+          const uint32_t pk = bf16x2_rne(acc[f][g][r2] * alpha, acc[f][g][r2 + 1] * alpha);
+          if (row < r_end && col < p.n) ntstore_u16(p.y + row * p.ld_y + col, pk);
+          if (row + 1 < r_end && col < p.n)
+            ntstore_u16(p.y + (row + 1) * p.ld_y + col, pk >> 16);
+        }
+      }
+}
+
 template <bool W2D>
 __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_gemm_grouped_lds(GroupedArgs p) {
   constexpr int BM = 128, BN = 256, NT = 128;
@@ -768,77 +936,15 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       if (!W2D) *(uint32_t *)(S.ws + (NT + tid) * 4) = r.ws1;
     };
 
-    floatx16_t acc[4][4];
-#pragma unroll
-    for (int f = 0; f < 4; ++f)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) acc[f][g] = floatx16_t{};
-
-    __syncthreads();  // the previous tile's last fragment reads are done with both stages
-    WindowRegsG r;
-    load(0, r);
-    store(r, st[0]);
-    load(min((int64_t)1, nwin - 1), r);
-    lds_barrier();
-    Frags<4, 4> cur, nxt;
-    read_stage_frags<W2D>(st[0], wave, 0, wn, lr, kh, cur);
-    half2_t sa[4], sw[4];
-    window_scales(cur, sa, sw);
-    StepOps ev, od;
-    decode_step(cur, sa, sw, 0, ev);
-    for (int64_t w = 0; w + 1 < nwin; ++w) {
-      store(r, st[(w + 1) & 1]);
-      load(min(w + 2, nwin - 1), r);
-      decode_step(cur, sa, sw, 1, od);
-      mfma_step(ev, acc);
-      interleave_step_mem<0x200, 9, 0x020, 9>();
-      end_step(ev);
-      lds_barrier();
-      read_stage_frags<W2D>(st[(w + 1) & 1], wave, 0, wn, lr, kh, nxt);
-      decode_step(cur, sa, sw, 2, ev);
-      mfma_step(od, acc);
-      interleave_step_mem<0x100, 16>();
-      end_step(od);
-      decode_step(cur, sa, sw, 3, od);
-      mfma_step(ev, acc);
-      interleave_step();
-      end_step(ev);
-      window_scales(nxt, sa, sw);
-      decode_step(nxt, sa, sw, 0, ev);
-      mfma_step(od, acc);
-      interleave_step();
-      end_step(od);
-      cur = nxt;
-    }
-    decode_step(cur, sa, sw, 1, od);
-    mfma_step(ev, acc);
-    interleave_step();
-    end_step(ev);
-    decode_step(cur, sa, sw, 2, ev);
-    mfma_step(od, acc);
-    interleave_step();
-    end_step(od);
-    decode_step(cur, sa, sw, 3, od);
-    mfma_step(ev, acc);
-    interleave_step();
-    end_step(ev);
-    mfma_step(od, acc);
-
-    const float alpha = (*p.a.gs) * p.w.gs[e];
-    const int64_t n0 = n_tile + wn * 128;
-#pragma unroll
-    for (int f = 0; f < 4; ++f)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int64_t col = n0 + g * 32 + lr;
-#pragma unroll
-        for (int r2 = 0; r2 < 16; r2 += 2) {  // rows r2 and r2 + 1 are adjacent
-          const int64_t row = m_tile + f * 32 + 8 * (r2 >> 2) + 4 * kh + (r2 & 3);
-          const uint32_t pk = bf16x2_rne(acc[f][g][r2] * alpha, acc[f][g][r2 + 1] * alpha);
-          if (row < r_end && col < p.n) ntstore_u16(p.y + row * p.ld_y + col, pk);
-          if (row + 1 < r_end && col < p.n) ntstore_u16(p.y + (row + 1) * p.ld_y + col, pk >> 16);
-        }
-      }
+    const int nf = (int)((min((int64_t)BM, (int64_t)r_end - m_tile) + 31) / 32);  // 1..4
+    if (nf >= 4)
+      grouped_lds_tile<W2D, 4>(p, st, load, store, wave, wn, lr, kh, nwin, e, m_tile, n_tile, r_end);
+    else if (nf == 3)
+      grouped_lds_tile<W2D, 3>(p, st, load, store, wave, wn, lr, kh, nwin, e, m_tile, n_tile, r_end);
+    else if (nf == 2)
+      grouped_lds_tile<W2D, 2>(p, st, load, store, wave, wn, lr, kh, nwin, e, m_tile, n_tile, r_end);
+    else
+      grouped_lds_tile<W2D, 1>(p, st, load, store, wave, wn, lr, kh, nwin, e, m_tile, n_tile, r_end);
   }
 }
 

@@ -963,6 +963,11 @@ struct SmallMArgs {
   uint16_t *y;
   int64_t ld_y;
   int scale_pairs;  // both scale arrays 2-byte aligned with even row strides
+  // Decode kernels, full windows, W with 16x16 tile scales, every wave holding its whole
+  // share of windows, scale rows 4-byte aligned: a wave's scale bytes of a band (the same for
+  // all its lanes) come in one scalar load (the launcher then takes the kernels' SS form,
+  // where nothing touches LDS before the band loop).
+  int scalar_scales;
   // Decode kernel with the activation quantization fused in: bf16 A (m x k, row stride ld_a),
   // and where workgroup 0 writes the quantized A (each pointer may be NULL: not written; the
   // row strides are a.ld_codes / a.ld_scales).
@@ -1079,7 +1084,18 @@ struct DecodeW {
   // Two scale bytes per window (the lane's two 16-value blocks), kept 16-bit so that no
   // widening of a loaded value is placed ahead of its use.
   uint16_t s[WIN];
+  // The SS form: the wave's 8 WIN scale bytes of the band, as loaded by one scalar load
+  // (uniform, so they stay in scalar registers); lane group q's pair is picked at use.
+  uint32_t sd[2 * WIN];
 };
+
+// Scale pair of window u for lane group q (bits 0-15).
+template <bool SS, int WIN>
+__device__ __forceinline__ uint32_t scale_pair(const DecodeW<WIN> &w, int u, int q) {
+  if (!SS) return w.s[u];
+  const uint32_t dw = (q & 2) ? w.sd[2 * u + 1] : w.sd[2 * u];
+  return dw >> ((q & 1) * 16);
+}
 
 // Buffer resources over W's codes and scales (raw, byte-addressed, sized to the data).
 struct WBufs {
@@ -1096,7 +1112,7 @@ __device__ __forceinline__ WBufs make_wbufs(const SmallMArgs &p) {
   return b;
 }
 
-template <bool W2D, bool FULL, int WIN>
+template <bool W2D, bool FULL, int WIN, bool SS = false>
 __device__ __forceinline__ void load_decode_w(const SmallMArgs &p, const WBufs &buf, int64_t band,
                                               int64_t nbands, int i16, int q, int64_t win0,
                                               int nw, DecodeW<WIN> &r) {
@@ -1108,6 +1124,33 @@ __device__ __forceinline__ void load_decode_w(const SmallMArgs &p, const WBufs &
     uint32_t rs = (uint32_t)(W2D ? band : row) * (uint32_t)p.w.ld_scales;
     asm volatile("" : "+v"(rc), "+v"(rs));
     const uint32_t cb = rc + q * 16, sb = rs + q * 2;
+    if (SS) {
+      // The wave's 8 WIN scale bytes of the band (bands past the last read the last band's,
+      // whose codes load as zeros and whose outputs are never stored): one scalar load; lane
+      // group q takes the two bytes of its blocks in each window at use (scale_pair).
+      typedef __attribute__((address_space(4))) const u32x4_t cu32x4;
+      typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+      typedef __attribute__((address_space(4))) const u32x2 cu32x2;
+      const uint32_t off = __builtin_amdgcn_readfirstlane(
+          (uint32_t)(min(band, nbands - 1) * p.w.ld_scales + win0 * 8));
+      const uint8_t *sp = p.w.scales + off;
+      if (WIN == 2) {
+        const u32x4_t v = *(cu32x4 *)(uintptr_t)sp;
+        r.sd[0] = v[0];
+        r.sd[1] = v[1];
+        r.sd[2 * WIN - 2] = v[2];
+        r.sd[2 * WIN - 1] = v[3];
+      } else {
+        const u32x2 v = *(cu32x2 *)(uintptr_t)sp;
+        r.sd[0] = v[0];
+        r.sd[1] = v[1];
+      }
+#pragma unroll
+      for (int u = 0; u < WIN; ++u)
+        r.v[u] = __builtin_amdgcn_raw_buffer_load_b128(
+            buf.codes, (int)(valid ? cb + (uint32_t)(win0 + u) * 64 : kBufOutOfRange), 0, 0);
+      return;
+    }
 #pragma unroll
     for (int u = 0; u < WIN; ++u) {
       const bool in = valid && u < nw;
@@ -1142,13 +1185,13 @@ __device__ __forceinline__ void load_decode_w(const SmallMArgs &p, const WBufs &
 }
 
 // Issues the loads of the workgroup's first dec_depth bands.
-template <bool W2D, bool FULL, int WIN, int D>
+template <bool W2D, bool FULL, int WIN, bool SS, int D>
 __device__ __forceinline__ void decode_ring_start(const SmallMArgs &p, const WBufs &buf,
                                                   int64_t nbands, int i16, int q, int64_t win0,
                                                   int nw, DecodeW<WIN> (&ring)[D]) {
 #pragma unroll
   for (int j = 0; j < D; ++j)
-    load_decode_w<W2D, FULL, WIN>(p, buf, blockIdx.x + (int64_t)j * gridDim.x, nbands, i16, q,
+    load_decode_w<W2D, FULL, WIN, SS>(p, buf, blockIdx.x + (int64_t)j * gridDim.x, nbands, i16, q,
                                   win0, nw, ring[j]);
   // Work on A that follows must not move above these loads (it would wait for A first).
   __builtin_amdgcn_sched_barrier(0);
@@ -1163,7 +1206,7 @@ __device__ __forceinline__ void decode_ring_start(const SmallMArgs &p, const WBu
 // the last band they load nothing in the FULL form); the last, partial round only drains.  The
 // scheduler may interleave the W decode of one band with the MFMAs of another; that overlap
 // measured faster than keeping each band's waits precise with scheduling barriers.
-template <bool W2D, bool FULL, int WIN, int D, class Mul>
+template <bool W2D, bool FULL, int WIN, bool SS, int D, class Mul>
 __device__ __forceinline__ void decode_band_loop(const SmallMArgs &p, const WBufs &buf,
                                                  int64_t nbands, int lane, int wave,
                                                  int64_t win0, int nw, float alpha,
@@ -1184,7 +1227,9 @@ __device__ __forceinline__ void decode_band_loop(const SmallMArgs &p, const WBuf
 #pragma unroll
       for (int w2 = 0; w2 < kDecWaves; ++w2) t += ((const float *)&s_red[fj][w2][fl])[fc];
       const int64_t n = band * 16 + 4 * (fl >> 4) + fc;
-      if (n < p.n) ntstore_u16(p.y + (int64_t)frow * p.ld_y + n, f32_to_bf16_rne(t * alpha));
+      // A plain store: the end of the kernel waits for it, and a write-back one through L2
+      // completes sooner than a streaming one (measured 0.1-0.3 us per call).
+      if (n < p.n) p.y[(int64_t)frow * p.ld_y + n] = (uint16_t)f32_to_bf16_rne(t * alpha);
     }
     __syncthreads();
   };
@@ -1194,7 +1239,8 @@ __device__ __forceinline__ void decode_band_loop(const SmallMArgs &p, const WBuf
 #pragma unroll
     for (int j = 0; j < D; ++j) {
       acc[j] = mul(ring[j]);
-      load_decode_w<W2D, FULL, WIN>(p, buf, base + (j + D) * g, nbands, i16, q, win0, nw, ring[j]);
+      load_decode_w<W2D, FULL, WIN, SS>(p, buf, base + (j + D) * g, nbands, i16, q, win0, nw,
+                                        ring[j]);
     }
     finish(acc, base);
   }
@@ -1214,8 +1260,9 @@ __device__ __forceinline__ void decode_band_loop(const SmallMArgs &p, const WBuf
 // meet it at one barrier.  Otherwise each wave loads and encodes its own slice, and the rings
 // start after the amax barrier (a W ring issued before it delays the activation loads of the
 // waves that start later).
-template <bool W2D, bool FUSED, bool FULL, int WIN, bool LEAD = false>
+template <bool W2D, bool FUSED, bool FULL, int WIN, bool LEAD = false, bool SS = false>
 __global__ __launch_bounds__(kDecWaves * 64) void k_gemm_decode(SmallMArgs p) {
+  static_assert(!SS || (W2D && FULL), "one scalar scale load per band needs 2D scales, full windows");
   static_assert(!LEAD || FUSED, "the lead-wave form quantizes A");
   constexpr int D = dec_depth(WIN, FULL && (!FUSED || LEAD));
   __shared__ floatx4_t s_red[D][kDecWaves][kWave];
@@ -1259,7 +1306,7 @@ __global__ __launch_bounds__(kDecWaves * 64) void k_gemm_decode(SmallMArgs p) {
           xa[j][0] = *(const uint4 *)src;
           xa[j][1] = *(const uint4 *)(src + 8);
         }
-        decode_ring_start<W2D, FULL, WIN>(p, buf, nbands, i16, q, win0, nw, ring);
+        decode_ring_start<W2D, FULL, WIN, SS>(p, buf, nbands, i16, q, win0, nw, ring);
         uint32_t mx = 0;
 #pragma unroll
         for (int j = 0; j < kLB; ++j) mx = max(mx, absmax16(xa[j][0], xa[j][1]));
@@ -1286,7 +1333,7 @@ __global__ __launch_bounds__(kDecWaves * 64) void k_gemm_decode(SmallMArgs p) {
           }
         }
       } else {
-        decode_ring_start<W2D, FULL, WIN>(p, buf, nbands, i16, q, win0, nw, ring);
+        decode_ring_start<W2D, FULL, WIN, SS>(p, buf, nbands, i16, q, win0, nw, ring);
       }
       __syncthreads();
       gs_a = tab.gs;
@@ -1320,7 +1367,7 @@ __global__ __launch_bounds__(kDecWaves * 64) void k_gemm_decode(SmallMArgs p) {
       mx = wave_max_u32(mx);
       if (lane == 0) red[wave] = mx;
       __syncthreads();
-      decode_ring_start<W2D, FULL, WIN>(p, buf, nbands, i16, q, win0, nw, ring);
+      decode_ring_start<W2D, FULL, WIN, SS>(p, buf, nbands, i16, q, win0, nw, ring);
       mx = red[0];
 #pragma unroll
       for (int w2 = 1; w2 < kDecWaves; ++w2) mx = max(mx, red[w2]);
@@ -1387,7 +1434,7 @@ __global__ __launch_bounds__(kDecWaves * 64) void k_gemm_decode(SmallMArgs p) {
                 (remb > 1 ? (uint32_t)asrow[win * 8 + 1] << 8 : 0u);
       }
     }
-    decode_ring_start<W2D, FULL, WIN>(p, buf, nbands, i16, q, win0, nw, ring);
+    decode_ring_start<W2D, FULL, WIN, SS>(p, buf, nbands, i16, q, win0, nw, ring);
 #pragma unroll
     for (int u = 0; u < WIN; ++u) {
       const half2_t sp = scales_f16x2(as[u]);
@@ -1398,13 +1445,13 @@ __global__ __launch_bounds__(kDecWaves * 64) void k_gemm_decode(SmallMArgs p) {
   }
 
   const float alpha = (FUSED ? gs_a : gs_a_in) * gs_w;
-  decode_band_loop<W2D, FULL, WIN>(
+  decode_band_loop<W2D, FULL, WIN, SS>(
       p, buf, nbands, lane, wave, win0, nw, alpha, ring, s_red, [&](const DecodeW<WIN> &w) {
         floatx4_t acc = floatx4_t{};
 #pragma unroll
         for (int u = 0; u < WIN; ++u) {
           if (FULL || u < nw) {  // FULL: W of windows past the share is zero
-            const half2_t sp = scales_f16x2(w.s[u]);
+            const half2_t sp = scales_f16x2(scale_pair<SS>(w, u, q));
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) {
               const half8_t wop =
@@ -1434,8 +1481,9 @@ __device__ __forceinline__ bf16x8_t load_a_bf16x8(const uint16_t *row, int64_t k
 }
 
 // K <= 4096: the decode form above with bf16 A held in registers.
-template <bool W2D, bool FULL, int WIN>
+template <bool W2D, bool FULL, int WIN, bool SS = false>
 __global__ __launch_bounds__(kDecWaves * 64) void k_gemm_w4a16_decode(SmallMArgs p) {
+  static_assert(!SS || (W2D && FULL), "one scalar scale load per band needs 2D scales, full windows");
   constexpr int D = dec_depth(WIN, FULL);
   __shared__ floatx4_t s_red[D][kDecWaves][kWave];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -1467,15 +1515,15 @@ __global__ __launch_bounds__(kDecWaves * 64) void k_gemm_w4a16_decode(SmallMArgs
         aop[u][kk] = load_a_bf16x8(arow, (win0 + u) * 128 + q * 32 + kk * 8, p.k, a_ok && u < nw);
   }
   DecodeW<WIN> ring[D];
-  decode_ring_start<W2D, FULL, WIN>(p, buf, nbands, i16, q, win0, nw, ring);
+  decode_ring_start<W2D, FULL, WIN, SS>(p, buf, nbands, i16, q, win0, nw, ring);
 
-  decode_band_loop<W2D, FULL, WIN>(
+  decode_band_loop<W2D, FULL, WIN, SS>(
       p, buf, nbands, lane, wave, win0, nw, gs_w, ring, s_red, [&](const DecodeW<WIN> &w) {
         floatx4_t acc = floatx4_t{};
 #pragma unroll
         for (int u = 0; u < WIN; ++u) {
           if (FULL || u < nw) {  // FULL: W of windows past the share is zero
-            const floatx2_t sf = scales_f32x2(w.s[u]);
+            const floatx2_t sf = scales_f32x2(scale_pair<SS>(w, u, q));
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) {
               const bf16x8_t wop = decode8_bf16(word(w.v[u], kk), kk < 2 ? sf[0] : sf[1]);
@@ -1983,7 +2031,12 @@ static bool decode_full(const SmallMArgs &p) {
 template <bool FUSED, bool FULL, int WIN, bool LEAD = false>
 static void launch_decode_t(const SmallMArgs &p, bool w2d, hipStream_t stream) {
   const dim3 grid(decode_grid(p.n)), block(kDecWaves * 64);
-  if (w2d)
+  // Not in the forms that quantize A: scalar loads and LDS accesses share one wait counter, so
+  // the activation's LDS work would wait for the ring's scale loads (measured 0.4 us slower).
+  if (!FUSED && FULL && w2d && p.scalar_scales)
+    hipLaunchKernelGGL((k_gemm_decode<true, FUSED, FULL, WIN, LEAD, !FUSED && FULL>), grid, block,
+                       0, stream, p);
+  else if (w2d)
     hipLaunchKernelGGL((k_gemm_decode<true, FUSED, FULL, WIN, LEAD>), grid, block, 0, stream, p);
   else
     hipLaunchKernelGGL((k_gemm_decode<false, FUSED, FULL, WIN, LEAD>), grid, block, 0, stream, p);
@@ -1996,10 +2049,21 @@ static void launch_decode_m(const SmallMArgs &p, bool w2d, hipStream_t stream) {
   else launch_decode_t<FUSED, FULL, WIN>(p, w2d, stream);
 }
 
+// Whether a decode launch can take each wave's scale bytes of a band with one scalar load:
+// 16x16 tile scales, full windows, every wave holding WIN windows (K = 16 x 128 x WIN), scale
+// rows 4-byte aligned.
+static bool decode_scalar_scales(const SmallMArgs &p, bool w2d, bool full) {
+  const int64_t nwin = (p.k + 127) / 128;
+  return w2d && full && (nwin == kDecWaves || nwin == kDecWaves * kDecWin) &&
+         (uintptr_t)p.w.scales % 4 == 0 && p.w.ld_scales % 4 == 0;
+}
+
 template <bool FUSED>
-static hipError_t launch_decode(const SmallMArgs &p, bool w2d, hipStream_t stream) {
+static hipError_t launch_decode(const SmallMArgs &args, bool w2d, hipStream_t stream) {
+  SmallMArgs p = args;
   const bool full = decode_full(p);
   const bool one = (p.k + 127) / 128 <= kDecWaves;  // one window per wave
+  p.scalar_scales = decode_scalar_scales(p, w2d, full) ? 1 : 0;
   if (full && one) launch_decode_m<FUSED, true, 1>(p, w2d, stream);
   if (full && !one) launch_decode_m<FUSED, true, 2>(p, w2d, stream);
   if (!full && one) launch_decode_m<FUSED, false, 1>(p, w2d, stream);
@@ -2010,7 +2074,9 @@ static hipError_t launch_decode(const SmallMArgs &p, bool w2d, hipStream_t strea
 template <bool FULL, int WIN>
 static void launch_w4a16_t(const SmallMArgs &p, bool w2d, hipStream_t stream) {
   const dim3 grid(decode_grid(p.n)), block(kDecWaves * 64);
-  if (w2d)
+  if (FULL && w2d && p.scalar_scales)
+    hipLaunchKernelGGL((k_gemm_w4a16_decode<true, FULL, WIN, FULL>), grid, block, 0, stream, p);
+  else if (w2d)
     hipLaunchKernelGGL((k_gemm_w4a16_decode<true, FULL, WIN>), grid, block, 0, stream, p);
   else
     hipLaunchKernelGGL((k_gemm_w4a16_decode<false, FULL, WIN>), grid, block, 0, stream, p);
@@ -2059,6 +2125,7 @@ hipError_t launch_gemm_decode_fused(const void *a_bf16, int64_t ld_a, const Gemm
   p.y = y;
   p.ld_y = ld_y;
   p.scale_pairs = ((uintptr_t)w.scales % 2 == 0) && (w.ld_scales % 2 == 0);
+  p.scalar_scales = 0;
   p.a_bf16 = (const uint16_t *)a_bf16;
   p.ld_a = ld_a;
   p.aq_codes = (uint8_t *)aq.codes;
@@ -2079,6 +2146,7 @@ hipError_t launch_gemm_w4a16(const void *a_bf16, int64_t ld_a, const GemmOperand
   p.y = y;
   p.ld_y = ld_y;
   p.scale_pairs = ((uintptr_t)w.scales % 2 == 0) && (w.ld_scales % 2 == 0);
+  p.scalar_scales = 0;
   p.a_bf16 = (const uint16_t *)a_bf16;
   p.ld_a = ld_a;
   p.aq_codes = p.aq_scales = nullptr;
@@ -2092,6 +2160,7 @@ hipError_t launch_gemm_w4a16(const void *a_bf16, int64_t ld_a, const GemmOperand
   if (dec_fits) {
     const bool full = decode_full(p);
     const bool one = (k + 127) / 128 <= kDecWaves;
+    p.scalar_scales = decode_scalar_scales(p, w2d, full) ? 1 : 0;
     if (full && one) launch_w4a16_t<true, 1>(p, w2d, stream);
     if (full && !one) launch_w4a16_t<true, 2>(p, w2d, stream);
     if (!full && one) launch_w4a16_t<false, 1>(p, w2d, stream);
@@ -2118,6 +2187,7 @@ hipError_t launch_gemm_small_m(const GemmOperand &a, const GemmOperand &w, int64
   p.ld_y = ld_y;
   p.scale_pairs = ((uintptr_t)a.scales % 2 == 0) && (a.ld_scales % 2 == 0) &&
                   ((uintptr_t)w.scales % 2 == 0) && (w.ld_scales % 2 == 0);
+  p.scalar_scales = 0;
   p.a_bf16 = nullptr;
   p.ld_a = 0;
   p.aq_codes = p.aq_scales = nullptr;

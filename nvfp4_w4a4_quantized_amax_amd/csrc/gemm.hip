@@ -1209,7 +1209,7 @@ __device__ __forceinline__ void decode_ring_start(const SmallMArgs &p, const WBu
 template <bool W2D, bool FULL, int WIN, bool SS, int D, class Mul>
 __device__ __forceinline__ void decode_band_loop(const SmallMArgs &p, const WBufs &buf,
                                                  int64_t nbands, int lane, int wave,
-                                                 int64_t win0, int nw, float alpha,
+                                                 int64_t win0, int nw, float alpha_a, float alpha_w,
                                                  DecodeW<WIN> (&ring)[D],
                                                  floatx4_t (*s_red)[kDecWaves][kWave], Mul mul) {
   static_assert(D * 256 <= kDecWaves * 64, "at most one output per thread and round");
@@ -1229,7 +1229,12 @@ __device__ __forceinline__ void decode_band_loop(const SmallMArgs &p, const WBuf
       const int64_t n = band * 16 + 4 * (fl >> 4) + fc;
       // A plain store: the end of the kernel waits for it, and a write-back one through L2
       // completes sooner than a streaming one (measured 0.1-0.3 us per call).
-      if (n < p.n) p.y[(int64_t)frow * p.ld_y + n] = (uint16_t)f32_to_bf16_rne(t * alpha);
+      // The W global scale is first used here, after the bands: its load went out before the W
+      // ring, and a use hoisted ahead of the loop would wait for the whole ring (the empty asm
+      // keeps the multiply in place).
+      float aw = alpha_w;
+      asm volatile("" : "+v"(aw));
+      if (n < p.n) p.y[(int64_t)frow * p.ld_y + n] = (uint16_t)f32_to_bf16_rne(t * (alpha_a * aw));
     }
     __syncthreads();
   };
@@ -1335,7 +1340,9 @@ __global__ __launch_bounds__(kDecWaves * 64) void k_gemm_decode(SmallMArgs p) {
       } else {
         decode_ring_start<W2D, FULL, WIN, SS>(p, buf, nbands, i16, q, win0, nw, ring);
       }
-      __syncthreads();
+      // Only LDS passes between the waves here; the barrier waits for LDS accesses alone, not
+      // for the W rings in flight.
+      lds_barrier();
       gs_a = tab.gs;
     } else {
       // Each wave loads its own K slice of all m rows of A, coalesced: step j gives lane l the
@@ -1372,7 +1379,7 @@ __global__ __launch_bounds__(kDecWaves * 64) void k_gemm_decode(SmallMArgs p) {
 #pragma unroll
       for (int w2 = 1; w2 < kDecWaves; ++w2) mx = max(mx, red[w2]);
       gs_a = global_scale_from_amax_bits(mx);
-      build_tables(tab, gs_a);
+      build_tables<true>(tab, gs_a);  // an LDS-only barrier: the W ring is in flight
       if (p.aq_gs && blockIdx.x == 0 && threadIdx.x == 0) *p.aq_gs = gs_a;
       const float inv6gs = tab.inv6gs;
       // Encode; codes and scales of the slice go to this wave's LDS corner (row-major, 16 blocks
@@ -1393,7 +1400,11 @@ __global__ __launch_bounds__(kDecWaves * 64) void k_gemm_decode(SmallMArgs p) {
           }
         }
       }
-      __syncthreads();
+      // Each wave reads back only its own corner, and a wave's LDS accesses complete in order:
+      // ordering them at wavefront scope suffices, with no workgroup barrier.
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
     // MFMA layout: lane (i16, q), window u holds blocks 8u + 2q and 8u + 2q + 1 of row i16.
     const bool a_ok = i16 < p.m;
@@ -1444,9 +1455,9 @@ __global__ __launch_bounds__(kDecWaves * 64) void k_gemm_decode(SmallMArgs p) {
     }
   }
 
-  const float alpha = (FUSED ? gs_a : gs_a_in) * gs_w;
   decode_band_loop<W2D, FULL, WIN, SS>(
-      p, buf, nbands, lane, wave, win0, nw, alpha, ring, s_red, [&](const DecodeW<WIN> &w) {
+      p, buf, nbands, lane, wave, win0, nw, FUSED ? gs_a : gs_a_in, gs_w, ring, s_red,
+      [&](const DecodeW<WIN> &w) {
         floatx4_t acc = floatx4_t{};
 #pragma unroll
         for (int u = 0; u < WIN; ++u) {
@@ -1518,7 +1529,7 @@ __global__ __launch_bounds__(kDecWaves * 64) void k_gemm_w4a16_decode(SmallMArgs
   decode_ring_start<W2D, FULL, WIN, SS>(p, buf, nbands, i16, q, win0, nw, ring);
 
   decode_band_loop<W2D, FULL, WIN, SS>(
-      p, buf, nbands, lane, wave, win0, nw, gs_w, ring, s_red, [&](const DecodeW<WIN> &w) {
+      p, buf, nbands, lane, wave, win0, nw, 1.0f, gs_w, ring, s_red, [&](const DecodeW<WIN> &w) {
         floatx4_t acc = floatx4_t{};
 #pragma unroll
         for (int u = 0; u < WIN; ++u) {

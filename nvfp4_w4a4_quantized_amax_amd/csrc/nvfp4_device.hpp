@@ -274,6 +274,9 @@ __device__ __forceinline__ bool gs_usable(float gs) { return gs > 0.0f && gs < 3
 // Fill `t` (in LDS) for global scale gs.  Must be called by every thread of a workgroup of at
 // least 128 threads; ends with a barrier (the only one).  A usable gs lies in (0, 3e38);
 // otherwise every block gets scale 0.  Threads 0..127 (two whole waves) each write one entry.
+// LDS_ONLY: the barrier waits for the waves' LDS accesses alone, not for their outstanding
+// global loads (a workgroup barrier with the usual fence waits for every load in flight).
+template <bool LDS_ONLY = false>
 __device__ inline void build_tables(QuantTables &t, float gs) {
   const int tid = threadIdx.x;
   const double gsd = (double)gs;
@@ -286,7 +289,10 @@ __device__ inline void build_tables(QuantTables &t, float gs) {
     t.gs = gs;
     t.inv6gs = usable ? (float)(1.0 / (6.0 * gsd)) : 0.0f;
   }
-  __syncthreads();
+  if (LDS_ONLY)
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  else
+    __syncthreads();
 }
 
 // The same tables built by one wave alone (all 64 lanes call it; each writes entries lane and

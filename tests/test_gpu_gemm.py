@@ -113,6 +113,37 @@ def test_prequantized_a(nv, m):
     check_gemm(y, y64, what=f"prequantized m={m}")
 
 
+# The decode kernels read a wave's scale bytes of a band with one scalar load when W has 16x16
+# tile scales, K is 2048 or 4096 (every wave holds its whole share of windows) and the scale rows
+# are 4-byte aligned; otherwise with vector loads.  Both, for A prequantized (the form that takes
+# the scalar loads) and A quantized inside the call (the form that does not): bit-identical
+# outputs, and the oracle's bound.
+@pytest.mark.parametrize("k", [2048, 4096])
+@pytest.mark.parametrize("pad", [0, 2])
+def test_decode_scale_load_paths(nv, k, pad):
+    rng = np.random.default_rng(k + pad)
+    n = 1040
+    w = W.to_bf16_bits(rng.standard_normal((n, k)) * 0.02)
+    scales = torch.full((n // 16, k // 16 + pad), 0xEE, dtype=torch.uint8, device="cuda")
+    wq0 = nv.empty_qtensor(n, k, 16)
+    wq = nv.QTensor(wq0.codes, scales[:, :k // 16], wq0.global_scale, n, k, 16)
+    nv.quantize_2d(dev_bf16(w), out=wq)
+    ow = O.quantize_2d(w) + (16,)
+    wc, ws, wg = host_q(wq)
+    assert_codes_equal(ws, ow[1], f"k={k} pad={pad} W scales")
+    assert_codes_equal(wc, ow[0], f"k={k} pad={pad} W codes")
+    for m in (1, 8, 16):
+        a = W.to_bf16_bits(rng.standard_normal((m, k)))
+        aq = nv.quantize_1d(dev_bf16(a))
+        y = nv.gemm_w4a4(aq, wq)
+        y_fused = nv.gemm_w4a4(dev_bf16(a), wq)
+        assert torch.equal(y, y_fused), f"k={k} pad={pad} m={m}: prequantized and fused differ"
+        check_gemm(y, O.gemm64(O.quantize_1d(a) + (1,), ow), what=f"k={k} pad={pad} m={m}")
+    torch.cuda.synchronize()
+    if pad:
+        assert bool((scales[:, k // 16:] == 0xEE).all()), "padding of the scale rows written"
+
+
 # A single activation row: K <= 4096 takes the decode kernel, whose first wave quantizes the
 # bf16 activation for the whole workgroup (the quantized A it writes is checked; K = 2064 and
 # 1040 leave the last waves' K slices short or empty); K = 8192 a quantize launch and the

@@ -158,6 +158,28 @@ def test_decode_config_full_size(nv):
                    what=f"w4a16 decode M={m}")
 
 
+# 16x16-tile W scales with K = 2048 and 4096 and 4-byte aligned scale rows take the decode
+# kernel's scalar scale loads; padded (2-byte aligned) rows take the vector loads.
+@pytest.mark.parametrize("k", [2048, 4096])
+@pytest.mark.parametrize("pad", [0, 2])
+def test_scale_load_paths(nv, k, pad):
+    rng = np.random.default_rng(3 * k + pad)
+    n = 1040
+    w = W.to_bf16_bits(rng.standard_normal((n, k)) * 0.02)
+    scales = torch.full((n // 16, k // 16 + pad), 0xEE, dtype=torch.uint8, device="cuda")
+    wq0 = nv.empty_qtensor(n, k, 16)
+    wq = nv.QTensor(wq0.codes, scales[:, :k // 16], wq0.global_scale, n, k, 16)
+    nv.quantize_2d(dev_bf16(w), out=wq)
+    ow = O.quantize_2d(w) + (16,)
+    wc, ws, wg = host_q(wq)
+    assert_codes_equal(ws, ow[1], f"k={k} pad={pad} W scales")
+    assert_codes_equal(wc, ow[0], f"k={k} pad={pad} W codes")
+    for m in (1, 8, 16):
+        a = W.to_bf16_bits(rng.standard_normal((m, k)))
+        y = nv.gemm_w4a16(dev_bf16(a), wq)
+        check_gemm(y, O.gemm64_w4a16(a, ow), what=f"w4a16 k={k} pad={pad} m={m}")
+
+
 def test_rejects_prefill_shapes(nv):
     a = torch.zeros((17, 64), dtype=torch.bfloat16, device="cuda")
     wq = nv.quantize_1d(torch.zeros((32, 64), dtype=torch.bfloat16, device="cuda"))

@@ -1184,13 +1184,15 @@ __device__ __forceinline__ void load_decode_w(const SmallMArgs &p, const WBufs &
   }
 }
 
-// Issues the loads of the workgroup's first dec_depth bands.
-template <bool W2D, bool FULL, int WIN, bool SS, int D>
+// Issues the loads of ring slots J0 .. J1 - 1 (the workgroup's bands J0 .. J1 - 1 of its first
+// dec_depth), all of them by default.
+template <bool W2D, bool FULL, int WIN, bool SS, int D, int J0 = 0, int J1 = D>
 __device__ __forceinline__ void decode_ring_start(const SmallMArgs &p, const WBufs &buf,
                                                   int64_t nbands, int i16, int q, int64_t win0,
                                                   int nw, DecodeW<WIN> (&ring)[D]) {
+  static_assert(0 <= J0 && J0 < J1 && J1 <= D, "ring slots");
 #pragma unroll
-  for (int j = 0; j < D; ++j)
+  for (int j = J0; j < J1; ++j)
     load_decode_w<W2D, FULL, WIN, SS>(p, buf, blockIdx.x + (int64_t)j * gridDim.x, nbands, i16, q,
                                   win0, nw, ring[j]);
   // Work on A that follows must not move above these loads (it would wait for A first).
@@ -1262,9 +1264,15 @@ __device__ __forceinline__ void decode_band_loop(const SmallMArgs &p, const WBuf
 // 16 rows, so the redundant work is small and no workgroup waits for another.
 // LEAD (FUSED with one activation row): wave 0 alone loads the row, finds its amax, builds the
 // tables and encodes every slice, while the other waves' W rings are already in flight; they
-// meet it at one barrier.  Otherwise each wave loads and encodes its own slice, and the rings
-// start after the amax barrier (a W ring issued before it delays the activation loads of the
-// waves that start later).
+// meet it at one barrier.  Otherwise each wave loads and encodes its own slice, and its ring
+// goes out in three parts after the amax barrier (a W ring issued before it delays the
+// activation loads of the waves that start later): one band there, one after the tables, the
+// rest after the encode.  A wave that issues loads while the CU's memory pipeline is full of W
+// requests stalls at that instruction until earlier requests drain, so a whole ring issued at
+// the barrier held up the table build behind it (1.2 us alone, 3 us behind the ring at 16
+// rows); issued in parts, the quantization runs while the first bands stream (measured
+// 1.0-1.6 us faster at 2-16 rows than the whole ring at the barrier; the whole ring after the
+// encode, or two bands at the barrier, measured in between).
 template <bool W2D, bool FUSED, bool FULL, int WIN, bool LEAD = false, bool SS = false>
 __global__ __launch_bounds__(kDecWaves * 64) void k_gemm_decode(SmallMArgs p) {
   static_assert(!SS || (W2D && FULL), "one scalar scale load per band needs 2D scales, full windows");
@@ -1374,12 +1382,13 @@ __global__ __launch_bounds__(kDecWaves * 64) void k_gemm_decode(SmallMArgs p) {
       mx = wave_max_u32(mx);
       if (lane == 0) red[wave] = mx;
       __syncthreads();
-      decode_ring_start<W2D, FULL, WIN, SS>(p, buf, nbands, i16, q, win0, nw, ring);
+      decode_ring_start<W2D, FULL, WIN, SS, D, 0, 1>(p, buf, nbands, i16, q, win0, nw, ring);
       mx = red[0];
 #pragma unroll
       for (int w2 = 1; w2 < kDecWaves; ++w2) mx = max(mx, red[w2]);
       gs_a = global_scale_from_amax_bits(mx);
       build_tables<true>(tab, gs_a);  // an LDS-only barrier: the W ring is in flight
+      decode_ring_start<W2D, FULL, WIN, SS, D, 1, 2>(p, buf, nbands, i16, q, win0, nw, ring);
       if (p.aq_gs && blockIdx.x == 0 && threadIdx.x == 0) *p.aq_gs = gs_a;
       const float inv6gs = tab.inv6gs;
       // Encode; codes and scales of the slice go to this wave's LDS corner (row-major, 16 blocks
@@ -1405,6 +1414,7 @@ __global__ __launch_bounds__(kDecWaves * 64) void k_gemm_decode(SmallMArgs p) {
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      decode_ring_start<W2D, FULL, WIN, SS, D, 2, D>(p, buf, nbands, i16, q, win0, nw, ring);
     }
     // MFMA layout: lane (i16, q), window u holds blocks 8u + 2q and 8u + 2q + 1 of row i16.
     const bool a_ok = i16 < p.m;

@@ -1955,7 +1955,10 @@ hipError_t launch_gemm_tile(const GemmOperand &a, const GemmOperand &w, int64_t 
                             hipStream_t stream) {
   const bool scales2 = ((uintptr_t)a.scales % 2 == 0) && ((uintptr_t)w.scales % 2 == 0) &&
                        a.ld_scales % 2 == 0 && w.ld_scales % 2 == 0;
-  if (gemm_uses_mid(m, n, k) && scales2) {
+  const bool scv = (uintptr_t)a.scales % 16 == 0 && (uintptr_t)w.scales % 16 == 0 &&
+                   a.ld_scales % 16 == 0 && w.ld_scales % 16 == 0;
+  if ((gemm_uses_mid(m, n, k) && scales2) ||
+      (gemm_uses_mid_wide(m, n, k) && w.block_rows == 16 && scv)) {
     DenseArgs p{};
     p.a = a;
     p.w = w;
@@ -1967,10 +1970,8 @@ hipError_t launch_gemm_tile(const GemmOperand &a, const GemmOperand &w, int64_t 
     p.tiles_m = (int)((m + 63) / 64);
     p.tiles_n = (int)((n + 63) / 64);
     const unsigned grid = (unsigned)p.tiles_m * (unsigned)p.tiles_n;
-    const bool scv = (uintptr_t)a.scales % 16 == 0 && (uintptr_t)w.scales % 16 == 0 &&
-                     a.ld_scales % 16 == 0 && w.ld_scales % 16 == 0;
-    // M = 65-128 against a wide weight (2D scales, aligned scale rows): 128-row tiles read W
-    // once (measured 0.7-1.8 us faster than two 64-row slices).
+    // M = 65-384 against a wide weight (2D scales, aligned scale rows): 128-row tiles (W read
+    // once per row slice; measured 0.7-1.8 us faster than two 64-row slices at M = 65-128).
     if (w.block_rows == 16 && scv && m > 64 && (n + 63) / 64 >= 128) {
       p.tiles_m = (int)((m + 127) / 128);
       hipLaunchKernelGGL((k_gemm_mid<4, true, true>), dim3((unsigned)p.tiles_m * (unsigned)p.tiles_n),

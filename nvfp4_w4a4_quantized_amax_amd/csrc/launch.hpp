@@ -62,9 +62,19 @@ struct GemmOperand {
 // For M = 65-128 against a weight of at least 8192 rows with 16x16 tile scales and 16-byte
 // aligned scale rows, the launcher takes 128-row tiles instead (one workgroup per CU, W read
 // once: 0.7-1.8 us faster on the 14336 x 4096 weight); elsewhere 128-row tiles measured no
-// faster.  Past M = 128 the 256 x 256 tiles with their interleaved decode win.
+// faster.  On such a weight the 128-row tiles also serve M = 129-384 (gemm_uses_mid_wide; two
+// or three row slices, W re-read from L2): 2-4 us faster than the 256 x 256 tiles with a K split
+// at 14336 x 4096 (41-68 us against 45-70 us prequantized), but slower at M = 512 (89 against
+// 74 us).  Otherwise past M = 128 the 256 x 256 tiles with their interleaved decode win.
 inline bool gemm_uses_mid(int64_t m, int64_t n, int64_t k) {
   return m > 16 && m <= 128 && k > 0 && k % 1024 == 0 && ((m + 63) / 64) * ((n + 63) / 64) >= 128;
+}
+
+// The M = 129-384 shapes that take the mid-size kernel's 128-row tiles when W has 16x16 tile
+// scales and 16-byte aligned scale rows (checked by the launcher; other layouts split K, so the
+// workspace still covers the split).
+inline bool gemm_uses_mid_wide(int64_t m, int64_t n, int64_t k) {
+  return m > 128 && m <= 384 && k > 0 && k % 1024 == 0 && (n + 63) / 64 >= 128;
 }
 
 inline int gemm_k_splits(int64_t m, int64_t n, int64_t k) {

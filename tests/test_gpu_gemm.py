@@ -68,6 +68,9 @@ def test_tiny_config(nv):
     # register-prefetch kernel with 256-row tiles), 2D and 1D.
     (65, 8192, 4096, 16), (200, 512, 4096, 1), (513, 1024, 1024, 1), (1024, 2048, 512, 1),
     (200, 256, 1040, 16), (150, 272, 528, 1),
+    # M = 129-384 on a wide 2D-scaled weight: 128-row tiles of the mid-size kernel in two or
+    # three row slices (ragged M and N); the same shape with 1D W scales splits K instead.
+    (129, 8192, 1024, 16), (256, 8256, 2048, 16), (384, 8192, 1024, 16), (200, 8192, 1024, 1),
 ])
 def test_shapes(nv, m, n, k, br):
     rng = np.random.default_rng(m * 7 + n * 3 + k)
@@ -77,10 +80,11 @@ def test_shapes(nv, m, n, k, br):
 
 
 @pytest.mark.parametrize("br", [16, 1])
-@pytest.mark.parametrize("m", [40, 100])
+@pytest.mark.parametrize("m", [40, 100, 200])
 def test_mid_kernel_strided_scales(nv, m, br):
     """Mid-size M on a wide weight whose scale rows are not 16-byte aligned (a strided view of
-    a wider scale buffer): the mid-size kernel's form that loads scales 2 bytes at a time."""
+    a wider scale buffer): the mid-size kernel's form that loads scales 2 bytes at a time, and
+    at M = 200 the 256 x 256 tiles with a K split (the 128-row tiles need aligned rows)."""
     rng = np.random.default_rng(m + br)
     n, k = 8192, 2048
     a = W.to_bf16_bits(W.normal_with_outliers(rng, m, k, 0.01, 20.0))

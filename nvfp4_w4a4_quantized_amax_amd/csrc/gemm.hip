@@ -1073,8 +1073,9 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_small_m(SmallMArgs p) {
 constexpr int kDecWaves = 16;
 constexpr int kDecWin = 2;  // 128-wide K windows per wave at most (K <= 16 * 2 * 128)
 // Bands of W in flight per workgroup: as many as the 128 registers of a 16-wave workgroup hold
-// next to the rest of the kernel (deep: the FULL forms, except the W4A4 one that quantizes A
-// itself, which measured faster with 3 bands of two windows).
+// next to the rest of the kernel (deep: the FULL forms, except the W4A4 one where every wave
+// quantizes its slice of A, which measured faster with 3 bands of two windows while its ring
+// went out whole, and no slower since the ring goes out in parts).
 constexpr int dec_depth(int win, bool deep) { return win == 1 || deep ? 4 : 3; }
 constexpr uint32_t kBufOutOfRange = 0x80000000u;  // above every buffer size used here
 

@@ -1264,8 +1264,8 @@ __device__ __forceinline__ void decode_band_loop(const SmallMArgs &p, const WBuf
 // nvfp4_quantize_1d would; workgroup 0 also writes the quantized A when asked to.  A is at most
 // 16 rows, so the redundant work is small and no workgroup waits for another.
 // LEAD (FUSED with one activation row): wave 0 alone loads the row, finds its amax, builds the
-// tables and encodes every slice, while the other waves' W rings are already in flight; they
-// meet it at one barrier.  Otherwise each wave loads and encodes its own slice, and its ring
+// tables and encodes every slice, while the other waves' W rings, issued once the row's loads
+// are out (a first barrier), are in flight; they meet it at a second barrier.  Otherwise each wave loads and encodes its own slice, and its ring
 // goes out in three parts after the amax barrier (a W ring issued before it delays the
 // activation loads of the waves that start later): one band there, one after the tables, the
 // rest after the encode.  A wave that issues loads while the CU's memory pipeline is full of W
@@ -1320,6 +1320,9 @@ __global__ __launch_bounds__(kDecWaves * 64) void k_gemm_decode(SmallMArgs p) {
           xa[j][0] = *(const uint4 *)src;
           xa[j][1] = *(const uint4 *)(src + 8);
         }
+        // The other waves issue their rings only after this barrier, behind the row's loads.
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_barrier();
         decode_ring_start<W2D, FULL, WIN, SS>(p, buf, nbands, i16, q, win0, nw, ring);
         uint32_t mx = 0;
 #pragma unroll
@@ -1347,6 +1350,7 @@ __global__ __launch_bounds__(kDecWaves * 64) void k_gemm_decode(SmallMArgs p) {
           }
         }
       } else {
+        __builtin_amdgcn_s_barrier();  // wave 0's row loads are out (measured 0.1 us faster)
         decode_ring_start<W2D, FULL, WIN, SS>(p, buf, nbands, i16, q, win0, nw, ring);
       }
       // Only LDS passes between the waves here; the barrier waits for LDS accesses alone, not

@@ -1265,15 +1265,16 @@ __device__ __forceinline__ void decode_band_loop(const SmallMArgs &p, const WBuf
 // 16 rows, so the redundant work is small and no workgroup waits for another.
 // LEAD (FUSED with one activation row): wave 0 alone loads the row, finds its amax, builds the
 // tables and encodes every slice, while the other waves' W rings, issued once the row's loads
-// are out (a first barrier), are in flight; they meet it at a second barrier.  Otherwise each wave loads and encodes its own slice, and its ring
-// goes out in three parts after the amax barrier (a W ring issued before it delays the
-// activation loads of the waves that start later): one band there, one after the tables, the
-// rest after the encode.  A wave that issues loads while the CU's memory pipeline is full of W
-// requests stalls at that instruction until earlier requests drain, so a whole ring issued at
-// the barrier held up the table build behind it (1.2 us alone, 3 us behind the ring at 16
-// rows); issued in parts, the quantization runs while the first bands stream (measured
-// 1.0-1.6 us faster at 2-16 rows than the whole ring at the barrier; the whole ring after the
-// encode, or two bands at the barrier, measured in between).
+// are out (a first barrier), are in flight; they meet it at a second barrier.  Otherwise each
+// wave loads and encodes its own slice, and its ring goes out in three parts after the amax
+// barrier (a W ring issued before it delays the activation loads of the waves that start
+// later): one band there, one after the tables, the rest after the encode.  A wave that issues
+// loads while the CU's memory pipeline is full of W requests stalls at that instruction until
+// earlier requests drain, so with the whole ring issued at the amax barrier the table barrier
+// waited for the last wave to get its loads out (the table phase took 3 us at 16 rows, 1.2 us
+// with no ring in flight); issued in parts, the quantization runs while the first bands stream
+// (1.0-1.6 us faster at 2-16 rows; the whole ring after the tables or after the encode, or two
+// bands at the amax barrier, measured in between).
 template <bool W2D, bool FUSED, bool FULL, int WIN, bool LEAD = false, bool SS = false>
 __global__ __launch_bounds__(kDecWaves * 64) void k_gemm_decode(SmallMArgs p) {
   static_assert(!SS || (W2D && FULL), "one scalar scale load per band needs 2D scales, full windows");

@@ -17,6 +17,8 @@ Infinity Cache left there by the previous step.
 GEMMs, activation quantization inside the call; the weight-only W4A16 form of the decode
 shapes; the dequantization of the headline activation; the MXFP4 variant and the MSE-observer
 weight quantization), each timed the same way with its own roofline.
+"accuracy" reports the error of each format on the same seeded inputs (dequantized tensors
+against their bf16 inputs, products against the float64 product of the bf16 inputs).
 "cpu_baseline" times the CPU oracle (test infrastructure, float64 numpy) on the same headline
 input on the host.
 """
@@ -394,6 +396,48 @@ def extra_workloads(args, torch, np, nv, W, only):
     return out
 
 
+def accuracy(torch, np, nv, W):
+    """Error of the formats the library serves on the seeded workloads, computed on the device
+    from the library's own outputs: relative Frobenius norms ||Q(x) - x|| / ||x|| of the
+    dequantized tensors against their bf16 inputs, and ||Y - Y64|| / ||Y64|| of the products
+    against the float64 product of the same bf16 inputs (measurement only, not the path)."""
+    def rel(a, b):
+        a, b = a.double(), b.double()
+        return float(torch.linalg.vector_norm(a - b) / torch.linalg.vector_norm(b))
+
+    out = {"what": "relative Frobenius error against the bf16 inputs (quantize) or against the "
+                   "float64 product of the bf16 inputs (products)"}
+    x = dev_bf16(torch, np, W.activation(seed=1, rows=8192, cols=8192)["x"])
+    out["activation_8192x8192"] = {
+        "nvfp4_1d": rel(nv.dequantize(nv.quantize_1d(x)), x),
+        "mxfp4": rel(nv.mxfp4_dequantize(nv.mxfp4_quantize(x)), x)}
+    del x
+    d = W.decode()  # the decode configuration: W, then A for M = 1, 8, 16
+    w = dev_bf16(torch, np, d["w"])
+    wq2, wq1 = nv.quantize_2d(w), nv.quantize_1d(w)
+    wmse, wmx = nv.quantize_mse(w, 16), nv.mxfp4_quantize(w)
+    out["decode_weight_14336x4096"] = {
+        "nvfp4_2d": rel(nv.dequantize(wq2), w), "nvfp4_2d_mse_observer": rel(nv.dequantize(wmse), w),
+        "nvfp4_1d": rel(nv.dequantize(wq1), w), "mxfp4": rel(nv.mxfp4_dequantize(wmx), w)}
+    a = dev_bf16(torch, np, d["a"][16])
+    y64 = a.double() @ w.double().t()
+    out["decode_product_16x14336x4096"] = {
+        "w4a4_nvfp4": rel(nv.gemm_w4a4(a, wq2), y64),
+        "w4a4_nvfp4_mse_weights": rel(nv.gemm_w4a4(a, wmse), y64),
+        "w4a16_nvfp4": rel(nv.gemm_w4a16(a, wq2), y64),
+        "w4a4_mxfp4": rel(nv.mxfp4_gemm(a, wmx), y64)}
+    del w, wq2, wq1, wmse, wmx, a, y64
+    d = W.prefill()
+    a, w = dev_bf16(torch, np, d["a"]), dev_bf16(torch, np, d["w"])
+    y64 = a.double() @ w.double().t()
+    out["prefill_product_8192x8192x8192"] = {
+        "w4a4_nvfp4": rel(nv.gemm_w4a4(a, nv.quantize_2d(w)), y64),
+        "w4a4_mxfp4": rel(nv.mxfp4_gemm(a, nv.mxfp4_quantize(w)), y64)}
+    del a, w, y64
+    torch.cuda.empty_cache()
+    return out
+
+
 def host_info():
     """Host cores as the CPU oracle sees them: os.cpu_count(), the affinity mask and the BLAS
     thread pools numpy's matmul uses."""
@@ -514,6 +558,8 @@ def main():
     if not args.no_extra:
         only = [s for s in args.only.split(",") if s]
         rec["workloads"] = extra_workloads(args, torch, np, nv, W, only)
+        if not only or "accuracy" in only:
+            rec["accuracy"] = accuracy(torch, np, nv, W)
     rec["roofline"]["median_gbs"] = h["median_gbs"]
     rec["roofline"]["per_call"] = h["stats"]
     rec["clocks"] = clocks()

@@ -33,8 +33,9 @@ struct QuantTables {
   //       block scale code is >= s (thresh[127] = 0xFFFF, never reached);
   //   y, z = float bits of the element multipliers of codes c and c + 1; w unused.
   // The multiplier k of scale code s is a float with RNE_fp4(RN_fp32(x * k)) equal to the exact
-  // nearest-code rule for every bf16 x; a negative value (-k) means no such k was found and the
-  // block takes the exact slow path.  Codes 0, -1 and 127 have k = 0.
+  // nearest-code rule for every bf16 x; a negative value means no such k was found: -khi
+  // (finite) selects the two-term multiplier, -infinity the exact slow path (encode16).  Codes
+  // 0, -1 and 127 have k = 0.
   uint4 ent[128];
 };
 
@@ -180,6 +181,28 @@ __device__ __forceinline__ uint32_t fast_code(uint32_t bits, float k) {
   return cvt_fp4x2<0>(0u, y, y) & 7u;
 }
 
+// Two-term multiplier for a scale S whose rounded reciprocal khi = RN_fp32(1/S) fails (no single
+// float reproduces the rule; this happens when gs has few significant bits, so that exact ties
+// x = midpoint * S occur): klo = RN_fp32((1 - S khi) khi) carries 1/S - khi to about 2^-24 of
+// itself (the residual comes from one double FMA: S has <= 28 significant bits, khi 24), and an
+// element takes y = RN_fp32(x khi + RN_fp32(x klo)), monotone in x like the single product.
+// Scaling S by 2^E scales khi and klo by 2^-E exactly while klo stays a normal float, which
+// the global-scale range of two_term_range guarantees for every block-scale code.
+__device__ __forceinline__ float two_term_lo(float khi, double S) {
+  const double e = fma(-S, (double)khi, 1.0);
+  return (float)(e * (double)khi);
+}
+
+__device__ __forceinline__ bool two_term_range(double gsd) {
+  return gsd >= 0x1p-60 && gsd <= 0x1p60;
+}
+
+__device__ __forceinline__ uint32_t fast_code2(uint32_t bits, float khi, float klo) {
+  const float x = __uint_as_float(bits << 16);
+  const float y = fmaf(x, khi, x * klo);
+  return cvt_fp4x2<0>(0u, y, y) & 7u;
+}
+
 // ---------------------------------------------------------------------------------------------
 // Per-tensor tables, built in LDS by every workgroup that encodes (256 threads, three phases).
 // ---------------------------------------------------------------------------------------------
@@ -194,7 +217,9 @@ __device__ __forceinline__ double e2m1_mid(int i) {
 // 6) around midpoint i under the exact scale S = sb * gs?  The fast code is monotone in x, so it
 // suffices that the largest bf16 that must map to <= i does and the smallest bf16 that must map
 // to >= i+1 does; checking all 7 midpoints covers every bf16 input.
-__device__ __forceinline__ bool multiplier_ok_at(float k, double S, int i) {
+// `code_of(bits)` is the per-element rule under test (the single or the two-term multiplier).
+template <class CodeOf>
+__device__ __forceinline__ bool midpoint_ok(const CodeOf &code_of, double S, int i) {
   double P = e2m1_mid(i) * S;  // exact: <= 3 + 28 significant bits
   bool exact;
   uint32_t rd = bf16_round_down(P, &exact);
@@ -202,7 +227,15 @@ __device__ __forceinline__ bool multiplier_ok_at(float k, double S, int i) {
   bool tie_down = (i & 1) == 0;  // midpoint between an even index i and i+1 goes down
   uint32_t below = exact ? (tie_down ? rd : rd - 1u) : rd;
   uint32_t above = exact ? (tie_down ? rd + 1u : rd) : rd + 1u;
-  return fast_code(below, k) <= (uint32_t)i && fast_code(above, k) >= (uint32_t)i + 1u;
+  return code_of(below) <= (uint32_t)i && code_of(above) >= (uint32_t)i + 1u;
+}
+
+__device__ __forceinline__ bool multiplier_ok_at(float k, double S, int i) {
+  return midpoint_ok([&](uint32_t b) { return fast_code(b, k); }, S, i);
+}
+
+__device__ __forceinline__ bool multiplier2_ok_at(float khi, float klo, double S, int i) {
+  return midpoint_ok([&](uint32_t b) { return fast_code2(b, khi, klo); }, S, i);
 }
 
 // Block-scale threshold for code s (1..126): bamax / (6 gs) is rounded to the nearest E4M3 code,
@@ -229,8 +262,10 @@ __device__ __forceinline__ uint32_t scale_threshold(int s, double gsd) {
 // checked the same way, one midpoint per lane, so the repair costs two more checks rather than
 // up to fourteen in a row.
 
-// The lane's base multiplier (lanes 7m, m = 0..7, hold mantissa m's; a negative value means no
-// float passed and blocks with that mantissa take the exact slow path).  Every lane of the wave
+// The lane's base multiplier (lanes 7m, m = 0..7, hold mantissa m's).  A negative value means
+// that no single float passed: -khi (finite) when the two-term multiplier (khi, two_term_lo)
+// passes every check, -infinity when it does not either (or gs is outside two_term_range); the
+// blocks with that mantissa take the two-term or the exact slow path.  Every lane of the wave
 // must call it (ballots).
 __device__ inline float table_base_multiplier(double gsd, bool usable) {
   const int lane = threadIdx.x & 63;
@@ -242,13 +277,19 @@ __device__ inline float table_base_multiplier(double gsd, bool usable) {
   const unsigned long long bad = __ballot(!ok);
   if (bad) {  // uniform: the ballot is the same in every lane
     // The rounded reciprocal of some mantissa fails somewhere: try the float above it, then
-    // the one below, else take the exact path (negative multiplier).
+    // the one below, then the two-term multiplier, else take the exact path.
     const float ku = __uint_as_float(__float_as_uint(kb) + 1u);
     const float kd = __uint_as_float(__float_as_uint(kb) - 1u);
     const unsigned long long bad_u = __ballot(checker && !multiplier_ok_at(ku, S, i));
     const unsigned long long bad_d = __ballot(checker && !multiplier_ok_at(kd, S, i));
+    const bool two_ok = two_term_range(gsd);
+    const float klo = checker && two_ok ? two_term_lo(kb, S) : 0.0f;
+    const unsigned long long bad_2 =
+        __ballot(checker && (!two_ok || !multiplier2_ok_at(kb, klo, S, i)));
     const unsigned long long mine = 0x7Full << (7 * m);
-    if (checker && (bad & mine)) kb = !(bad_u & mine) ? ku : (!(bad_d & mine) ? kd : -kb);
+    if (checker && (bad & mine))
+      kb = !(bad_u & mine) ? ku
+                           : (!(bad_d & mine) ? kd : (!(bad_2 & mine) ? -kb : -INFINITY));
   }
   return kb;
 }
@@ -451,15 +492,35 @@ __device__ __forceinline__ uint32_t encode8_fast(uint4 v, float k) {
   return r;
 }
 
+// Eight codes under the two-term multiplier (khi, klo) of the block's scale.
+__device__ __forceinline__ uint32_t encode8_two(uint4 v, float khi, float klo) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  uint32_t r = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float lo = bf16_lo(w[j]), hi = bf16_hi(w[j]);
+    const float ylo = fmaf(lo, khi, lo * klo), yhi = fmaf(hi, khi, hi * klo);
+    r |= (__builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, ylo, yhi, 1.0f, 0) & 0xFFu) << (8 * j);
+  }
+  return r;
+}
+
 // The 16 codes of one block (a: values 0..7, b: values 8..15).  The multiplier path runs
-// unconditionally; the rare blocks whose scale has no exact multiplier (k < 0) are redone on
-// the exact path.
+// unconditionally; the rare blocks whose scale has no single exact multiplier (k < 0) are redone
+// with the two-term multiplier (k = -khi, finite) or on the exact path (k = -infinity).
 __device__ __forceinline__ uint2 encode16(const uint4 &a, const uint4 &b, float k, int code,
                                           float gs) {
   uint2 r = make_uint2(encode8_fast(a, k), encode8_fast(b, k));
   if (k < 0.0f) {
-    r.x = encode8_exact(a, code, gs);
-    r.y = encode8_exact(b, code, gs);
+    if (k != -INFINITY) {
+      const float khi = -k;
+      const float klo = two_term_lo(khi, (double)e4m3_to_float((uint32_t)code) * (double)gs);
+      r.x = encode8_two(a, khi, klo);
+      r.y = encode8_two(b, khi, klo);
+    } else {
+      r.x = encode8_exact(a, code, gs);
+      r.y = encode8_exact(b, code, gs);
+    }
   }
   return r;
 }

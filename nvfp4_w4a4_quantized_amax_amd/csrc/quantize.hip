@@ -153,37 +153,58 @@ __global__ __launch_bounds__(kQThreads) void k_encode_1d(const uint4 *__restrict
                                                          int n_slots, float *__restrict__ gs_out) {
   __shared__ QuantTables tab;
   __shared__ uint32_t red[kQWaves];
-  tables_from_slots(slots, n_slots, tab, red, gs_out);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const uint32_t S = gridDim.x * kQWaves;
   const uint32_t n_tiles = (n_blocks + kTileBlocks - 1) / kTileBlocks;
   const uint32_t first = blockIdx.x * kQWaves + wave;
-  if (first >= n_tiles) return;
-  // This wave's tiles are first + i * S, i = 0 .. cnt - 1; walk them from the last, two at a
-  // time (four 16-byte loads in flight per lane).  Only the last tile of all can be partial.
-  const uint32_t cnt = (n_tiles - first + S - 1) / S;
+  // This wave's tiles are first + i * S, i = 0 .. cnt - 1; they are walked from the last, two
+  // at a time (four 16-byte loads in flight per lane).  Only the last tile of all can be partial.
+  const uint32_t cnt = first < n_tiles ? (n_tiles - first + S - 1) / S : 0u;
+  // The slot loads go out first, then the loads of the first two tiles: the tiles do not
+  // depend on the global scale, so they are in flight while the slots are reduced and the tables
+  // are built (loads complete in order, so waiting for the slots does not wait for the tiles,
+  // and the barriers below wait for LDS work only).
+  // Every load below is unconditional (indices clamped into range; max is idempotent and the
+  // clamped tile loads are never used), so the compiler can wait for the slots alone.
+  uint32_t m = 0;
+#pragma unroll
+  for (int j = 0; j < kMaxAmaxSlots / kQThreads; ++j)
+    m = max(m, slots[min(j * kQThreads + (int)threadIdx.x, n_slots - 1)]);
   int32_t i = (int32_t)cnt - 1;
-  for (; i >= 1; i -= 2) {
+  const uint32_t ba0 = (first + (uint32_t)max(i, 0) * S) * kTileBlocks + lane;
+  const bool va = i >= 0 && ba0 < n_blocks;
+  const bool vb = i >= 1;
+  const uint32_t bb0 = vb ? ba0 - S * kTileBlocks : 0u;
+  const size_t ia0 = block_index<CONTIG>(va ? ba0 : 0u, bpr, ld_x8);
+  const size_t ib0 = block_index<CONTIG>(bb0, bpr, ld_x8);
+  uint4 a0 = x[ia0], a1 = x[ia0 + 1];
+  uint4 b0 = x[ib0], b1 = x[ib0 + 1];
+  m = wave_max_u32(m);
+  if (lane == 0) red[wave] = m;
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+#pragma unroll
+  for (int w = 0; w < kQWaves; ++w) m = max(m, red[w]);
+  const float gs = global_scale_from_amax_bits(m);
+  if (blockIdx.x == 0 && threadIdx.x == 0) *gs_out = gs;
+  build_tables<true>(tab, gs);
+  if (va) encode_block_1d<CONTIG>(a0, a1, ba0, bpr, o, tab);
+  if (vb) encode_block_1d<CONTIG>(b0, b1, bb0, bpr, o, tab);
+  for (i -= 2; i >= 1; i -= 2) {
     const uint32_t ba = (first + (uint32_t)i * S) * kTileBlocks + lane;
     const uint32_t bb = ba - S * kTileBlocks;
-    const bool va = ba < n_blocks;
-    uint4 a0 = make_uint4(0, 0, 0, 0), a1 = a0;
-    if (va) {
-      const size_t ia = block_index<CONTIG>(ba, bpr, ld_x8);
-      a0 = x[ia];
-      a1 = x[ia + 1];
-    }
+    const size_t ia = block_index<CONTIG>(ba, bpr, ld_x8);  // not the last tile: whole
+    a0 = x[ia];
+    a1 = x[ia + 1];
     const size_t ib = block_index<CONTIG>(bb, bpr, ld_x8);
-    const uint4 b0 = x[ib], b1 = x[ib + 1];
-    if (va) encode_block_1d<CONTIG>(a0, a1, ba, bpr, o, tab);
+    b0 = x[ib];
+    b1 = x[ib + 1];
+    encode_block_1d<CONTIG>(a0, a1, ba, bpr, o, tab);
     encode_block_1d<CONTIG>(b0, b1, bb, bpr, o, tab);
   }
-  if (i == 0) {
+  if (i == 0) {  // a whole tile: the wave has at least three
     const uint32_t ba = first * kTileBlocks + lane;
-    if (ba < n_blocks) {
-      const size_t ia = block_index<CONTIG>(ba, bpr, ld_x8);
-      encode_block_1d<CONTIG>(x[ia], x[ia + 1], ba, bpr, o, tab);
-    }
+    const size_t ia = block_index<CONTIG>(ba, bpr, ld_x8);
+    encode_block_1d<CONTIG>(x[ia], x[ia + 1], ba, bpr, o, tab);
   }
 }
 

@@ -34,6 +34,8 @@ def main():
         "activation band 512x8192": W.activation(seed=1, rows=512, cols=8192)["x"],
         "ragged 1000x1040": W.to_bf16_bits(rng.laplace(0, 1, (1000, 1040))),
         "strided 700x1024 (ld 1088)": None,
+        # two-kernel path: 4 or 5 tiles per wave of the encode pass, the last tile partial
+        "ragged 5001x4112": W.to_bf16_bits(rng.laplace(0, 1, (5001, 4112))),
     }
     big = W.to_bf16_bits(rng.standard_normal((700, 1088)))
     for name, x in cases.items():

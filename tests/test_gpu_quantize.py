@@ -106,16 +106,19 @@ def test_adversarial_ties_and_zeros(nv):
 
 
 @pytest.mark.parametrize("amax_sig", [21, 42, 63, 105, 128, 255])
-def test_short_global_scales(nv, amax_sig):
+@pytest.mark.parametrize("exp", [0, 100, -100])
+def test_short_global_scales(nv, amax_sig, exp):
     """amax significands that are multiples of 21 make gs short (few bits), so exact E2M1 and
-    E4M3 midpoints occur often and exercise the exact slow path."""
+    E4M3 midpoints occur often and some block-scale mantissa has no single exact multiplier:
+    those blocks take the two-term multiplier (exp = 0), or the exact slow path where gs lies
+    outside the two-term range (exp = +-100: gs near 2^93 and 2^-110)."""
     rng = np.random.default_rng(amax_sig)
     x = rng.integers(-255, 256, size=(96, 512)).astype(np.float64) * 2.0 ** -4
     x[0, 0] = amax_sig * 2.0 ** -3
     x[np.abs(x) > amax_sig * 2.0 ** -3] = 0
-    x = W.to_bf16_bits(x)
-    check_1d(nv, x, f"short gs {amax_sig}")
-    check_1d(nv, np.tile(x, (200, 1)), f"short gs {amax_sig}, large")
+    x = W.to_bf16_bits(x * 2.0 ** exp)
+    check_1d(nv, x, f"short gs {amax_sig} x 2^{exp}")
+    check_1d(nv, np.tile(x, (200, 1)), f"short gs {amax_sig} x 2^{exp}, large")
 
 
 def test_extremes(nv):
@@ -239,4 +242,4 @@ def test_other_quantize_paths(path, spin):
     r = subprocess.run([sys.executable, "-u", os.path.join(here, "quantize_path_check.py")],
                        env=env, capture_output=True, text=True, timeout=110)
     assert r.returncode == 0, r.stdout[-2000:] + r.stderr[-2000:]
-    assert r.stdout.count(" ok") == 3, r.stdout
+    assert r.stdout.count(" ok") == 4, r.stdout
